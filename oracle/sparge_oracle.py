@@ -1,0 +1,561 @@
+"""Float64 CPU oracle for the SpargeAttn hot path.  TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import or run this module.  The product path (the HIP
+library and its Python binding) never calls it, and this module imports
+nothing from the product package: the two share no code.
+
+It is a plain, slow restatement of the method, step by step, in float64:
+
+Pages cited (by title and section):
+
+* [Review]   "SpargeAttn: Accurate and Training-free Sparse Attention
+             Accelerating Any Model Inference", xllm-io paper-review blog:
+             section "Core formulas" (eqs. 1-9), the sparse warp online softmax
+             rule, "Algorithm 1", the components table and "HilbertCurve
+             Permutation".
+* [Rebuttal] "SpargeAttention: Accurate and Training-free Sparse Attention
+             Accelerating Any Model Inference", OpenReview author rebuttal:
+             replies "Weaknesses1", "Weaknesses3.1" and "Weaknesses3.2".
+
+Readings taken where the pages are open (each is listed in the design doc):
+
+* CosSim (eq. 6) is the mean of the b x b cosine-similarity matrix of the
+  block's tokens, diagonal included; a zero row has cosine 0 with everything
+  ([Review] eq. 6 with [Rebuttal] Weaknesses3.1, which calls the printed
+  matrix a typo and asks for one mean cosine similarity per block).
+* The compressed map uses the same 1/sqrt(d) scale as S in eq. 1.
+* TopCdf (eq. 8) orders entries by probability, descending, ties to the lower
+  column, and keeps the shortest prefix whose inclusive cumulative sum reaches
+  tau * sum(P): entry r is kept iff the exclusive prefix c_{r-1} < tau * sum.
+  The sum is the last value of the same sequential cumulative sum.
+* Causal prediction: key blocks that lie wholly in the future of a query block
+  are -inf in the compressed map and 0 in M_g; eq. 9 only forces live tiles.
+* The lambda vote is taken per group of R consecutive query rows (one GPU
+  wavefront) in natural-log units of S; rows whose local max is -inf take no
+  part, and a group with no such row skips.  l still takes rowsum(P~) when PV
+  is skipped (Algorithm 1 computes m and P~ before testing M_pv).
+* A query row with l = 0 at the end (no visible key executed) outputs 0.
+* int8 (Algorithm 1 step 2, SageAttention-style): symmetric per-block scale
+  delta = max|x| / 127 (1 for an all-zero block), code = clamp(rint(x/delta),
+  -127, 127) with ties to even; K first has its per-(b, kv-head) mean over all
+  tokens subtracted; S = (codes_q . codes_k) * delta_q * delta_k / sqrt(d).
+  The garbled "delta Bias" term is dropped: it is constant along a row, and
+  softmax and the lambda vote are invariant to a per-row constant.
+* GQA: query head h reads kv head h // (H / H_kv).
+* 3D Hilbert order: Skilling's transpose algorithm ("Programming the Hilbert
+  curve", AIP Conf. Proc. 707, 2004) on the enclosing 2^b cube with axes
+  (t, h, w), then tokens are sorted by curve index.
+
+Pins: every function here is checked by ``tests/test_oracle_*.py`` against
+closed forms, special cases, brute force on tiny inputs, hand-built rows and
+the rebuttal's worked sparsity example.  Parity unpinned: the sparsity values
+the method reaches on the synthetic workloads (only GPU-vs-oracle agreement
+covers them; the pages' sparsities come from real models).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+BQ = 128          # query block rows (b_q)
+BK = 64           # key/value block rows (b_k)
+ROWS_PER_GROUP = 32   # rows that vote together in the lambda rule (b_q / c_w)
+
+NEG_INF = -np.inf
+
+
+# ---------------------------------------------------------------------------
+# storage widening
+# ---------------------------------------------------------------------------
+
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of bfloat16 / float16 bit patterns (uint16) to float64."""
+    bits = np.asarray(bits)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(bits, dtype=np.float64)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# blocks and causal liveness
+# ---------------------------------------------------------------------------
+
+def num_blocks(N: int, b: int) -> int:
+    return (N + b - 1) // b
+
+
+def block_rows(N: int, b: int, i: int) -> range:
+    """Rows of block i: [b*i, min(N, b*i + b)) ([Review] Algorithm 1 step 1)."""
+    return range(b * i, min(N, b * i + b))
+
+
+def tile_live(N: int, bq: int, bk: int, causal: bool) -> np.ndarray:
+    """[Tm, Tn] bool: tile (i, j) holds at least one visible (query, key) pair.
+
+    Non-causal: every tile.  Causal: the first key of block j is not after the
+    last query of block i.
+    """
+    Tm, Tn = num_blocks(N, bq), num_blocks(N, bk)
+    live = np.ones((Tm, Tn), dtype=bool)
+    if causal:
+        for i in range(Tm):
+            last_q = min(N, bq * i + bq) - 1
+            for j in range(Tn):
+                live[i, j] = bk * j <= last_q
+    return live
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: selective token compression ([Review] eqs. 4-9, Algorithm 1 steps 3-5)
+# ---------------------------------------------------------------------------
+
+def mean_pool(X: np.ndarray, b: int) -> np.ndarray:
+    """Eqs. 4-5: the mean token of every block of b rows.  X [N, d] -> [T, d]."""
+    N = X.shape[0]
+    return np.stack([X[block_rows(N, b, t)].mean(axis=0) for t in range(num_blocks(N, b))])
+
+
+def cossim(Xb: np.ndarray) -> float:
+    """Eq. 6 (as corrected in [Rebuttal] Weaknesses3.1): one block's mean cosine
+    similarity, the mean of the b x b matrix of cos(x_a, x_c), diagonal included.
+    """
+    norms = np.sqrt((Xb * Xb).sum(axis=1))
+    xhat = np.zeros_like(Xb)
+    nz = norms > 0
+    xhat[nz] = Xb[nz] / norms[nz, None]
+    G = xhat @ xhat.T
+    return float(G.mean())
+
+
+def block_cossim(X: np.ndarray, b: int) -> np.ndarray:
+    N = X.shape[0]
+    return np.array([cossim(X[block_rows(N, b, t)]) for t in range(num_blocks(N, b))])
+
+
+def topcdf(p: np.ndarray, tau: float) -> Tuple[np.ndarray, Dict[str, np.ndarray]]:
+    """Eq. 8: TopCdf over one row of probabilities p [n] (all finite, >= 0).
+
+    Entries are ordered by p descending with ties going to the lower index; the
+    entry at sorted position r is kept iff the exclusive prefix sum
+    c_{r-1} (c_{-1} = 0) is below tau * sum(p).  Returns (keep [n] bool, info)
+    where info holds, per original index, the exclusive prefix and the order.
+    """
+    n = p.shape[0]
+    order = np.lexsort((np.arange(n), -p))          # primary: -p ascending; secondary: index
+    ps = p[order]
+    c = np.cumsum(ps)                               # sequential, hence non-decreasing
+    total = c[-1] if n else 0.0
+    excl = np.concatenate([[0.0], c[:-1]]) if n else c
+    keep_sorted = excl < tau * total
+    keep = np.zeros(n, dtype=bool)
+    keep[order] = keep_sorted
+    excl_by_idx = np.empty(n)
+    excl_by_idx[order] = excl
+    return keep, {"excl": excl_by_idx, "order": order, "thresh": tau * total, "p": p}
+
+
+def predict_mask_head(Qh: np.ndarray, Kh: np.ndarray, tau: float, theta: float, causal: bool,
+                      bq: int = BQ, bk: int = BK, fix_q: Optional[np.ndarray] = None,
+                      fix_k: Optional[np.ndarray] = None, scale_in_map: bool = True,
+                      near_cdf: float = 1e-4, near_tie: float = 1e-6) -> Dict[str, np.ndarray]:
+    """Stage 1 for one (batch, query head): M_g [Tm, Tn] from Q [N, d] and K [N, d].
+
+    Algorithm 1 steps 3-5 of [Review]: pool (eqs. 4-5), self-similarity
+    (eq. 6), compressed map with -inf on fix key blocks (eq. 7), row softmax and
+    TopCdf (eq. 8), then force fix rows and columns (eq. 9).  ``fix_q`` /
+    ``fix_k`` override the (s < theta) classification, so a run can replay
+    another implementation's decision for blocks whose similarity lies next to
+    theta.  The returned ``ambiguous`` marks entries whose selection depends on
+    rounding: exclusive prefix within ``near_cdf`` of tau*sum, or probability
+    tied (relative ``near_tie``) with the last kept entry of its row.
+    """
+    N, d = Qh.shape
+    Tm, Tn = num_blocks(N, bq), num_blocks(N, bk)
+    qbar = mean_pool(Qh, bq)
+    kbar = mean_pool(Kh, bk)
+    s_q = block_cossim(Qh, bq)
+    s_k = block_cossim(Kh, bk)
+    fq = (s_q < theta) if fix_q is None else np.asarray(fix_q, dtype=bool)
+    fk = (s_k < theta) if fix_k is None else np.asarray(fix_k, dtype=bool)
+    live = tile_live(N, bq, bk, causal)
+
+    shat = qbar @ kbar.T
+    if scale_in_map:
+        shat = shat / math.sqrt(d)
+    shat[:, fk] = NEG_INF                           # eq. 7
+    shat[~live] = NEG_INF                           # future key blocks (causal)
+
+    mg = np.zeros((Tm, Tn), dtype=bool)
+    ambiguous = np.zeros((Tm, Tn), dtype=bool)
+    for i in range(Tm):
+        cols = np.nonzero(np.isfinite(shat[i]))[0]
+        if cols.size == 0:
+            continue
+        z = shat[i, cols]
+        e = np.exp(z - z.max())
+        p = e / e.sum()                              # P^[i] = softmax(S^[i])
+        keep, info = topcdf(p, tau)
+        mg[i, cols[keep]] = True
+        amb = np.abs(info["excl"] - info["thresh"]) <= near_cdf
+        last_kept = info["order"][int(keep.sum()) - 1]
+        tied = np.abs(p - p[last_kept]) <= near_tie * p[last_kept]
+        if tied.sum() > 1:                           # a near-tie straddles the cut
+            amb |= tied
+        ambiguous[i, cols[amb]] = True
+    mg[fq, :] = True                                 # eq. 9, rows
+    mg[:, fk] = True                                 # eq. 9, columns
+    mg &= live
+    ambiguous &= live & ~fq[:, None] & ~fk[None, :]
+    return {"mg": mg, "s_q": s_q, "s_k": s_k, "qbar": qbar, "kbar": kbar, "fix_q": fq,
+            "fix_k": fk, "live": live, "ambiguous": ambiguous, "shat": shat}
+
+
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """GQA grouping: contiguous groups of H / H_kv query heads share a kv head."""
+    return h // (H // H_kv)
+
+
+def predict_mask(Q: np.ndarray, K: np.ndarray, tau: float, theta: float, causal: bool,
+                 bq: int = BQ, bk: int = BK, fix_q=None, fix_k=None, heads=None, **kw):
+    """Stage 1 for Q [B, H, N, d], K [B, H_kv, N, d].
+
+    Returns M_g [B, H, Tm, Tn] (bool), s_q [B, H, Tm], s_k [B, H_kv, Tn],
+    ambiguous [B, H, Tm, Tn].  ``heads`` restricts the work to a list of
+    (b, h) pairs (other rows stay zero).  ``fix_q`` [B, H, Tm] / ``fix_k``
+    [B, H_kv, Tn] override the fix classification.
+    """
+    B, H, N, d = Q.shape
+    H_kv = K.shape[1]
+    Tm, Tn = num_blocks(N, bq), num_blocks(N, bk)
+    mg = np.zeros((B, H, Tm, Tn), dtype=bool)
+    amb = np.zeros((B, H, Tm, Tn), dtype=bool)
+    s_q = np.zeros((B, H, Tm))
+    s_k = np.zeros((B, H_kv, Tn))
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in todo:
+        hk = kv_head(h, H, H_kv)
+        r = predict_mask_head(Q[b, h], K[b, hk], tau, theta, causal, bq, bk,
+                              None if fix_q is None else fix_q[b, h],
+                              None if fix_k is None else fix_k[b, hk], **kw)
+        mg[b, h] = r["mg"]
+        amb[b, h] = r["ambiguous"]
+        s_q[b, h] = r["s_q"]
+        s_k[b, hk] = r["s_k"]
+    return {"mg": mg, "s_q": s_q, "s_k": s_k, "ambiguous": amb}
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: block-sparse FlashAttention with the lambda rule
+# ([Review] eqs. 1-3, sparse warp online softmax, Algorithm 1 steps 6-17)
+# ---------------------------------------------------------------------------
+
+# Counters, in this order: live tiles; tiles whose QK^T ran (M_g = 1) and were
+# skipped; row groups whose PV ran, were skipped by the lambda vote, or had no
+# visible key in the tile at all (void: nothing to add); rows that saw no key;
+# rows.
+COUNT_NAMES = ("live_tiles", "qk_exec", "qk_skip", "pv_exec", "pv_skip", "pv_void",
+               "empty_rows", "rows")
+
+
+def _scores_float(Qi: np.ndarray, Kj: np.ndarray) -> np.ndarray:
+    return Qi @ Kj.T / math.sqrt(Qi.shape[1])
+
+
+def attend_row_block(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.ndarray, i: int,
+                     lam: float, causal: bool, bq: int = BQ, bk: int = BK,
+                     R: int = ROWS_PER_GROUP, skip_override: Optional[np.ndarray] = None,
+                     score_fn=None, vote_info: Optional[list] = None):
+    """O_i for one query block i of one head, visiting key blocks j with
+    M_g[i, j] = 1 in ascending j (eq. 1 with eqs. 2-3 and the lambda rule).
+
+    ``skip_override`` [Tn, c_w] (int8: 1 execute, 2 skip, anything else = use
+    the rule) replays another implementation's PV decisions.
+    ``score_fn(rows, keys)`` replaces Q_i K_j^T / sqrt(d) (used by the int8
+    path).  Returns (O_i [n, d_v], counts dict, decisions [Tn, c_w] int8 with
+    1 = PV executed, 2 = skipped by the lambda vote, 3 = void group (no visible
+    key in the tile), 0 = tile not visited).
+    """
+    N, d = Qh.shape
+    Tn = num_blocks(N, bk)
+    rows = block_rows(N, bq, i)
+    n = len(rows)
+    q_idx = np.arange(rows.start, rows.stop)
+    Qi = Qh[rows.start:rows.stop]
+    m = np.full(n, NEG_INF)
+    l = np.zeros(n)
+    O = np.zeros((n, Vh.shape[1]))
+    cw = (bq + R - 1) // R
+    groups = [np.arange(g * R, min(n, g * R + R)) for g in range(cw) if g * R < n]
+    live = tile_live(N, bq, bk, causal)[i]
+    decisions = np.zeros((Tn, cw), dtype=np.int8)
+    cnt = dict.fromkeys(COUNT_NAMES, 0)
+    cnt["live_tiles"] = int(live.sum())
+    for j in range(Tn):                               # ascending j
+        if not (mg_row[j] and live[j]):
+            continue
+        cnt["qk_exec"] += 1
+        keys = block_rows(N, bk, j)
+        k_idx = np.arange(keys.start, keys.stop)
+        if score_fn is None:
+            S = _scores_float(Qi, Kh[keys.start:keys.stop])
+        else:
+            S = score_fn(rows, keys)
+        if causal:
+            S = np.where(k_idx[None, :] > q_idx[:, None], NEG_INF, S)
+        m_loc = S.max(axis=1)
+        m_new = np.maximum(m, m_loc)
+        with np.errstate(invalid="ignore"):
+            m_sub = np.where(np.isfinite(m_new), m_new, 0.0)
+            Pt = np.exp(S - m_sub[:, None])           # exp(-inf) = 0
+            alpha = np.where(np.isfinite(m), np.exp(m - m_sub), 0.0)
+        l = alpha * l + Pt.sum(axis=1)
+        for g, gi in enumerate(groups):
+            fin = np.isfinite(m_loc[gi])
+            rule_skip = (not fin.any()) or (np.max(m_loc[gi][fin] - m_new[gi][fin]) < lam)
+            if vote_info is not None and fin.any():
+                vote_info.append((j, g, float(np.max(m_loc[gi][fin] - m_new[gi][fin])),
+                                  bool(np.any(m_new[gi] != m[gi]))))
+            skip = rule_skip
+            if skip_override is not None and fin.any() and skip_override[j, g] in (1, 2):
+                skip = skip_override[j, g] == 2
+            if not fin.any():
+                cnt["pv_void"] += 1
+                decisions[j, g] = 3
+            elif skip:
+                cnt["pv_skip"] += 1
+                decisions[j, g] = 2                   # O_ij[I_w] = O_i,j-1[I_w]
+            else:
+                cnt["pv_exec"] += 1
+                decisions[j, g] = 1
+                O[gi] = alpha[gi, None] * O[gi] + Pt[gi] @ Vh[keys.start:keys.stop]
+        m = m_new
+    out = np.zeros_like(O)
+    nz = l > 0
+    out[nz] = O[nz] / l[nz, None]
+    cnt["qk_skip"] = cnt["live_tiles"] - cnt["qk_exec"]
+    cnt["empty_rows"] = int((~nz).sum())
+    cnt["rows"] = n
+    return out, cnt, decisions
+
+
+def sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray, lam: float,
+                     causal: bool, bq: int = BQ, bk: int = BK, R: int = ROWS_PER_GROUP,
+                     blocks: Optional[Sequence[Tuple[int, int, int]]] = None,
+                     skip_override: Optional[np.ndarray] = None, quant: Optional[dict] = None):
+    """Stage 2 for Q [B, H, N, d], K/V [B, H_kv, N, d] and M_g [B, H, Tm, Tn].
+
+    ``blocks`` restricts the work to (b, h, i) query blocks; the other rows of
+    the returned O stay 0.  ``skip_override`` [B, H, Tm, Tn, c_w] replays PV
+    decisions.  ``quant`` (from :func:`quantize_qk`) switches S to the int8
+    form.  Returns (O [B, H, N, d_v], counts dict summed over the blocks,
+    decisions [B, H, Tm, Tn, c_w]).
+    """
+    B, H, N, d = Q.shape
+    H_kv = K.shape[1]
+    Tm, Tn = num_blocks(N, bq), num_blocks(N, bk)
+    cw = (bq + R - 1) // R
+    O = np.zeros((B, H, N, V.shape[3]))
+    dec = np.zeros((B, H, Tm, Tn, cw), dtype=np.int8)
+    tot = dict.fromkeys(COUNT_NAMES, 0)
+    todo = blocks if blocks is not None else [(b, h, i) for b in range(B) for h in range(H)
+                                              for i in range(Tm)]
+    for b, h, i in todo:
+        hk = kv_head(h, H, H_kv)
+        score_fn = None
+        if quant is not None:
+            qc, kc = quant["q_codes"][b, h], quant["k_codes"][b, hk]
+            dq, dk = quant["q_scale"][b, h], quant["k_scale"][b, hk]
+
+            def score_fn(rows, keys, qc=qc, kc=kc, dq=dq, dk=dk, i=i):
+                j = keys.start // bk
+                acc = qc[rows.start:rows.stop] @ kc[keys.start:keys.stop].T   # exact integers
+                return acc * (dq[i] * dk[j]) / math.sqrt(d)
+        ov = None if skip_override is None else skip_override[b, h, i]
+        o, c, decision = attend_row_block(Q[b, h], K[b, hk], V[b, hk], mg[b, h, i], i, lam, causal,
+                                          bq, bk, R, ov, score_fn)
+        rows = block_rows(N, bq, i)
+        O[b, h, rows.start:rows.stop] = o
+        dec[b, h, i] = decision
+        for kname in COUNT_NAMES:
+            tot[kname] += c[kname]
+    return O, tot, dec
+
+
+def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, causal: bool) -> np.ndarray:
+    """Brute force softmax(Q K^T / sqrt(d)) V (two-pass), Q [B,H,N,d], K/V [B,H_kv,N,d]."""
+    B, H, N, d = Q.shape
+    H_kv = K.shape[1]
+    O = np.zeros((B, H, N, V.shape[3]))
+    for b in range(B):
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            S = Q[b, h] @ K[b, hk].T / math.sqrt(d)
+            if causal:
+                S = np.where(np.triu(np.ones((N, N), dtype=bool), 1), NEG_INF, S)
+            S = S - S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            O[b, h] = (P / P.sum(axis=1, keepdims=True)) @ V[b, hk]
+    return O
+
+
+def masked_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray, causal: bool,
+                     bq: int = BQ, bk: int = BK) -> np.ndarray:
+    """Closed form of eqs. 1-2 without the lambda rule: softmax(S + log M~) V, with
+    M_g expanded to tokens (two-pass, per row); a row with no visible key gives 0."""
+    B, H, N, d = Q.shape
+    H_kv = K.shape[1]
+    O = np.zeros((B, H, N, V.shape[3]))
+    qb = np.arange(N) // bq
+    kb = np.arange(N) // bk
+    for b in range(B):
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            S = Q[b, h] @ K[b, hk].T / math.sqrt(d)
+            allow = mg[b, h][qb[:, None], kb[None, :]].astype(bool)
+            if causal:
+                allow &= ~np.triu(np.ones((N, N), dtype=bool), 1)
+            S = np.where(allow, S, NEG_INF)
+            for r in range(N):
+                if not allow[r].any():
+                    continue
+                p = np.exp(S[r] - S[r].max())
+                O[b, h, r] = (p / p.sum()) @ V[b, hk]
+    return O
+
+
+# ---------------------------------------------------------------------------
+# int8 per-block quantisation ([Review] Algorithm 1 step 2, components table)
+# ---------------------------------------------------------------------------
+
+def quantize_block(X: np.ndarray) -> Tuple[np.ndarray, float]:
+    """Symmetric int8 codes of one block: delta = max|x| / 127, code = rint(x/delta)."""
+    amax = float(np.abs(X).max()) if X.size else 0.0
+    delta = amax / 127.0 if amax > 0 else 1.0
+    codes = np.clip(np.rint(X / delta), -127, 127)
+    return codes, delta
+
+
+def quantize_qk(Q: np.ndarray, K: np.ndarray, bq: int = BQ, bk: int = BK) -> dict:
+    """Per-block int8 codes and scales of Q [B,H,N,d] and of K - mean_t(K) [B,H_kv,N,d].
+
+    Returns q_codes / k_codes (float64 holding integers), q_scale [B,H,Tm],
+    k_scale [B,H_kv,Tn] (float64), k_mean [B,H_kv,d] and the per-element
+    distance of x/delta from the nearest rounding tie (for near-tie accounting).
+    """
+    B, H, N, d = Q.shape
+    H_kv = K.shape[1]
+    Tm, Tn = num_blocks(N, bq), num_blocks(N, bk)
+    k_mean = K.mean(axis=2)                                  # over all N tokens
+    Kc = K - k_mean[:, :, None, :]
+    q_codes = np.zeros_like(Q)
+    k_codes = np.zeros_like(K)
+    q_scale = np.zeros((B, H, Tm))
+    k_scale = np.zeros((B, H_kv, Tn))
+    q_tie = np.zeros_like(Q)
+    k_tie = np.zeros_like(K)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Tm):
+                r = block_rows(N, bq, i)
+                c, dl = quantize_block(Q[b, h, r.start:r.stop])
+                q_codes[b, h, r.start:r.stop] = c
+                q_scale[b, h, i] = dl
+                t = Q[b, h, r.start:r.stop] / dl
+                q_tie[b, h, r.start:r.stop] = np.abs(t - np.floor(t) - 0.5)
+        for h in range(H_kv):
+            for j in range(Tn):
+                r = block_rows(N, bk, j)
+                c, dl = quantize_block(Kc[b, h, r.start:r.stop])
+                k_codes[b, h, r.start:r.stop] = c
+                k_scale[b, h, j] = dl
+                t = Kc[b, h, r.start:r.stop] / dl
+                k_tie[b, h, r.start:r.stop] = np.abs(t - np.floor(t) - 0.5)
+    return {"q_codes": q_codes, "k_codes": k_codes, "q_scale": q_scale, "k_scale": k_scale,
+            "k_mean": k_mean, "k_centered": Kc, "q_tie_dist": q_tie, "k_tie_dist": k_tie}
+
+
+# ---------------------------------------------------------------------------
+# 3D Hilbert-curve order ([Review] "HilbertCurve Permutation";
+# [Rebuttal] Weaknesses3 / Weaknesses3.2)
+# ---------------------------------------------------------------------------
+
+def hilbert_index(coords: Sequence[int], bits: int) -> int:
+    """Curve index of a point of the 2^bits cube, by Skilling's method: undo the
+    excess work (inverse-undo pass), Gray-encode the transposed form, then
+    interleave the transposed bits from the most significant level down."""
+    x = [int(c) for c in coords]
+    n = len(x)
+    m = 1 << (bits - 1)
+    q = m
+    while q > 1:                                   # inverse undo
+        p = q - 1
+        for a in range(n):
+            if x[a] & q:
+                x[0] ^= p                          # invert low bits of axis 0
+            else:
+                t = (x[0] ^ x[a]) & p              # exchange low bits of axes 0 and a
+                x[0] ^= t
+                x[a] ^= t
+        q >>= 1
+    for a in range(1, n):                          # Gray encode
+        x[a] ^= x[a - 1]
+    t = 0
+    q = m
+    while q > 1:
+        if x[n - 1] & q:
+            t ^= q - 1
+        q >>= 1
+    for a in range(n):
+        x[a] ^= t
+    h = 0                                          # interleave: axis 0 is the most significant
+    for level in range(bits - 1, -1, -1):
+        for a in range(n):
+            h = (h << 1) | ((x[a] >> level) & 1)
+    return h
+
+
+def hilbert_permutation(T: int, Hg: int, Wg: int) -> Tuple[np.ndarray, np.ndarray]:
+    """perm[p] = raster token (t*Hg + h)*Wg + w whose curve rank is p; inv = perm^-1.
+
+    Points are indexed on the enclosing 2^bits cube (bits = ceil(log2(max side)))
+    and sorted by their index; indices are distinct, so the order is unique.
+    """
+    side = max(T, Hg, Wg, 1)
+    bits = max(1, int(math.ceil(math.log2(side))))
+    keys = np.empty(T * Hg * Wg, dtype=np.int64)
+    for t in range(T):
+        for h in range(Hg):
+            for w in range(Wg):
+                keys[(t * Hg + h) * Wg + w] = hilbert_index((t, h, w), bits)
+    perm = np.argsort(keys, kind="stable").astype(np.int32)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size, dtype=np.int32)
+    return perm, inv
+
+
+def permute_tokens(X: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """X' [..., p, :] = X[..., perm[p], :] (gather along the token axis)."""
+    return X[..., perm, :]
+
+
+def unpermute_tokens(Xp: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`permute_tokens`: X[..., perm[p], :] = X'[..., p, :]."""
+    out = np.empty_like(Xp)
+    out[..., perm, :] = Xp
+    return out
+
+
+# ---------------------------------------------------------------------------
+# relative L1 error ([Review] hyper-parameter section: L1 = sum|O - O'| / sum|O|)
+# ---------------------------------------------------------------------------
+
+def rel_l1(O_ref: np.ndarray, O: np.ndarray) -> float:
+    den = float(np.abs(O_ref).sum())
+    return float(np.abs(O_ref - O).sum()) / den if den > 0 else float(np.abs(O).sum())
