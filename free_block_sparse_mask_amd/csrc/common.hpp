@@ -1,0 +1,133 @@
+// Internal declarations shared by the HIP kernels and the C ABI of libsparge.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/sparge.h"
+
+namespace sparge {
+
+constexpr int kBq = SPARGE_BQ;              // query block rows
+constexpr int kBk = SPARGE_BK;              // key/value block rows
+constexpr int kRowsPerWave = 32;            // rows voting together (one wavefront)
+constexpr int kWavesPerBlock = kBq / kRowsPerWave;
+constexpr int kThreads = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Workspace layout (all regions 256-byte aligned, carved in this order)
+// ---------------------------------------------------------------------------
+struct Workspace {
+  // stage 1
+  double* qbar;        // [B,H,Tm,d]
+  double* kbar;        // [B,Hkv,Tn,d]
+  double* sq;          // [B,H,Tm]
+  double* sk;          // [B,Hkv,Tn]
+  double* shat;        // [B,H,Tm,Tn]
+  // int8 quantisation: per-chunk column sums of K, then the mean
+  double* ksum_part;   // [B,Hkv,kQuantChunks,d]
+  double* kmean;       // [B,Hkv,d]
+  // attention: row lists built from a caller's mask
+  int32_t* list_cnt;   // [B,H,Tm]
+  uint16_t* list_idx;  // [B,H,Tm,Tn]
+  size_t total;
+};
+
+constexpr int kQuantChunkRows = 1024;       // tokens per partial K column sum
+
+Workspace carve_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d);
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int B, H, Hkv, N, Tm, Tn, d;
+  int kind;           // 0 f16, 1 bf16, 2 i8 QK + f16 PV, 3 i8 QK + bf16 PV
+  int out_f32;        // store float32 O instead of the P~V type
+  int causal;
+  const int32_t* row_cnt;
+  const uint16_t* row_idx;
+  const float* q_scale;
+  const float* k_scale;
+  float scale_log2;   // log2(e) / sqrt(d)
+  float lam_log2;     // lambda * log2(e)
+  unsigned long long* counts;
+  uint8_t* dbg;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+hipError_t launch_zero_counts(unsigned long long* counts, int n, hipStream_t st);
+
+// M_g rows -> ascending lists of live j with M_g = 1
+hipError_t launch_compact(const uint8_t* mg, int64_t rows, int Tm, int Tn, int N, int causal,
+                          int32_t* cnt, uint16_t* idx, hipStream_t st);
+
+struct PredictArgs {
+  const void* q;
+  const void* k;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int B, H, Hkv, N, Tm, Tn, d;
+  int bf16;
+  int causal;
+  double tau, theta;
+  uint8_t* mg;
+  int32_t* row_cnt;
+  uint16_t* row_idx;
+  double* s_q_out;    // may be null
+  double* s_k_out;    // may be null
+  Workspace ws;
+};
+hipError_t launch_predict(const PredictArgs& a, hipStream_t st);
+
+struct QuantArgs {
+  const void* q;
+  const void* k;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int B, H, Hkv, N, Tm, Tn, d;
+  int bf16;
+  int8_t* q8;
+  int8_t* k8;
+  float* q_scale;
+  float* k_scale;
+  Workspace ws;
+};
+hipError_t launch_quant(const QuantArgs& a, hipStream_t st);
+
+struct PermuteArgs {
+  const void* x;
+  void* y;
+  int64_t x_sb, x_sh, x_sn;   // in bytes
+  int64_t y_sb, y_sh, y_sn;   // in bytes
+  int B, H, N;
+  int row_bytes;
+  const int32_t* perm;
+  int inverse;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
+
+// host-side 3D Hilbert order
+int hilbert_order(int T, int H, int W, int32_t* perm, int32_t* inv);
+
+}  // namespace sparge

@@ -1,0 +1,76 @@
+// Host-side 3D Hilbert order for visual tokens.
+//
+// Pages: [Review] "SpargeAttn: Accurate and Training-free Sparse Attention
+// Accelerating Any Model Inference" (xllm-io paper-review blog), "HilbertCurve
+// Permutation" and the components table (HilbertCurve permutation, block 4);
+// [Rebuttal] replies "Weaknesses3" and "Weaknesses3.2".
+//
+// The curve index of a point follows J. Skilling, "Programming the Hilbert
+// curve", AIP Conf. Proc. 707 (2004): the coordinates are turned into the
+// curve's "transposed" index by undoing the rotations level by level from the
+// top bit down, Gray-encoding across axes, and a final correction; the index
+// is the transposed bits read level by level (axis 0 = t most significant).
+// Points of a T x H x W grid are indexed on the enclosing 2^b cube and sorted
+// by index (indices are distinct, so the order is unique).
+#include <algorithm>
+#include <cstdint>
+#include <numeric>
+#include <vector>
+
+#include "common.hpp"
+
+namespace sparge {
+
+namespace {
+
+uint64_t curve_index(uint32_t x[3], int bits) {
+  const uint32_t top = 1u << (bits - 1);
+  for (uint32_t q = top; q > 1; q >>= 1) {
+    const uint32_t lowmask = q - 1;
+    for (int axis = 0; axis < 3; ++axis) {
+      if (x[axis] & q) {
+        x[0] ^= lowmask;
+      } else {
+        const uint32_t swapbits = (x[0] ^ x[axis]) & lowmask;
+        x[0] ^= swapbits;
+        x[axis] ^= swapbits;
+      }
+    }
+  }
+  x[1] ^= x[0];
+  x[2] ^= x[1];
+  uint32_t flip = 0;
+  for (uint32_t q = top; q > 1; q >>= 1)
+    if (x[2] & q) flip ^= q - 1;
+  for (int axis = 0; axis < 3; ++axis) x[axis] ^= flip;
+  uint64_t index = 0;
+  for (int level = bits - 1; level >= 0; --level)
+    for (int axis = 0; axis < 3; ++axis) index = (index << 1) | ((x[axis] >> level) & 1u);
+  return index;
+}
+
+}  // namespace
+
+int hilbert_order(int T, int H, int W, int32_t* perm, int32_t* inv) {
+  const int side = std::max(T, std::max(H, W));
+  int bits = 1;
+  while ((1 << bits) < side) ++bits;
+  const int64_t n = (int64_t)T * H * W;
+  std::vector<uint64_t> key((size_t)n);
+  for (int t = 0; t < T; ++t)
+    for (int h = 0; h < H; ++h)
+      for (int w = 0; w < W; ++w) {
+        uint32_t x[3] = {(uint32_t)t, (uint32_t)h, (uint32_t)w};
+        key[(size_t)(((int64_t)t * H + h) * W + w)] = curve_index(x, bits);
+      }
+  std::vector<int32_t> order((size_t)n);
+  std::iota(order.begin(), order.end(), 0);
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return key[a] < key[b]; });
+  for (int64_t p = 0; p < n; ++p) {
+    perm[p] = order[(size_t)p];
+    inv[order[(size_t)p]] = (int32_t)p;
+  }
+  return 0;
+}
+
+}  // namespace sparge

@@ -1,0 +1,432 @@
+// Stage 1 of SpargeAttn on gfx950: predict the block mask M_g.
+//
+// Pages: [Review] "SpargeAttn: Accurate and Training-free Sparse Attention
+// Accelerating Any Model Inference" (xllm-io paper-review blog), "Core
+// formulas" eqs. (4)-(9) and "Algorithm 1" steps 3-5; [Rebuttal] OpenReview
+// author rebuttal, reply "Weaknesses3.1" (CosSim is one mean cosine
+// similarity per block) and "Weaknesses1" (only self-similar blocks are
+// compressed; the others are always computed).
+//
+// Every quantity that decides a mask bit (block means, self-similarity, the
+// compressed map, its softmax and the TopCdf prefix sums) is computed in
+// float64.  Three kernels:
+//   pool_cossim   one workgroup per Q or K block: coalesced 16-byte loads,
+//                 per-token norms by a 16-lane shuffle reduction, column sums
+//                 of x and x/|x| combined through LDS; s = |mean x/|x||^2.
+//   shat_gemm     Shat = qbar kbar^T / sqrt(d) per (batch, head) on 64 x 64
+//                 tiles staged through LDS (tiles wholly in the causal future
+//                 are skipped).
+//   mask_rows     one workgroup per query block row: softmax over the live
+//                 selective columns, a bitonic sort in LDS by (P desc, j asc),
+//                 a workgroup prefix scan for TopCdf, eq. 9 forcing, then the
+//                 M_g row and its compacted ascending list.
+#include "common.hpp"
+
+namespace sparge {
+
+namespace {
+
+constexpr double kNegInfD = -__builtin_huge_val();
+
+__device__ __forceinline__ double bits_to_double(unsigned short u, bool bf16) {
+  if (bf16) return (double)__uint_as_float((unsigned int)u << 16);
+  return (double)(float)__builtin_bit_cast(_Float16, u);
+}
+
+// Workgroup-wide exclusive scan of one int per thread (256 threads).
+__device__ int block_excl_scan_int(int v, int* lds, int& total) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int t = tid >= off ? lds[tid - off] : 0;
+    __syncthreads();
+    lds[tid] += t;
+    __syncthreads();
+  }
+  total = lds[kThreads - 1];
+  const int incl = lds[tid];
+  __syncthreads();
+  return incl - v;
+}
+
+__device__ double block_excl_scan_double(double v, double* lds, double& total) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const double t = tid >= off ? lds[tid - off] : 0.0;
+    __syncthreads();
+    lds[tid] += t;
+    __syncthreads();
+  }
+  total = lds[kThreads - 1];
+  const double incl = lds[tid];
+  __syncthreads();
+  return incl - v;
+}
+
+__device__ double block_reduce_max(double v, double* lds) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) lds[tid] = fmax(lds[tid], lds[tid + off]);
+    __syncthreads();
+  }
+  const double r = lds[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ double block_reduce_sum(double v, double* lds) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) lds[tid] += lds[tid + off];
+    __syncthreads();
+  }
+  const double r = lds[0];
+  __syncthreads();
+  return r;
+}
+
+// Writes the M_g row (Tn bytes) and the ascending list of its ones.
+// keep(j) must be readable by every thread.
+template <typename Keep>
+__device__ void write_row(int Tn, Keep keep, uint8_t* mg_row, int32_t* cnt_out, uint16_t* idx_row,
+                          int* scan_lds) {
+  const int tid = threadIdx.x;
+  const int per = (Tn + kThreads - 1) / kThreads;
+  const int lo = min(Tn, tid * per), hi = min(Tn, lo + per);
+  int mine = 0;
+  for (int j = lo; j < hi; ++j) mine += keep(j) ? 1 : 0;
+  int total;
+  int pos = block_excl_scan_int(mine, scan_lds, total);
+  for (int j = lo; j < hi; ++j)
+    if (keep(j)) idx_row[pos++] = (uint16_t)j;
+  if (mg_row != nullptr)
+    for (int j = tid; j < Tn; j += kThreads) mg_row[j] = keep(j) ? 1 : 0;
+  if (tid == 0) *cnt_out = total;
+}
+
+// ---------------------------------------------------------------------------
+// pool_cossim: eqs. (4)-(6)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
+  constexpr int DCH = D / 8;                 // lanes per token row
+  constexpr int SLOTS = kThreads / DCH;      // token rows in flight
+  __shared__ double red_x[SLOTS][D + 1];
+  __shared__ double red_h[SLOTS][D + 1];
+  __shared__ double red_s[kThreads];
+
+  const long long nq = (long long)a.B * a.H * a.Tm;
+  long long blk = blockIdx.x;
+  const bool is_q = blk < nq;
+  int b, h, t, brows;
+  const unsigned short* base;
+  long long sn;
+  if (is_q) {
+    t = (int)(blk % a.Tm);
+    const long long bh = blk / a.Tm;
+    b = (int)(bh / a.H);
+    h = (int)(bh % a.H);
+    brows = kBq;
+    base = static_cast<const unsigned short*>(a.q) + b * a.q_sb + h * a.q_sh;
+    sn = a.q_sn;
+  } else {
+    blk -= nq;
+    t = (int)(blk % a.Tn);
+    const long long bh = blk / a.Tn;
+    b = (int)(bh / a.Hkv);
+    h = (int)(bh % a.Hkv);
+    brows = kBk;
+    base = static_cast<const unsigned short*>(a.k) + b * a.k_sb + h * a.k_sh;
+    sn = a.k_sn;
+  }
+  const int r0 = t * brows;
+  const int nrows = min(a.N, r0 + brows) - r0;
+  const int tid = threadIdx.x;
+  const int c = tid % DCH, slot = tid / DCH;
+  const bool bf = a.bf16 != 0;
+
+  double sx[8], sh[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sx[e] = sh[e] = 0.0;
+  for (int r = slot; r < nrows; r += SLOTS) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(base + (long long)(r0 + r) * sn + 8 * c);
+    double x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = bits_to_double((unsigned short)(w[e >> 1] >> ((e & 1) * 16)), bf);
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+#pragma unroll
+    for (int off = 1; off < DCH; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sx[e] += x[e];
+      sh[e] += x[e] * inv;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    red_x[slot][8 * c + e] = sx[e];
+    red_h[slot][8 * c + e] = sh[e];
+  }
+  __syncthreads();
+  double contrib = 0.0;
+  if (tid < D) {
+    double tx = 0.0, th = 0.0;
+    for (int s = 0; s < SLOTS; ++s) {
+      tx += red_x[s][tid];
+      th += red_h[s][tid];
+    }
+    const double mean = tx / nrows;
+    const double mh = th / nrows;
+    contrib = mh * mh;
+    if (is_q)
+      a.ws.qbar[(((long long)b * a.H + h) * a.Tm + t) * D + tid] = mean;
+    else
+      a.ws.kbar[(((long long)b * a.Hkv + h) * a.Tn + t) * D + tid] = mean;
+  }
+  const double s = block_reduce_sum(contrib, red_s);
+  if (tid == 0) {
+    if (is_q) {
+      const long long o = ((long long)b * a.H + h) * a.Tm + t;
+      a.ws.sq[o] = s;
+      if (a.s_q_out) a.s_q_out[o] = s;
+    } else {
+      const long long o = ((long long)b * a.Hkv + h) * a.Tn + t;
+      a.ws.sk[o] = s;
+      if (a.s_k_out) a.s_k_out[o] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// shat_gemm: Shat = qbar kbar^T / sqrt(d) (eq. 7 before the -inf columns)
+// ---------------------------------------------------------------------------
+constexpr int kGT = 64;     // tile rows / cols
+constexpr int kGK = 16;     // d chunk
+__global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_sqrt_d) {
+  __shared__ double qt[kGK][kGT + 1];
+  __shared__ double kt[kGK][kGT + 1];
+  const int it = blockIdx.x, jt = blockIdx.y;
+  const int bh = blockIdx.z;
+  const int b = bh / a.H, h = bh % a.H;
+  const int hk = h / (a.H / a.Hkv);
+  const int i0 = it * kGT, j0 = jt * kGT;
+  if (a.causal) {
+    const int i_last = min(a.Tm - 1, i0 + kGT - 1);
+    const int last_q = min(a.N, (i_last + 1) * kBq) - 1;
+    if (j0 * kBk > last_q) return;
+  }
+  const double* qb = a.ws.qbar + ((long long)b * a.H + h) * a.Tm * a.d;
+  const double* kb = a.ws.kbar + ((long long)b * a.Hkv + hk) * a.Tn * a.d;
+  const int tid = threadIdx.x;
+  const int ti = tid / 16, tj = tid % 16;      // 4 x 4 outputs each
+  double acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  for (int k0 = 0; k0 < a.d; k0 += kGK) {
+    for (int e = tid; e < kGT * kGK; e += kThreads) {
+      const int r = e / kGK, kk = e % kGK;
+      const int gi = i0 + r, gj = j0 + r;
+      qt[kk][r] = gi < a.Tm ? qb[(long long)gi * a.d + k0 + kk] : 0.0;
+      kt[kk][r] = gj < a.Tn ? kb[(long long)gj * a.d + k0 + kk] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kGK; ++kk) {
+      double qv[4], kv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qv[x] = qt[kk][ti + 16 * x];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) kv[y] = kt[kk][tj + 16 * y];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(qv[x], kv[y], acc[x][y]);
+    }
+    __syncthreads();
+  }
+  double* out = a.ws.shat + ((long long)b * a.H + h) * a.Tm * a.Tn;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int gi = i0 + ti + 16 * x;
+    if (gi >= a.Tm) continue;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int gj = j0 + tj + 16 * y;
+      if (gj < a.Tn) out[(long long)gi * a.Tn + gj] = acc[x][y] * inv_sqrt_d;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// mask_rows: eqs. (7)-(9) for one query block row, then its compacted list
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int npad_max) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  double* pv = reinterpret_cast<double*>(dyn);                        // [npad_max]
+  int* pj = reinterpret_cast<int*>(dyn + 8 * (size_t)npad_max);         // [npad_max]
+  uint8_t* flag = dyn + 12 * (size_t)npad_max;                        // [Tn]: bit0 fix_k, bit1 kept
+  __shared__ double dred[kThreads];
+  __shared__ int ired[kThreads];
+  __shared__ int cut;
+
+  const long long row = blockIdx.x;               // (b*H + h)*Tm + i
+  const int i = (int)(row % a.Tm);
+  const int bh = (int)(row / a.Tm);
+  const int b = bh / a.H, h = bh % a.H;
+  const int hk = h / (a.H / a.Hkv);
+  const int tid = threadIdx.x;
+  const int last_q = min(a.N, (i + 1) * kBq) - 1;
+  const int n_live = a.causal ? min(a.Tn, last_q / kBk + 1) : a.Tn;
+  const bool fix_q = a.ws.sq[row] < a.theta;
+  const double* skr = a.ws.sk + ((long long)b * a.Hkv + hk) * a.Tn;
+  for (int j = tid; j < a.Tn; j += kThreads) flag[j] = (skr[j] < a.theta) ? 1 : 0;
+  __syncthreads();
+
+  if (!fix_q) {
+    // gather the live selective columns in ascending j
+    const int per = (n_live + kThreads - 1) / kThreads;
+    const int lo = min(n_live, tid * per), hi = min(n_live, lo + per);
+    int mine = 0;
+    for (int j = lo; j < hi; ++j) mine += (flag[j] & 1) ? 0 : 1;
+    int m;
+    int pos = block_excl_scan_int(mine, ired, m);
+    const double* srow = a.ws.shat + row * a.Tn;
+    for (int j = lo; j < hi; ++j)
+      if (!(flag[j] & 1)) {
+        pv[pos] = srow[j];
+        pj[pos] = j;
+        ++pos;
+      }
+    __syncthreads();
+    if (m > 0) {
+      int npad = 1;
+      while (npad < m) npad <<= 1;
+      // softmax over the m finite entries (eq. 8's P^[i])
+      double mx = kNegInfD;
+      for (int r = tid; r < m; r += kThreads) mx = fmax(mx, pv[r]);
+      mx = block_reduce_max(mx, dred);
+      double se = 0.0;
+      for (int r = tid; r < m; r += kThreads) {
+        const double e = exp(pv[r] - mx);
+        pv[r] = e;
+        se += e;
+      }
+      se = block_reduce_sum(se, dred);
+      for (int r = tid; r < npad; r += kThreads) {
+        if (r < m) {
+          pv[r] = pv[r] / se;
+        } else {
+          pv[r] = -1.0;                         // padding sorts after every probability
+          pj[r] = 0x7fffffff;
+        }
+      }
+      __syncthreads();
+      // bitonic sort into the order (P descending, j ascending)
+      for (int k = 2; k <= npad; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+          for (int x = tid; x < npad; x += kThreads) {
+            const int y = x ^ jj;
+            if (y > x) {
+              const double px = pv[x], py = pv[y];
+              const int jx = pj[x], jy = pj[y];
+              const bool y_first = py > px || (py == px && jy < jx);
+              const bool x_first = px > py || (px == py && jx < jy);
+              const bool swap = ((x & k) == 0) ? y_first : x_first;
+              if (swap) {
+                pv[x] = py;
+                pv[y] = px;
+                pj[x] = jy;
+                pj[y] = jx;
+              }
+            }
+          }
+          __syncthreads();
+        }
+      }
+      // TopCdf: keep sorted position r iff its exclusive prefix < tau * sum
+      const int per2 = (m + kThreads - 1) / kThreads;
+      const int lo2 = min(m, tid * per2), hi2 = min(m, lo2 + per2);
+      double part = 0.0;
+      for (int r = lo2; r < hi2; ++r) part += pv[r];
+      double total;
+      const double base = block_excl_scan_double(part, dred, total);
+      const double thresh = a.tau * total;
+      if (tid == 0) cut = m;
+      __syncthreads();
+      double run = base;
+      for (int r = lo2; r < hi2; ++r) {
+        if (run >= thresh) {
+          atomicMin(&cut, r);
+          break;
+        }
+        run += pv[r];
+      }
+      __syncthreads();
+      const int kept = cut;
+      for (int r = tid; r < kept; r += kThreads) flag[pj[r]] |= 2;
+      __syncthreads();
+    }
+  }
+
+  uint8_t* mg_row = a.mg + row * a.Tn;
+  const int Tn = a.Tn;
+  write_row(
+      Tn, [&](int j) { return j < n_live && (fix_q || (flag[j] & 3) != 0); }, mg_row,
+      a.row_cnt + row, a.row_idx + row * Tn, ired);
+}
+
+// compaction of a caller's mask (live tiles only)
+__global__ __launch_bounds__(kThreads) void compact_rows(const uint8_t* mg, int Tm, int Tn, int N,
+                                                         int causal, int32_t* cnt, uint16_t* idx) {
+  __shared__ int ired[kThreads];
+  const long long row = blockIdx.x;
+  const int i = (int)(row % Tm);
+  const int last_q = min(N, (i + 1) * kBq) - 1;
+  const int n_live = causal ? min(Tn, last_q / kBk + 1) : Tn;
+  const uint8_t* m = mg + row * Tn;
+  write_row(
+      Tn, [&](int j) { return j < n_live && m[j] != 0; }, nullptr, cnt + row, idx + row * Tn, ired);
+}
+
+}  // namespace
+
+hipError_t launch_compact(const uint8_t* mg, int64_t rows, int Tm, int Tn, int N, int causal,
+                          int32_t* cnt, uint16_t* idx, hipStream_t st) {
+  hipLaunchKernelGGL(compact_rows, dim3((unsigned)rows), dim3(kThreads), 0, st, mg, Tm, Tn, N,
+                     causal, cnt, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_predict(const PredictArgs& a, hipStream_t st) {
+  const long long pool_blocks = (long long)a.B * a.H * a.Tm + (long long)a.B * a.Hkv * a.Tn;
+  if (a.d == 64)
+    hipLaunchKernelGGL(pool_cossim<64>, dim3((unsigned)pool_blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(pool_cossim<128>, dim3((unsigned)pool_blocks), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g((unsigned)ceil_div(a.Tm, kGT), (unsigned)ceil_div(a.Tn, kGT), (unsigned)(a.B * a.H));
+  hipLaunchKernelGGL(shat_gemm, g, dim3(kThreads), 0, st, a, 1.0 / sqrt((double)a.d));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int npad = 1;
+  while (npad < a.Tn) npad <<= 1;
+  const size_t lds = 12 * (size_t)npad + (size_t)a.Tn;
+  hipLaunchKernelGGL(mask_rows, dim3((unsigned)((long long)a.B * a.H * a.Tm)), dim3(kThreads), lds, st,
+                     a, npad);
+  return hipGetLastError();
+}
+
+}  // namespace sparge

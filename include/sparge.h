@@ -1,0 +1,195 @@
+/*
+ * sparge.h -- C ABI of the MI355X (gfx950) SpargeAttn hot path.
+ *
+ * The method is SpargeAttn's two-stage online filter on a FlashAttention
+ * tiling.  Pages cited by title and section:
+ *   [Review]   "SpargeAttn: Accurate and Training-free Sparse Attention
+ *              Accelerating Any Model Inference" (xllm-io paper-review blog):
+ *              "Core formulas" eqs. (1)-(9), the sparse warp online softmax,
+ *              "Algorithm 1", the components table, "HilbertCurve Permutation".
+ *   [Rebuttal] "SpargeAttention: ..." OpenReview author rebuttal, replies
+ *              "Weaknesses1", "Weaknesses3", "Weaknesses3.1", "Weaknesses3.2".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are 4-D [B, heads, N, d] with the d axis contiguous.  A
+ *   sparge_tensor gives the sizes and the strides (in elements) of the other
+ *   three axes.  Base pointers and the byte strides must be 16-byte aligned.
+ * - Query blocks hold SPARGE_BQ rows, key/value blocks SPARGE_BK rows:
+ *   Tm = ceil(N / SPARGE_BQ), Tn = ceil(N / SPARGE_BK).  A ragged last block
+ *   holds the remaining rows.
+ * - GQA: query head h reads key/value head h / (H / H_kv); H % H_kv == 0.
+ * - Every device pointer is owned by the caller.  The library never
+ *   allocates device memory: scratch lives in the caller's `workspace`,
+ *   sized by sparge_workspace_size().
+ * - Every device call is asynchronous on `stream` (a hipStream_t; NULL is
+ *   the default stream).  Arguments are checked on the host before anything
+ *   is enqueued; on a negative return nothing was launched (SPARGE_EHIP: a
+ *   launch failed).  sparge_last_error() gives the calling thread's message.
+ * - N == 0, B == 0 or H == 0 is valid and launches nothing.
+ */
+#ifndef SPARGE_H
+#define SPARGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARGE_OK 0
+#define SPARGE_EINVAL (-1)        /* bad argument (null pointer, shape, range)  */
+#define SPARGE_EUNSUPPORTED (-2)  /* valid but outside this build (d, N, dtype) */
+#define SPARGE_EWORKSPACE (-3)    /* workspace smaller than sparge_workspace_size */
+#define SPARGE_EHIP (-4)          /* a HIP call or kernel launch failed           */
+
+#define SPARGE_BQ 128             /* query block rows b_q                        */
+#define SPARGE_BK 64              /* key/value block rows b_k                    */
+#define SPARGE_MAX_TN 4096        /* largest Tn (so N <= 262144)                 */
+
+/* element types */
+#define SPARGE_F16 0
+#define SPARGE_BF16 1
+#define SPARGE_I8 2
+#define SPARGE_F32 3              /* output only                                 */
+
+/* counters written by sparge_attn, int64 each, in this order */
+#define SPARGE_CNT_LIVE 0         /* live tiles (causal: tiles with a visible pair)   */
+#define SPARGE_CNT_QK_EXEC 1      /* live tiles with M_g = 1: QK^T computed          */
+#define SPARGE_CNT_QK_SKIP 2      /* live tiles with M_g = 0 (= LIVE - QK_EXEC)       */
+#define SPARGE_CNT_PV_EXEC 3      /* (tile, row group) pairs whose P~V ran            */
+#define SPARGE_CNT_PV_SKIP 4      /* pairs skipped by the lambda vote                 */
+#define SPARGE_CNT_PV_VOID 5      /* pairs with no visible key in the tile (causal)   */
+#define SPARGE_CNT_EMPTY_ROWS 6   /* query rows whose executed tiles held no key: O=0 */
+#define SPARGE_CNT_ROWS 7         /* query rows                                       */
+#define SPARGE_NUM_COUNTERS 8
+
+typedef struct {
+  int64_t B, H, N, d;   /* batch, heads, tokens, head dim                        */
+  int64_t sb, sh, sn;   /* element strides of the batch, head and token axes     */
+} sparge_tensor;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int sparge_version(void);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* sparge_last_error(void);
+
+/* Query rows that take the lambda decision together: b_q / c_w, one 64-lane
+ * wavefront of the attention kernel ([Review] sparse warp online softmax: the
+ * rows I_w of warp i_w). */
+int sparge_rows_per_wave(void);
+
+/* Bytes of device workspace any entry point below needs for Q of `q` and K/V
+ * of `k` (same B, N, d; k->H = H_kv).  0 for invalid shapes. */
+size_t sparge_workspace_size(const sparge_tensor* q, const sparge_tensor* k);
+
+/*
+ * Host only.  3D Hilbert order of a T x H x W token grid stored in raster
+ * order (token id (t*H + h)*W + w) ([Review] "HilbertCurve Permutation";
+ * [Rebuttal] Weaknesses3): every point gets its index on the Hilbert curve of
+ * the enclosing 2^b cube (Skilling's transpose algorithm, axes t, h, w, axis t
+ * most significant), and tokens are sorted by index.  perm[p] = token of rank
+ * p, inv[perm[p]] = p; both hold T*H*W int32 and are written by the library.
+ * Returns SPARGE_EINVAL for non-positive sizes or null pointers,
+ * SPARGE_EUNSUPPORTED if T*H*W >= 2^31.
+ */
+int sparge_hilbert_index(int T, int H, int W, int32_t* perm, int32_t* inv);
+
+/*
+ * Token gather or scatter along N of one tensor x -> y (same sizes; dtype
+ * SPARGE_F16, SPARGE_BF16, SPARGE_I8 or SPARGE_F32 only sets the element
+ * size; a row of d elements must be a multiple of 16 bytes).
+ * inverse = 0: y[b,h,p,:] = x[b,h,perm[p],:] (Q, K, V into curve order).
+ * inverse = 1: y[b,h,perm[p],:] = x[b,h,p,:] (the output back to raster order).
+ * perm is a device int32 array of N entries forming a permutation of 0..N-1
+ * (not checked on the device).  x and y must not overlap.
+ */
+int sparge_hilbert_permute(const void* x, const sparge_tensor* xs, void* y, const sparge_tensor* ys,
+                           int dtype, const int32_t* perm, int inverse, void* stream);
+
+/*
+ * Per-block symmetric int8 quantisation of Q and K ([Review] Algorithm 1
+ * step 2, components table: per-block quantisation, FP16 -> INT8).
+ * K first has its mean over all N tokens of each (b, kv head) subtracted.
+ * Per block X (SPARGE_BQ rows of Q, SPARGE_BK rows of K - mean):
+ *   delta = max|X| / 127 (1 if X is all zero), code = clamp(rint(X/delta), +-127)
+ * with ties to even, all in float64.  Outputs are contiguous:
+ *   q8 [B,H,N,d] int8, k8 [B,H_kv,N,d] int8, q_scale [B,H,Tm] float,
+ *   k_scale [B,H_kv,Tn] float (delta rounded to float).
+ * dtype is the element type of q and k (SPARGE_F16 or SPARGE_BF16).
+ */
+int sparge_quant_qk_int8(const void* q, const sparge_tensor* qs, const void* k,
+                         const sparge_tensor* ks, int dtype, int8_t* q8, int8_t* k8,
+                         float* q_scale, float* k_scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Stage 1: predict the block mask M_g ([Review] eqs. (4)-(9), Algorithm 1
+ * steps 3-5), in float64:
+ *   qbar_i, kbar_j = block means (eqs. 4-5);
+ *   s = mean pairwise cosine similarity of the block's tokens, computed as
+ *       || mean_a x_a / ||x_a|| ||^2 (eq. 6 as corrected in [Rebuttal]
+ *       Weaknesses3.1; a zero token counts as a zero unit vector);
+ *   Shat[i,j] = qbar_i . kbar_j / sqrt(d), -inf where s_k[j] < theta or the
+ *       key block is wholly in the future (causal) (eq. 7);
+ *   P^[i] = softmax of the finite entries; TopCdf keeps, in order of
+ *       descending P^ (ties: lower j), every entry whose exclusive prefix sum
+ *       is below tau * sum(P^[i]) (eq. 8);
+ *   M_g[i,:] = 1 on live tiles if s_q[i] < theta, M_g[:,j] = 1 on live tiles
+ *       if s_k[j] < theta (eq. 9); tiles wholly in the future are 0.
+ * Outputs (device, caller-allocated):
+ *   mg      [B,H,Tm,Tn] uint8 (0/1)
+ *   row_cnt [B,H,Tm] int32: number of ones in the row
+ *   row_idx [B,H,Tm,Tn] uint16: the row's j with M_g = 1, ascending, in the
+ *           first row_cnt entries (the rest is unspecified)
+ *   s_q [B,H,Tm], s_k [B,H_kv,Tn] float64 self-similarities (may be NULL).
+ * tau in (0, 1]; theta finite (theta > 1 makes every block fix: M_g = live).
+ * dtype: SPARGE_F16 or SPARGE_BF16.
+ */
+int sparge_predict_mask(const void* q, const sparge_tensor* qs, const void* k,
+                        const sparge_tensor* ks, int dtype, double tau, double theta, int causal,
+                        uint8_t* mg, int32_t* row_cnt, uint16_t* row_idx, double* s_q,
+                        double* s_k, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 2: block-sparse FlashAttention with the lambda rule ([Review] eqs.
+ * (1)-(3), sparse warp online softmax, Algorithm 1 steps 6-17).  For every
+ * query block i, key blocks j with M_g[i,j] = 1 on live tiles are visited in
+ * ascending j:  S = Q_i K_j^T / sqrt(d) (causal: -inf above the diagonal),
+ * m_new = max(m, rowmax S), P~ = exp(S - m_new),
+ * l = exp(m - m_new) l + rowsum P~, and, for each group of
+ * sparge_rows_per_wave() rows, unless every row with a finite rowmax has
+ * rowmax S - m_new < lambda (natural-log units), O = exp(m - m_new) O + P~ V.
+ * Finally O = O / l (0 where l = 0), stored in the element type of v.
+ *
+ * qk_dtype / pv_dtype: (F16, F16), (BF16, BF16), or (I8, F16) / (I8, BF16).
+ *   I8: q and k are the contiguous codes of sparge_quant_qk_int8 and
+ *   S = (q8 . k8) * q_scale[i] * k_scale[j] / sqrt(d); otherwise the scales
+ *   are ignored (may be NULL).  P~ is rounded to pv_dtype before P~V.
+ * o_dtype: pv_dtype, or SPARGE_F32 to store the float32 result before its
+ *   final rounding (the 16-bit output is exactly that value rounded to
+ *   nearest even).
+ * mg [B,H,Tm,Tn] uint8 is required.  row_cnt/row_idx (as written by
+ *   sparge_predict_mask) are optional: if both are NULL the row lists are
+ *   built from mg in the workspace.  Only live tiles are visited.
+ * lambda < 0 (-inf disables the rule).
+ * counts: int64[SPARGE_NUM_COUNTERS], overwritten (see SPARGE_CNT_*).
+ * pv_dbg: optional uint8 [B,H,Tm,Tn,SPARGE_BQ/sparge_rows_per_wave()] with
+ *   1 = group's P~V ran, 2 = skipped by the vote, 3 = no visible key,
+ *   0 = tile not visited; the caller clears it beforehand.
+ * o: [B,H,N,d] in o_dtype.
+ */
+int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+                const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+                int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+                const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+                double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARGE_H */

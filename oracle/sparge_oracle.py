@@ -271,16 +271,19 @@ def _scores_float(Qi: np.ndarray, Kj: np.ndarray) -> np.ndarray:
 def attend_row_block(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.ndarray, i: int,
                      lam: float, causal: bool, bq: int = BQ, bk: int = BK,
                      R: int = ROWS_PER_GROUP, skip_override: Optional[np.ndarray] = None,
-                     score_fn=None, vote_info: Optional[list] = None):
+                     score_fn=None, vote_info: Optional[list] = None,
+                     margins: Optional[np.ndarray] = None):
     """O_i for one query block i of one head, visiting key blocks j with
     M_g[i, j] = 1 in ascending j (eq. 1 with eqs. 2-3 and the lambda rule).
 
     ``skip_override`` [Tn, c_w] (int8: 1 execute, 2 skip, anything else = use
     the rule) replays another implementation's PV decisions.
     ``score_fn(rows, keys)`` replaces Q_i K_j^T / sqrt(d) (used by the int8
-    path).  Returns (O_i [n, d_v], counts dict, decisions [Tn, c_w] int8 with
-    1 = PV executed, 2 = skipped by the lambda vote, 3 = void group (no visible
-    key in the tile), 0 = tile not visited).
+    path).  ``margins`` [Tn, c_w], if given, receives max(m_loc - m_new) - lambda
+    of every voting group (the rule skips iff it is negative).  Returns
+    (O_i [n, d_v], counts dict, decisions [Tn, c_w] int8 with 1 = PV executed,
+    2 = skipped by the lambda vote, 3 = void group (no visible key in the
+    tile), 0 = tile not visited).
     """
     N, d = Qh.shape
     Tn = num_blocks(N, bk)
@@ -319,6 +322,8 @@ def attend_row_block(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.
         for g, gi in enumerate(groups):
             fin = np.isfinite(m_loc[gi])
             rule_skip = (not fin.any()) or (np.max(m_loc[gi][fin] - m_new[gi][fin]) < lam)
+            if margins is not None and fin.any():
+                margins[j, g] = np.max(m_loc[gi][fin] - m_new[gi][fin]) - lam
             if vote_info is not None and fin.any():
                 vote_info.append((j, g, float(np.max(m_loc[gi][fin] - m_new[gi][fin])),
                                   bool(np.any(m_new[gi] != m[gi]))))
@@ -348,13 +353,15 @@ def attend_row_block(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.
 def sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray, lam: float,
                      causal: bool, bq: int = BQ, bk: int = BK, R: int = ROWS_PER_GROUP,
                      blocks: Optional[Sequence[Tuple[int, int, int]]] = None,
-                     skip_override: Optional[np.ndarray] = None, quant: Optional[dict] = None):
+                     skip_override: Optional[np.ndarray] = None, quant: Optional[dict] = None,
+                     margins: Optional[np.ndarray] = None):
     """Stage 2 for Q [B, H, N, d], K/V [B, H_kv, N, d] and M_g [B, H, Tm, Tn].
 
     ``blocks`` restricts the work to (b, h, i) query blocks; the other rows of
     the returned O stay 0.  ``skip_override`` [B, H, Tm, Tn, c_w] replays PV
     decisions.  ``quant`` (from :func:`quantize_qk`) switches S to the int8
-    form.  Returns (O [B, H, N, d_v], counts dict summed over the blocks,
+    form.  ``margins`` [B, H, Tm, Tn, c_w] (NaN-filled by the caller) receives
+    every vote's margin, as in :func:`attend_row_block`.  Returns (O [B, H, N, d_v], counts dict summed over the blocks,
     decisions [B, H, Tm, Tn, c_w]).
     """
     B, H, N, d = Q.shape
@@ -379,7 +386,8 @@ def sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray
                 return acc * (dq[i] * dk[j]) / math.sqrt(d)
         ov = None if skip_override is None else skip_override[b, h, i]
         o, c, decision = attend_row_block(Q[b, h], K[b, hk], V[b, hk], mg[b, h, i], i, lam, causal,
-                                          bq, bk, R, ov, score_fn)
+                                          bq, bk, R, ov, score_fn,
+                                          margins=None if margins is None else margins[b, h, i])
         rows = block_rows(N, bq, i)
         O[b, h, rows.start:rows.stop] = o
         dec[b, h, i] = decision

@@ -1,0 +1,220 @@
+"""GPU parity of every hot-path kernel against the float64 oracle, on inputs
+the oracle finishes in seconds that still span several tiles and ragged tails.
+
+Every call goes through the C ABI (libsparge.so) via the ctypes binding.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import free_block_sparse_mask_amd as fb
+from free_block_sparse_mask_amd import inputs as I
+from oracle import sparge_oracle as O
+
+from gpu_common import (DEV, check_attention, check_mask, log, run_attn, to_bits, to_dev, widen_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(wid, **over):
+    w = I.workload(wid, **over)
+    q, k, v = I.make_qkv(w)
+    return w, q, k, v
+
+
+# (label, workload id, size overrides) -- all cover several tiles and a ragged tail
+CASES = [
+    ("tiny_full", 0, {}),
+    ("tiny_ragged", 0, {"N": 1000}),
+    ("llm_gqa_ragged", 2, {"N": 1000, "H": 4, "H_kv": 2}),
+    ("llm_small_causal", 2, {"N": 2048, "H": 2, "H_kv": 2}),
+    ("image_small", 1, {"N": 64 + 24 * 24, "H": 2, "H_kv": 2, "grid": (24, 24), "text_tokens": 64}),
+    ("video_small", 3, {"N": 4 * 16 * 12, "H": 2, "H_kv": 1, "grid": (4, 16, 12)}),
+]
+
+
+@pytest.mark.parametrize("label,wid,over", CASES, ids=[c[0] for c in CASES])
+def test_predict_mask_matches_oracle(label, wid, over):
+    w, q, k, v = _case(wid, **over)
+    log(f"[predict] {label}: B={w.B} H={w.H} Hkv={w.H_kv} N={w.N} d={w.d} causal={w.causal}")
+    qd, kd = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    torch.cuda.synchronize()
+    Q, K = O.widen(q, w.dtype), O.widen(k, w.dtype)
+    rep = check_mask(mask, Q, K, w.tau, w.theta, w.causal)
+    log(f"   near_theta={rep['near_theta']} ambiguous={rep['ambiguous']} s_err={rep['max_s_err']:.2e}")
+
+
+@pytest.mark.parametrize("label,wid,over", CASES, ids=[c[0] for c in CASES])
+def test_attention_given_oracle_mask(label, wid, over):
+    w, q, k, v = _case(wid, **over)
+    log(f"[attn] {label}: B={w.B} H={w.H} Hkv={w.H_kv} N={w.N} d={w.d} causal={w.causal} lam={w.lam}")
+    Q, K, V = (O.widen(x, w.dtype) for x in (q, k, v))
+    ref = O.predict_mask(Q, K, w.tau, w.theta, w.causal)
+    mg = torch.from_numpy(ref["mg"].astype(np.uint8)).to(DEV)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    o, o32, counts, dbg = run_attn(qd, kd, vd, mg, w.lam, w.causal)
+    rep = check_attention(o32, counts, dbg, Q, K, V, ref["mg"], w.lam, w.causal, "f32")
+    log(f"   max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} flips={rep['lambda_flips']} "
+        f"counts={rep['counts']}")
+
+
+@pytest.mark.parametrize("dtype,d,causal", [("f16", 128, False), ("bf16", 64, True), ("bf16", 128, True),
+                                            ("f16", 64, False)])
+def test_attention_random_mask_edge_rows(dtype, d, causal):
+    """A random mask with empty block rows, lambda strong enough to skip, and a
+    ragged N; also lambda = -inf (plain block-sparse attention)."""
+    N, H, Hkv = 777, 3, 1
+    rng = np.random.default_rng(5)
+    Qf = rng.standard_normal((1, H, N, d)) * 2.0
+    Kf = rng.standard_normal((1, Hkv, N, d)) * 2.0
+    Kf[0, 0, :64] += 3.0 * Qf[0, 0, :64].mean(axis=0)        # a dominant early block
+    Vf = rng.standard_normal((1, Hkv, N, d))
+    q, k, v = (I.to_bits(x, dtype) for x in (Qf, Kf, Vf))
+    Q, K, V = (O.widen(x, dtype) for x in (q, k, v))
+    Tm, Tn = O.num_blocks(N, 128), O.num_blocks(N, 64)
+    mg_np = rng.random((1, H, Tm, Tn)) < 0.6
+    mg_np[0, 0, 2] = False                                     # an empty row block
+    mg_np[0, 1, :, 0] = True
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    mg = torch.from_numpy(mg_np.astype(np.uint8)).to(DEV)
+    for lam in (-2.0, -math.inf):
+        log(f"[attn-random] dtype={dtype} d={d} causal={causal} lam={lam}")
+        o, o32, counts, dbg = run_attn(qd, kd, vd, mg, lam, causal)
+        rep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32")
+        log(f"   max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} counts={rep['counts']}")
+        assert rep["counts"]["empty_rows"] >= 128
+        if lam == -2.0:
+            assert rep["counts"]["pv_skip"] > 0
+
+
+def test_attention_with_predicted_lists_equals_mask_path():
+    """The row lists written by predict_mask and the lists built from M_g give
+    bit-identical outputs."""
+    w, q, k, v = _case(2, N=1500, H=4, H_kv=2)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    o1, c1, _ = fb.attn(qd, kd, vd, mask, w.lam, w.causal)
+    o2, c2, _ = fb.attn(qd, kd, vd, mask.mg, w.lam, w.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(c1, c2)
+
+
+def test_dense_limit_matches_brute_force():
+    """theta > 1 and lambda = -inf: the whole GPU path is dense attention."""
+    w, q, k, v = _case(2, N=900, H=2, H_kv=1)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    o, mask, counts = fb.sparge_attention(qd, kd, vd, 0.5, 2.0, -math.inf, True)
+    torch.cuda.synchronize()
+    Q, K, V = (O.widen(x, w.dtype) for x in (q, k, v))
+    ref = O.dense_attention(Q, K, V, True)
+    o32, _, _ = fb.attn(qd, kd, vd, mask, -math.inf, True, out_f32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o32.to(o.dtype))
+    og = o32.cpu().double().numpy()
+    assert np.max(np.abs(og - ref)) <= 1e-2 and O.rel_l1(ref, og) <= 5e-3
+    c = fb.counts_dict(counts)
+    assert c["qk_skip"] == 0 and c["pv_skip"] == 0
+
+
+def test_quant_codes_match_oracle():
+    for wid, over in ((4, {"N": 1100, "H": 4, "H_kv": 2}), (0, {"N": 700})):
+        w, q, k, v = _case(wid, **over)
+        log(f"[quant] wid={wid} N={w.N} H={w.H} Hkv={w.H_kv} d={w.d}")
+        qd, kd = to_dev(q, w.dtype), to_dev(k, w.dtype)
+        q8, k8, qs, ks = fb.quant_qk_int8(qd, kd)
+        torch.cuda.synchronize()
+        Q, K = O.widen(q, w.dtype), O.widen(k, w.dtype)
+        ref = O.quantize_qk(Q, K)
+        near_q = ref["q_tie_dist"] < 1e-6
+        near_k = ref["k_tie_dist"] < 1e-6
+        gq = q8.cpu().numpy().astype(np.float64)
+        gk = k8.cpu().numpy().astype(np.float64)
+        assert np.array_equal(gq[~near_q], ref["q_codes"][~near_q])
+        assert np.array_equal(gk[~near_k], ref["k_codes"][~near_k])
+        assert np.array_equal(qs.cpu().numpy(), ref["q_scale"].astype(np.float32))
+        assert np.array_equal(ks.cpu().numpy(), ref["k_scale"].astype(np.float32))
+        log(f"   near-tie codes: q={int(near_q.sum())} k={int(near_k.sum())}")
+
+
+def test_int8_attention_matches_oracle():
+    w, q, k, _ = _case(4, N=1100, H=4, H_kv=2)
+    v = I.make_tensor(w, I.TENSOR_V, dtype="f16")
+    Q, K = O.widen(q, w.dtype), O.widen(k, w.dtype)
+    V = O.widen(v, "f16")
+    qd, kd = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    vd = to_dev(v, "f16")
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    q8, k8, qs, ks = fb.quant_qk_int8(qd, kd)
+    o, o32, counts, dbg = run_attn(q8, k8, vd, mask, w.lam, w.causal, q_scale=qs, k_scale=ks)
+    ref_mask = O.predict_mask(Q, K, w.tau, w.theta, w.causal)["mg"]
+    assert np.array_equal(mask.mg.cpu().numpy().astype(bool), ref_mask)
+    quant = O.quantize_qk(Q, K)
+    rep = check_attention(o32, counts, dbg, Q, K, V, ref_mask, w.lam, w.causal, "f32", quant=quant,
+                          int8=True)
+    log(f"[int8] rel_l1={rep['rel_l1']:.2e} cos={rep['cos']:.6f} max_abs={rep['max_abs']:.2e} "
+        f"flips={rep['lambda_flips']}")
+    # against the unquantised oracle the error is the quantisation error
+    o_float, _, _ = O.sparse_attention(Q, K, V, ref_mask, w.lam, w.causal)
+    og = O.widen(to_bits(o), "f16")
+    log(f"   vs float path: rel_l1={O.rel_l1(o_float, og):.2e}")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_hilbert_permute_roundtrip(dtype, d):
+    T, Hg, Wg = 4, 16, 12
+    N = T * Hg * Wg
+    rng = np.random.default_rng(3)
+    x = I.to_bits(rng.standard_normal((2, 3, N, d)), dtype)
+    perm, inv = fb.hilbert_index(T, Hg, Wg)
+    perm_d = torch.from_numpy(perm).to(DEV)
+    xd = to_dev(x, dtype)
+    y = fb.hilbert_permute(xd, perm_d)
+    z = fb.hilbert_permute(y, perm_d, inverse=True)
+    torch.cuda.synchronize()
+    p_ref, _ = O.hilbert_permutation(T, Hg, Wg)
+    assert np.array_equal(to_bits(y), O.permute_tokens(x, p_ref))
+    assert np.array_equal(to_bits(z), x)
+    # a strided (non-contiguous heads) input
+    big = torch.zeros((2, 3, N, d + 8), dtype=xd.dtype, device=DEV)
+    big[..., :d] = xd
+    ys = fb.hilbert_permute(big[..., :d], perm_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(ys), O.permute_tokens(x, p_ref))
+
+
+def test_video_pipeline_with_hilbert_order():
+    """Gather -> predict -> attend -> scatter on the GPU vs the oracle doing the
+    same steps with its own Hilbert order."""
+    w, q, k, v = _case(3, N=4 * 16 * 12, H=2, H_kv=2, grid=(4, 16, 12))
+    T, Hg, Wg = w.grid
+    perm, _ = fb.hilbert_index(T, Hg, Wg)
+    perm_d = torch.from_numpy(perm).to(DEV)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    o, mask, counts = fb.sparge_attention(qd, kd, vd, w.tau, w.theta, w.lam, w.causal, perm=perm_d)
+    torch.cuda.synchronize()
+    p_ref, _ = O.hilbert_permutation(T, Hg, Wg)
+    Qp, Kp, Vp = (O.permute_tokens(O.widen(x, w.dtype), p_ref) for x in (q, k, v))
+    rep = check_mask(mask, Qp, Kp, w.tau, w.theta, w.causal)
+    o_ref, _, _ = O.sparse_attention(Qp, Kp, Vp, rep["ref_mg"], w.lam, w.causal)
+    o_ref = O.unpermute_tokens(o_ref, p_ref)
+    # the float32 result of the same attention, scattered back on the GPU
+    qp, kp, vp = (fb.hilbert_permute(x, perm_d) for x in (qd, kd, vd))
+    o32, _, _ = fb.attn(qp, kp, vp, mask, w.lam, w.causal, out_f32=True)
+    o32 = fb.hilbert_permute(o32, perm_d, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o32.to(o.dtype))
+    og = o32.cpu().double().numpy()
+    log(f"[video] rel_l1={O.rel_l1(o_ref, og):.2e} max_abs={np.max(np.abs(o_ref - og)):.2e}")
+    assert np.max(np.abs(o_ref - og)) <= 1e-2 and O.rel_l1(o_ref, og) <= 5e-3
+
+
+def test_empty_sequence_is_a_no_op():
+    qd = torch.zeros((1, 2, 0, 64), dtype=torch.float16, device=DEV)
+    mask = fb.predict_mask(qd, qd, 0.9, 0.5, True)
+    o, counts, _ = fb.attn(qd, qd, qd, mask, -5.0, True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and int(counts.sum()) == 0
