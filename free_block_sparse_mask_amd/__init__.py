@@ -197,7 +197,7 @@ def attn(q, k, v, mask, lam: float, causal: bool, q_scale=None, k_scale=None, co
         o = out
     counts = torch.empty(8, dtype=torch.int64, device=dev) if counts is None else counts
     pv_dbg = torch.zeros((B, H, Tm, Tn, BQ // 32), dtype=torch.uint8, device=dev) if dbg else None
-    ws = (workspace(q, k) if cnt is None else None) if ws is None else ws
+    ws = workspace(q, k) if ws is None else ws
     rc = lib().sparge_attn(_ptr(q), ctypes.byref(desc(q)), _ptr(k), ctypes.byref(desc(k)),
                            _ptr(v), ctypes.byref(desc(v)), _ptr(o), ctypes.byref(desc(o)),
                            _dtype_code(q), _dtype_code(v), _dtype_code(o), _ptr(q_scale),

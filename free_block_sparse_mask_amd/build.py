@@ -51,6 +51,10 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # a kernel whose host stub was not emitted only shows up as an undefined
+    # symbol at load time: load the library here so the build fails instead
+    import ctypes
+    ctypes.CDLL(LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB

@@ -99,6 +99,7 @@ Workspace carve_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t
   w.kmean = reinterpret_cast<double*>(take(8 * (size_t)(B * Hkv * d)));
   w.list_cnt = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * H * Tm)));
   w.list_idx = reinterpret_cast<uint16_t*>(take(2 * (size_t)(B * H * Tm * Tn)));
+  w.vt = reinterpret_cast<unsigned short*>(take(2 * (size_t)(B * Hkv * d * Tn * kBk)));
   w.total = off;
   return w;
 }
@@ -318,8 +319,8 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
   if (kind >= 2 && (!q_scale || !k_scale)) return fail(SPARGE_EINVAL, "int8 needs q_scale and k_scale");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(SPARGE_EINVAL, "q, k, v, o must be 16-byte aligned");
-  const bool need_ws = row_cnt == nullptr;
-  if (need_ws && (workspace == nullptr || workspace_bytes < sparge_workspace_size(qs, ks)))
+  const bool need_lists = row_cnt == nullptr;
+  if (workspace == nullptr || workspace_bytes < sparge_workspace_size(qs, ks))
     return fail(SPARGE_EWORKSPACE, "workspace needs %zu bytes", sparge_workspace_size(qs, ks));
 
   AttnArgs a{};
@@ -356,11 +357,13 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
   a.counts = reinterpret_cast<unsigned long long*>(counts);
   a.dbg = pv_dbg;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  void* base = reinterpret_cast<void*>(align256((size_t)workspace));
+  Workspace w = carve_workspace(base, a.B, a.H, a.Hkv, a.N, a.d);
+  a.vt = w.vt;
+  a.Np = (int64_t)a.Tn * kBk;
   hipError_t e = launch_zero_counts(a.counts, SPARGE_NUM_COUNTERS, st);
   if (e != hipSuccess) return hip_fail(e, "counter reset");
-  if (need_ws) {
-    void* base = reinterpret_cast<void*>(align256((size_t)workspace));
-    Workspace w = carve_workspace(base, a.B, a.H, a.Hkv, a.N, a.d);
+  if (need_lists) {
     e = launch_compact(mg, (int64_t)a.B * a.H * a.Tm, a.Tm, a.Tn, a.N, causal, w.list_cnt, w.list_idx, st);
     if (e != hipSuccess) return hip_fail(e, "mask compaction launch");
     a.row_cnt = w.list_cnt;

@@ -39,9 +39,10 @@ struct Workspace {
   // int8 quantisation: per-chunk column sums of K, then the mean
   double* ksum_part;   // [B,Hkv,kQuantChunks,d]
   double* kmean;       // [B,Hkv,d]
-  // attention: row lists built from a caller's mask
+  // attention: row lists built from a caller's mask, and V transposed
   int32_t* list_cnt;   // [B,H,Tm]
   uint16_t* list_idx;  // [B,H,Tm,Tn]
+  unsigned short* vt;  // [B,Hkv,d,Tn*64] 16-bit V^T, zero past N
   size_t total;
 };
 
@@ -57,6 +58,8 @@ struct AttnArgs {
   const void* k;
   const void* v;
   void* o;
+  unsigned short* vt;  // workspace V^T [B,Hkv,d,Np]
+  int64_t Np;          // padded token count of V^T rows (Tn * 64)
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;

@@ -13,12 +13,15 @@
 // * S^T = K_j Q_i^T on v_mfma_f32_32x32x16 (bf16/f16) or v_mfma_i32_32x32x32_i8:
 //   the accumulator layout of S^T puts one query row per lane (lane % 32) and
 //   16 of its 32 keys per 32x32 tile in registers, so the row max is an
-//   in-lane reduction plus one exchange with lane ^ 32, and P~ can feed the
-//   P~V MFMA as its B operand straight from registers.
-// * O^T = V_j^T P~^T: V is transposed into LDS as it is staged, so the A
-//   operand (8 keys of one d_v column) is two 8-byte LDS reads.
-// * K_j and V_j for the next listed block are fetched into registers while
-//   the current block is computed (one LDS buffer, two barriers per block).
+//   in-lane reduction plus one exchange with lane ^ 32, and P~ feeds the P~V
+//   MFMA as its B operand straight from registers.
+// * O^T = V_j^T P~^T with V^T from a once-per-call transposed copy of V, so
+//   the A operand (8 keys of one d_v column) is two 8-byte LDS reads.
+// * K_j and V_j^T tiles go from global memory straight into LDS
+//   (global_load_lds_dwordx4, no staging registers) into two alternating
+//   buffers: the next listed tile streams in while the current one is used,
+//   with one barrier per tile.  The 16-byte granules of each LDS row are
+//   XOR-swizzled by row so the MFMA operand reads hit distinct banks.
 // * The key blocks come from the compacted ascending list of M_g's ones.
 // * Grid order: heaviest query blocks (largest i) first; when the number of
 //   (batch, kv head) pairs is a multiple of 8, all query heads of one kv head
@@ -31,7 +34,11 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool BF16>
 __device__ __forceinline__ unsigned int pack2(float a, float b) {
@@ -55,6 +62,14 @@ __device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes land
+// at lds_dst + 16 L (lds_dst must be the same for the whole wavefront).
+__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_dst, 16, 0, 0);
 }
 
 // Workgroup id -> (b, h, i); returns false for padding workgroups.
@@ -91,21 +106,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd(AttnArgs p) {
   constexpr bool I8 = KIND >= 2;
   constexpr bool PVBF = (KIND == 1 || KIND == 3);
-  constexpr int KSB = I8 ? (D + 16) : (D + 8) * 2;   // K row stride in bytes (16-byte aligned)
-  constexpr int VSE = kBk + 4;                       // V^T row stride in 16-bit elements
-  constexpr int K_BYTES = kBk * KSB;
-  constexpr int V_BYTES = D * VSE * 2;
-  constexpr int DCH = D / 8;                         // 16-byte chunks per 16-bit row
-  constexpr int KCH = I8 ? D / 16 : DCH;             // 16-byte chunks per K row
-  constexpr int K_LOADS = kBk * KCH / kThreads;      // per thread
-  constexpr int V_UNITS = 16 * DCH;                  // (4 keys x 8 columns) units
-  constexpr int QS = I8 ? D / 32 : D / 16;           // k-steps of the QK^T MFMA
-  constexpr int OT = D / 32;                         // 32-column tiles of O^T
+  constexpr int KROW = I8 ? D : 2 * D;          // bytes per K row
+  constexpr int KG = KROW / 16;                 // 16-byte granules per K row
+  constexpr int KSW = 16 / KG;                  // rows sharing one swizzle step
+  constexpr int K_BYTES = kBk * KROW;
+  constexpr int VROW = kBk * 2;                 // bytes per V^T row (64 keys)
+  constexpr int V_BYTES = D * VROW;
+  constexpr int KCW = K_BYTES / 1024 / kWavesPerBlock;   // 1 KB chunks per wave
+  constexpr int VCW = V_BYTES / 1024 / kWavesPerBlock;
+  constexpr int QS = I8 ? D / 32 : D / 16;      // k-steps of the QK^T MFMA
+  constexpr int OT = D / 32;                    // 32-column tiles of O^T
+  static_assert(KCW >= 1 && VCW >= 1, "tile must span every wave");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[K_BYTES + V_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][K_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][V_BYTES];
   __shared__ unsigned long long red[kWavesPerBlock][4];
-  unsigned char* klds = smem;
-  unsigned short* vlds = reinterpret_cast<unsigned short*>(smem + K_BYTES);
 
   int b, h, i;
   if (!map_block(p, b, h, i)) return;
@@ -146,89 +161,98 @@ void attn_fwd(AttnArgs p) {
     kbase = static_cast<const unsigned char*>(p.k) + (b * p.k_sb + hk * p.k_sh) * 2;
     k_sn_bytes = p.k_sn * 2;
   }
-  const unsigned short* vbase = static_cast<const unsigned short*>(p.v) + b * p.v_sb + hk * p.v_sh;
+  const unsigned char* vtbase =
+      reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + hk) * D) * p.Np * 2;
   const float* kscale_row = I8 ? p.k_scale + (long long)(b * p.Hkv + hk) * p.Tn : nullptr;
 
   const long long row_id = (long long)(b * p.H + h) * p.Tm + i;
   const int cnt = p.row_cnt[row_id];
   const uint16_t* list = p.row_idx + row_id * p.Tn;
 
-  // ---- staging registers for the next K/V tile ----
-  u32x4 kreg[K_LOADS > 0 ? K_LOADS : 1];
-  u32x4 vreg[4];
-  const int vu_c = tid % DCH, vu_g = tid / DCH;      // V unit: column chunk, key group
+  // ---- global -> LDS tile loads (one 1 KB chunk per wave instruction) ----
+  // Lane offsets inside a tile are loop invariant; the tile base is uniform,
+  // so every load is a scalar base plus a 32-bit lane offset.
+  uint32_t k_off[KCW], v_off[VCW];
+  int k_row[KCW];
+#pragma unroll
+  for (int c = 0; c < KCW; ++c) {
+    const int chunk = wave * KCW + c;
+    const int row = chunk * (1024 / KROW) + lane / KG;
+    const int g = (lane % KG) ^ ((row / KSW) % KG);
+    k_row[c] = row;
+    k_off[c] = (uint32_t)(row * k_sn_bytes) + (uint32_t)(g * 16);
+  }
+#pragma unroll
+  for (int c = 0; c < VCW; ++c) {
+    const int chunk = wave * VCW + c;
+    const int row = chunk * 8 + lane / 8;                    // d_v row of V^T
+    const int g = (lane % 8) ^ ((row / 2) % 8);
+    v_off[c] = (uint32_t)(row * p.Np * 2) + (uint32_t)(g * 16);
+  }
+  auto issue = [&](int j, int st) {
+    const unsigned char* kt0 = kbase + (long long)j * kBk * k_sn_bytes;
+    const bool ragged = j * kBk + kBk > p.N;
+#pragma unroll
+    for (int c = 0; c < KCW; ++c) {
+      uint32_t off = k_off[c];
+      if (ragged) {                                          // rows past N re-read row N-1 (masked later)
+        const int row = min(k_row[c], p.N - 1 - j * kBk);
+        off = (uint32_t)(row * k_sn_bytes) + (k_off[c] - (uint32_t)(k_row[c] * k_sn_bytes));
+      }
+      dma16(kt0 + off, &kbuf[st][(wave * KCW + c) * 1024]);
+    }
+    const unsigned char* vt0 = vtbase + (long long)j * kBk * 2;
+#pragma unroll
+    for (int c = 0; c < VCW; ++c)
+      dma16(vt0 + v_off[c], &vbuf[st][(wave * VCW + c) * 1024]);
+  };
 
-  auto fetch = [&](int j) {
-#pragma unroll
-    for (int r = 0; r < K_LOADS; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / KCH, ch = c % KCH;
-      const int key = j * kBk + row;
-      kreg[r] = key < p.N ? *reinterpret_cast<const u32x4*>(kbase + key * k_sn_bytes + ch * 16)
-                          : u32x4{0, 0, 0, 0};
-    }
-    if (tid < V_UNITS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j * kBk + 4 * vu_g + r;
-        vreg[r] = key < p.N ? *reinterpret_cast<const u32x4*>(vbase + (long long)key * p.v_sn + 8 * vu_c)
-                            : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int r = 0; r < K_LOADS; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / KCH, ch = c % KCH;
-      *reinterpret_cast<u32x4*>(klds + row * KSB + ch * 16) = kreg[r];
-    }
-    if (tid < V_UNITS) {
-      // transpose 4 keys x 8 columns: column e gets keys 4g..4g+3 as one 8-byte word
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const int sh = (e & 1) * 16;
-        const unsigned int k0 = (vreg[0][w] >> sh) & 0xffffu, k1 = (vreg[1][w] >> sh) & 0xffffu;
-        const unsigned int k2 = (vreg[2][w] >> sh) & 0xffffu, k3 = (vreg[3][w] >> sh) & 0xffffu;
-        u32x2 word = {k0 | (k1 << 16), k2 | (k3 << 16)};
-        *reinterpret_cast<u32x2*>(vlds + (8 * vu_c + e) * VSE + 4 * vu_g) = word;
-      }
-    }
-  };
+  // LDS read bases: the swizzled offset of k-step s is base ^ (32 s), and the
+  // second 32-row tile sits a fixed distance further (see the layout above).
+  const int ksw = (l32 / KSW) % KG;
+  uint32_t k_rd = (uint32_t)(l32 * KROW) + (uint32_t)((ksw & ~1) * 16) + (uint32_t)((hl ^ (ksw & 1)) * 16);
+  const int vsw = (l32 / 2) % 8;
+  uint32_t v_rd = (uint32_t)(l32 * VROW) + (uint32_t)(vsw * 16) + (uint32_t)(8 * hl);
 
   f32x16 oacc[OT];
 #pragma unroll
   for (int t = 0; t < OT; ++t) oacc[t] = f32x16{};
   float m_run = kNegInf;      // running max, log2 units
   float l_half = 0.0f;        // this lane half's share of the row sum
-  unsigned long long n_exec = 0, n_skip = 0, n_void = 0, n_qk = 0;
+  // per-wavefront tallies (wave-uniform; one workgroup visits at most Tn tiles)
+  int n_exec = 0, n_skip = 0, n_void = 0, n_qk = 0;
+  uint8_t* dbg_row = p.dbg != nullptr ? p.dbg + row_id * p.Tn * kWavesPerBlock + wave : nullptr;
+  const bool write_dbg = dbg_row != nullptr && q0 < p.N;
 
-  if (cnt > 0) fetch(list[0]);
+  if (cnt > 0) issue(list[0], 0);
   for (int n = 0; n < cnt; ++n) {
+    const int st = n & 1;
     const int j = list[n];
-    __syncthreads();                      // previous tile fully consumed
-    stage();
-    __syncthreads();
-    if (n + 1 < cnt) fetch(list[n + 1]);  // overlaps with the math below
-    if (j >= n_live) continue;            // not a live tile (never in lists from M_g of live tiles)
+    wait_vmem();                          // this wave's loads of tile n have landed
+    __syncthreads();                      // everyone's have; everyone is done with tile n-1
+    if (n + 1 < cnt) issue(list[n + 1], st ^ 1);
+    if (j >= n_live) continue;            // not a live tile (lists from M_g of live tiles never hold one)
     ++n_qk;
+    const unsigned char* kt = kbuf[st];
+    const unsigned char* vt = vbuf[st];
+    asm volatile("" : "+v"(k_rd), "+v"(v_rd));
 
-    // ---- S^T = K_j Q_i^T : two 32-key x 32-row tiles ----
+    // ---- S^T = K_j Q_i^T : two 32-key x 32-row tiles (raw dot products) ----
     float sv[2][16];
+    float c_scale = p.scale_log2;
     if constexpr (I8) {
-      const float sc = qscale * kscale_row[j] * p.scale_log2;
+      c_scale = qscale * kscale_row[j] * p.scale_log2;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         i32x16 acc = {};
 #pragma unroll
         for (int s = 0; s < QS; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(klds + (32 * t + l32) * KSB + 32 * s + 16 * hl);
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kt + t * 32 * KROW + (k_rd ^ (32u * s)));
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
                                                      __builtin_bit_cast(i32x4, qf[s]), acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[r] * sc;
+        for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[r];
       }
     } else {
 #pragma unroll
@@ -236,11 +260,11 @@ void attn_fwd(AttnArgs p) {
         f32x16 acc = {};
 #pragma unroll
         for (int s = 0; s < QS; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(klds + (32 * t + l32) * KSB + 32 * s + 16 * hl);
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kt + t * 32 * KROW + (k_rd ^ (32u * s)));
           acc = mfma16<KIND == 1>(a, qf[s], acc);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sv[t][r] = acc[r] * p.scale_log2;
+        for (int r = 0; r < 16; ++r) sv[t][r] = acc[r];
       }
     }
 
@@ -258,67 +282,67 @@ void attn_fwd(AttnArgs p) {
         }
     }
 
-    // ---- online softmax (eq. 1), log2 units ----
+    // ---- online softmax (eq. 1) in log2 units; the scale is folded into an FMA ----
     float mx = kNegInf;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const bool finite_row = mx > kNegInf;
+    const float mloc = mx * c_scale;                 // c_scale > 0: max commutes with the scale
+    const float m_new = fmaxf(m_run, mloc);
+    const bool finite_row = mloc > kNegInf;
     // lambda vote over the wavefront's 32 rows
-    const bool wants_pv = finite_row && !(mx - m_new < p.lam_log2);
+    const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
     const bool any_finite = __any(finite_row);
     const bool exec = __any(wants_pv);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = (m_new == kNegInf) ? 1.0f : exp2f(m_run - m_new);
+    const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
     float psum = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[t][r] = exp2f(sv[t][r] - m_use);
-        psum += sv[t][r];
-      }
-    l_half = alpha * l_half + psum;
-    m_run = m_new;
-
     unsigned char code;
-    if (!any_finite) {
-      code = 3;
-      ++n_void;
-    } else if (!exec) {
-      code = 2;
-      ++n_skip;
-    } else {
-      code = 1;
-      ++n_exec;
-      if (__any(alpha != 1.0f)) {
+    if (!exec) {
+      // P~ only feeds the row sum l (Algorithm 1 computes it before the M_pv test)
 #pragma unroll
-        for (int t = 0; t < OT; ++t) oacc[t] *= alpha;
-      }
-      // ---- O^T += V_j^T P~^T ----
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) psum += fast_exp2(fmaf(sv[t][r], c_scale, neg_m));
+      code = any_finite ? 2 : 3;
+      n_skip += any_finite ? 1 : 0;
+      n_void += any_finite ? 0 : 1;
+    } else {
+      // P~ in the P~V input type, packed as the B operand of the four k-steps
+      u32x4 pb[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int tt = s >> 1, r0 = 8 * (s & 1);
-        u32x4 pb;
-        pb[0] = pack2<PVBF>(sv[tt][r0 + 0], sv[tt][r0 + 1]);
-        pb[1] = pack2<PVBF>(sv[tt][r0 + 2], sv[tt][r0 + 3]);
-        pb[2] = pack2<PVBF>(sv[tt][r0 + 4], sv[tt][r0 + 5]);
-        pb[3] = pack2<PVBF>(sv[tt][r0 + 6], sv[tt][r0 + 7]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = fast_exp2(fmaf(sv[tt][r0 + 2 * e], c_scale, neg_m));
+          const float x1 = fast_exp2(fmaf(sv[tt][r0 + 2 * e + 1], c_scale, neg_m));
+          psum += x0 + x1;
+          pb[s][e] = pack2<PVBF>(x0, x1);
+        }
+      }
+      code = 1;
+      ++n_exec;
+#pragma unroll
+      for (int t = 0; t < OT; ++t) oacc[t] *= alpha;
+      // ---- O^T += V_j^T P~^T ----
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t lo_off = v_rd ^ (32u * s), hi_off = lo_off ^ 16u;
 #pragma unroll
         for (int t = 0; t < OT; ++t) {
-          const unsigned short* vrow = vlds + (32 * t + l32) * VSE + 16 * s + 4 * hl;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + t * 32 * VROW + lo_off);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + t * 32 * VROW + hi_off);
           const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[t] = mfma16<PVBF>(a, pb, oacc[t]);
+          oacc[t] = mfma16<PVBF>(a, pb[s], oacc[t]);
         }
       }
     }
-    if (p.dbg != nullptr && lane == 0 && q0 < p.N)
-      p.dbg[(row_id * p.Tn + j) * kWavesPerBlock + wave] = code;
+    l_half = alpha * l_half + psum;
+    m_run = m_new;
+    if (write_dbg && lane == 0) dbg_row[j * kWavesPerBlock] = code;
   }
 
   // ---- epilogue: O / l ----
@@ -358,9 +382,9 @@ void attn_fwd(AttnArgs p) {
   const bool empty = qvalid && hl == 0 && !(l_tot > 0.0f);
   const unsigned long long n_empty = __popcll(__ballot(empty));
   if (lane == 0) {
-    red[wave][0] = n_exec;
-    red[wave][1] = n_skip;
-    red[wave][2] = n_void;
+    red[wave][0] = (unsigned long long)n_exec;
+    red[wave][1] = (unsigned long long)n_skip;
+    red[wave][2] = (unsigned long long)n_void;
     red[wave][3] = n_empty;
   }
   __syncthreads();
@@ -375,13 +399,41 @@ void attn_fwd(AttnArgs p) {
       em += red[w][3];
     }
     atomicAdd(p.counts + SPARGE_CNT_LIVE, (unsigned long long)n_live);
-    atomicAdd(p.counts + SPARGE_CNT_QK_EXEC, n_qk);
+    atomicAdd(p.counts + SPARGE_CNT_QK_EXEC, (unsigned long long)n_qk);
     atomicAdd(p.counts + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - n_qk));
     atomicAdd(p.counts + SPARGE_CNT_PV_EXEC, e);
     atomicAdd(p.counts + SPARGE_CNT_PV_SKIP, s);
     atomicAdd(p.counts + SPARGE_CNT_PV_VOID, v);
     atomicAdd(p.counts + SPARGE_CNT_EMPTY_ROWS, em);
     atomicAdd(p.counts + SPARGE_CNT_ROWS, (unsigned long long)(last_q - i * kBq + 1));
+  }
+}
+
+// V [B,Hkv,N,D] (strided, 16-bit) -> V^T [B,Hkv,D,Np], zero past N; 64 x 64 tiles.
+__global__ __launch_bounds__(kThreads) void transpose_v(AttnArgs p) {
+  __shared__ __attribute__((aligned(16))) unsigned short tile[64][72];
+  const int kt = blockIdx.x, dt = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int tid = threadIdx.x;
+  const unsigned short* vb = static_cast<const unsigned short*>(p.v) + b * p.v_sb + hk * p.v_sh;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int key = tid / 8 + 32 * r, ch = tid % 8;
+    const int gk = kt * 64 + key;
+    u32x4 val = {0, 0, 0, 0};
+    if (gk < p.N) val = *reinterpret_cast<const u32x4*>(vb + (long long)gk * p.v_sn + dt * 64 + 8 * ch);
+    *reinterpret_cast<u32x4*>(&tile[key][8 * ch]) = val;
+  }
+  __syncthreads();
+  unsigned short* out = p.vt + ((long long)bh * p.d) * p.Np;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int dv = tid / 8 + 32 * r, kc = tid % 8;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (unsigned int)tile[8 * kc + 2 * e][dv] | ((unsigned int)tile[8 * kc + 2 * e + 1][dv] << 16);
+    *reinterpret_cast<u32x4*>(out + (long long)(dt * 64 + dv) * p.Np + kt * 64 + 8 * kc) = w;
   }
 }
 
@@ -417,6 +469,10 @@ hipError_t launch_zero_counts(unsigned long long* counts, int n, hipStream_t st)
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+  dim3 g((unsigned)(a.Np / 64), (unsigned)(a.d / 64), (unsigned)(a.B * a.Hkv));
+  hipLaunchKernelGGL(transpose_v, g, dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return a.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
 }
 

@@ -75,7 +75,8 @@ def test_attn_rejects_bad_arguments_before_launch():
     assert _attn(q, k, k, q, mg=None) == fb.SPARGE_EINVAL               # M_g required
     assert _attn(q, k, k, q, counts=None) == fb.SPARGE_EINVAL
     assert _attn(q, k, k, q, cnt=FAKE) == fb.SPARGE_EINVAL              # lists come in pairs
-    assert _attn(q, k, k, q) == fb.SPARGE_EWORKSPACE                    # lists built in workspace
+    assert _attn(q, k, k, q) == fb.SPARGE_EWORKSPACE                    # V^T and lists in workspace
+    assert _attn(q, k, k, q, cnt=FAKE, idx=FAKE) == fb.SPARGE_EWORKSPACE
     assert _attn(q, k, k, q, qk=fb.I8, pv=fb.F16) == fb.SPARGE_EINVAL   # int8 needs scales
     strided = fb.SpargeTensor(1, 4, 256, 128, 4 * 256 * 136, 256 * 136, 136)
     assert _attn(strided, k, k, q, qk=fb.I8, pv=fb.F16, scales=(FAKE, FAKE)) == fb.SPARGE_EINVAL
