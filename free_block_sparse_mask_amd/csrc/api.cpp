@@ -295,6 +295,9 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
     return fail(SPARGE_EINVAL, "v must have the shape of k");
   if (os->B != qs->B || os->H != qs->H || os->N != qs->N || os->d != qs->d)
     return fail(SPARGE_EINVAL, "o must have the shape of q");
+  // the attention kernel forms per-lane offsets of 64 K rows in 32 bits
+  if (ks->sn * qk_es * (int64_t)kBk >= (1LL << 31) || qs->sn * qk_es * (int64_t)kBk >= (1LL << 31))
+    return fail(SPARGE_EUNSUPPORTED, "token stride too large (64 rows must span < 2 GiB)");
   if (kind >= 2) {
     // int8 codes are the contiguous output of sparge_quant_qk_int8
     const int64_t d = qs->d;

@@ -15,8 +15,9 @@
 //   16 of its 32 keys per 32x32 tile in registers, so the row max is an
 //   in-lane reduction plus one exchange with lane ^ 32, and P~ feeds the P~V
 //   MFMA as its B operand straight from registers.
-// * O^T = V_j^T P~^T with V^T from a once-per-call transposed copy of V, so
-//   the A operand (8 keys of one d_v column) is two 8-byte LDS reads.
+// * O^T = V_j^T P~^T with V^T from a once-per-call transposed copy of V whose
+//   keys are ordered so that the A operand (the 8 keys one lane half feeds
+//   one MFMA) is a single 16-byte LDS read.
 // * K_j and V_j^T tiles go from global memory straight into LDS
 //   (global_load_lds_dwordx4, no staging registers) into two alternating
 //   buffers: the next listed tile streams in while the current one is used,
@@ -26,6 +27,8 @@
 // * Grid order: heaviest query blocks (largest i) first; when the number of
 //   (batch, kv head) pairs is a multiple of 8, all query heads of one kv head
 //   land on one XCD (workgroup id % 8), so their K/V tiles share that XCD's L2.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace sparge {
@@ -36,21 +39,32 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
+// in the other, so combining the two gives every lane the pair (l, l ^ 32).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two 16-bit values (round to nearest even) in one 32-bit word;
+// the vector form maps to one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32
 template <bool BF16>
 __device__ __forceinline__ unsigned int pack2(float a, float b) {
-  if constexpr (BF16) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (unsigned int)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned int)__builtin_bit_cast(unsigned short, y) << 16);
-  } else {
-    _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (unsigned int)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned int)__builtin_bit_cast(unsigned short, y) << 16);
-  }
+  const f32x2 v = {a, b};
+  if constexpr (BF16)
+    return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2));
+  else
+    return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, f16x2));
 }
 
 template <bool BF16>
@@ -170,41 +184,39 @@ void attn_fwd(AttnArgs p) {
   const uint16_t* list = p.row_idx + row_id * p.Tn;
 
   // ---- global -> LDS tile loads (one 1 KB chunk per wave instruction) ----
-  // Lane offsets inside a tile are loop invariant; the tile base is uniform,
-  // so every load is a scalar base plus a 32-bit lane offset.
-  uint32_t k_off[KCW], v_off[VCW];
-  int k_row[KCW];
-#pragma unroll
-  for (int c = 0; c < KCW; ++c) {
-    const int chunk = wave * KCW + c;
-    const int row = chunk * (1024 / KROW) + lane / KG;
-    const int g = (lane % KG) ^ ((row / KSW) % KG);
-    k_row[c] = row;
-    k_off[c] = (uint32_t)(row * k_sn_bytes) + (uint32_t)(g * 16);
-  }
-#pragma unroll
-  for (int c = 0; c < VCW; ++c) {
-    const int chunk = wave * VCW + c;
-    const int row = chunk * 8 + lane / 8;                    // d_v row of V^T
-    const int g = (lane % 8) ^ ((row / 2) % 8);
-    v_off[c] = (uint32_t)(row * p.Np * 2) + (uint32_t)(g * 16);
-  }
-  auto issue = [&](int j, int st) {
-    const unsigned char* kt0 = kbase + (long long)j * kBk * k_sn_bytes;
+  // A chunk holds R = 1024 / row_bytes consecutive rows.  The swizzle repeats
+  // every 16 rows, so chunk c of wavefront w is placed at rows
+  // 16 (c (4/G) + w / G) + R (w % G) + lane / granules_per_row, G = 16 / R:
+  // every chunk of a wavefront then has the same lane offset (one register),
+  // and the chunk only moves the uniform base.
+  constexpr int KR = 1024 / KROW, KGRP = 16 / KR;
+  constexpr int VR = 1024 / VROW, VGRP = 16 / VR;
+  const int k_row0 = 16 * (wave / KGRP) + KR * (wave % KGRP) + lane / KG;
+  const uint32_t k_off = (uint32_t)(k_row0 * k_sn_bytes) + (uint32_t)(((lane % KG) ^ ((k_row0 / KSW) % KG)) * 16);
+  const int v_row0 = 16 * (wave / VGRP) + VR * (wave % VGRP) + lane / 8;
+  const uint32_t v_off = (uint32_t)(v_row0 * p.Np * 2) + (uint32_t)(((lane % 8) ^ ((v_row0 / 2) % 8)) * 16);
+  auto issue_k = [&](int j, int st) {
     const bool ragged = j * kBk + kBk > p.N;
 #pragma unroll
     for (int c = 0; c < KCW; ++c) {
-      uint32_t off = k_off[c];
-      if (ragged) {                                          // rows past N re-read row N-1 (masked later)
-        const int row = min(k_row[c], p.N - 1 - j * kBk);
-        off = (uint32_t)(row * k_sn_bytes) + (k_off[c] - (uint32_t)(k_row[c] * k_sn_bytes));
+      const int row_c = 16 * c * (4 / KGRP);                  // rows added by chunk c
+      const unsigned char* src = kbase + ((long long)j * kBk + row_c) * k_sn_bytes + k_off;
+      if (ragged) {
+        // rows past N re-read row N-1 (their scores are masked); the address is
+        // formed from the clamped key in signed 64-bit arithmetic
+        const long long key = (long long)j * kBk + row_c + min(k_row0, p.N - 1 - j * kBk - row_c);
+        src = kbase + key * k_sn_bytes + (k_off - (uint32_t)(k_row0 * k_sn_bytes));
       }
-      dma16(kt0 + off, &kbuf[st][(wave * KCW + c) * 1024]);
+      dma16(src, &kbuf[st][(row_c + 16 * (wave / KGRP) + KR * (wave % KGRP)) * KROW]);
     }
-    const unsigned char* vt0 = vtbase + (long long)j * kBk * 2;
+  };
+  auto issue_v = [&](int j, int st) {
 #pragma unroll
-    for (int c = 0; c < VCW; ++c)
-      dma16(vt0 + v_off[c], &vbuf[st][(wave * VCW + c) * 1024]);
+    for (int c = 0; c < VCW; ++c) {
+      const int row_c = 16 * c * (4 / VGRP);
+      const unsigned char* base = vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2;
+      dma16(base + v_off, &vbuf[st][(row_c + 16 * (wave / VGRP) + VR * (wave % VGRP)) * VROW]);
+    }
   };
 
   // LDS read bases: the swizzled offset of k-step s is base ^ (32 s), and the
@@ -212,7 +224,25 @@ void attn_fwd(AttnArgs p) {
   const int ksw = (l32 / KSW) % KG;
   uint32_t k_rd = (uint32_t)(l32 * KROW) + (uint32_t)((ksw & ~1) * 16) + (uint32_t)((hl ^ (ksw & 1)) * 16);
   const int vsw = (l32 / 2) % 8;
-  uint32_t v_rd = (uint32_t)(l32 * VROW) + (uint32_t)(vsw * 16) + (uint32_t)(8 * hl);
+  uint32_t v_rd = (uint32_t)(l32 * VROW) + (uint32_t)((vsw & ~1) * 16) + (uint32_t)((hl ^ (vsw & 1)) * 16);
+
+  // S^T of one tile: two 32-key x 32-row MFMA accumulators (raw dot products)
+  using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
+  auto qk = [&](const unsigned char* kt, Acc (&acc)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      acc[t] = Acc{};
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt + t * 32 * KROW + (k_rd ^ (32u * s)));
+        if constexpr (I8)
+          acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                        __builtin_bit_cast(i32x4, qf[s]), acc[t], 0, 0, 0);
+        else
+          acc[t] = mfma16<KIND == 1>(a, qf[s], acc[t]);
+      }
+    }
+  };
 
   f32x16 oacc[OT];
 #pragma unroll
@@ -220,55 +250,35 @@ void attn_fwd(AttnArgs p) {
   float m_run = kNegInf;      // running max, log2 units
   float l_half = 0.0f;        // this lane half's share of the row sum
   // per-wavefront tallies (wave-uniform; one workgroup visits at most Tn tiles)
-  int n_exec = 0, n_skip = 0, n_void = 0, n_qk = 0;
+  int n_exec = 0, n_skip = 0, n_void = 0;
   uint8_t* dbg_row = p.dbg != nullptr ? p.dbg + row_id * p.Tn * kWavesPerBlock + wave : nullptr;
   const bool write_dbg = dbg_row != nullptr && q0 < p.N;
 
-  if (cnt > 0) issue(list[0], 0);
-  for (int n = 0; n < cnt; ++n) {
-    const int st = n & 1;
+  // Software pipeline: while the softmax of listed tile n runs on the VALU,
+  // the QK^T MFMAs of tile n+1 are already in flight.  K_{n+2} and V_{n+1}
+  // stream into the buffers that tiles n and n-1 have released.  The MFMAs of
+  // the next tile and the whole softmax of this one form one branch-free
+  // block, so the scheduler can interleave them; only P~V sits behind the
+  // wavefront's vote.  After the last tile the next-tile MFMAs recompute a
+  // stale buffer and are discarded.
+  auto step = [&](int n, Acc (&cur)[2], Acc (&nxt)[2]) {
     const int j = list[n];
-    wait_vmem();                          // this wave's loads of tile n have landed
+    wait_vmem();                          // K_{n+1} and V_n have landed (this wave's part)
     __syncthreads();                      // everyone's have; everyone is done with tile n-1
-    if (n + 1 < cnt) issue(list[n + 1], st ^ 1);
-    if (j >= n_live) continue;            // not a live tile (lists from M_g of live tiles never hold one)
-    ++n_qk;
-    const unsigned char* kt = kbuf[st];
-    const unsigned char* vt = vbuf[st];
     asm volatile("" : "+v"(k_rd), "+v"(v_rd));
+    if (n + 2 < cnt) issue_k(list[n + 2], n & 1);
+    if (n + 1 < cnt) issue_v(list[n + 1], (n + 1) & 1);
+    const unsigned char* vt = vbuf[n & 1];
+    const unsigned char* kn = kbuf[(n + 1) & 1];
 
-    // ---- S^T = K_j Q_i^T : two 32-key x 32-row tiles (raw dot products) ----
-    float sv[2][16];
     float c_scale = p.scale_log2;
-    if constexpr (I8) {
-      c_scale = qscale * kscale_row[j] * p.scale_log2;
+    if constexpr (I8) c_scale = qscale * kscale_row[j] * p.scale_log2;
+    float sv[2][16];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        i32x16 acc = {};
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int s = 0; s < QS; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kt + t * 32 * KROW + (k_rd ^ (32u * s)));
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
-                                                     __builtin_bit_cast(i32x4, qf[s]), acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[r];
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < QS; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kt + t * 32 * KROW + (k_rd ^ (32u * s)));
-          acc = mfma16<KIND == 1>(a, qf[s], acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[t][r] = acc[r];
-      }
-    }
-
-    // ---- masking: keys beyond N, causal future, rows beyond N ----
+      for (int r = 0; r < 16; ++r) sv[t][r] = (float)cur[t][r];
+    // masking: keys beyond N, causal future, rows beyond N (diagonal and ragged tiles only)
     const bool need_mask = (j * kBk + kBk > p.N) || (q0 + kRowsPerWave > p.N) ||
                            (CAUSAL && j * kBk + kBk - 1 > q0);
     if (need_mask) {
@@ -282,13 +292,16 @@ void attn_fwd(AttnArgs p) {
         }
     }
 
+    // ---- next tile's S^T on the matrix cores ----
+    qk(kn, nxt);
+
     // ---- online softmax (eq. 1) in log2 units; the scale is folded into an FMA ----
     float mx = kNegInf;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_halves(mx);
     const float mloc = mx * c_scale;                 // c_scale > 0: max commutes with the scale
     const float m_new = fmaxf(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
@@ -298,55 +311,63 @@ void attn_fwd(AttnArgs p) {
     const bool exec = __any(wants_pv);
     const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
     const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
+    // P~ (eq. 1); it always feeds l (Algorithm 1 computes it before the M_pv
+    // test) and is packed in the P~V input type as the B operand of 4 k-steps
     float psum = 0.0f;
-    unsigned char code;
-    if (!exec) {
-      // P~ only feeds the row sum l (Algorithm 1 computes it before the M_pv test)
+    u32x4 pb[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int s = 0; s < 4; ++s) {
+      const int tt = s >> 1, r0 = 8 * (s & 1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) psum += fast_exp2(fmaf(sv[t][r], c_scale, neg_m));
-      code = any_finite ? 2 : 3;
-      n_skip += any_finite ? 1 : 0;
-      n_void += any_finite ? 0 : 1;
-    } else {
-      // P~ in the P~V input type, packed as the B operand of the four k-steps
-      u32x4 pb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int tt = s >> 1, r0 = 8 * (s & 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = fast_exp2(fmaf(sv[tt][r0 + 2 * e], c_scale, neg_m));
-          const float x1 = fast_exp2(fmaf(sv[tt][r0 + 2 * e + 1], c_scale, neg_m));
-          psum += x0 + x1;
-          pb[s][e] = pack2<PVBF>(x0, x1);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = fast_exp2(fmaf(sv[tt][r0 + 2 * e], c_scale, neg_m));
+        const float x1 = fast_exp2(fmaf(sv[tt][r0 + 2 * e + 1], c_scale, neg_m));
+        psum += x0 + x1;
+        pb[s][e] = pack2<PVBF>(x0, x1);
       }
-      code = 1;
-      ++n_exec;
+    }
+    l_half = alpha * l_half + psum;
+    m_run = m_new;
+    const unsigned char code = exec ? 1 : (any_finite ? 2 : 3);
+    n_exec += exec ? 1 : 0;
+    n_skip += (!exec && any_finite) ? 1 : 0;
+    n_void += any_finite ? 0 : 1;
+    if (exec) {
 #pragma unroll
       for (int t = 0; t < OT; ++t) oacc[t] *= alpha;
       // ---- O^T += V_j^T P~^T ----
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t lo_off = v_rd ^ (32u * s), hi_off = lo_off ^ 16u;
+        const uint32_t off = v_rd ^ (32u * s);
 #pragma unroll
         for (int t = 0; t < OT; ++t) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + t * 32 * VROW + lo_off);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + t * 32 * VROW + hi_off);
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+          const u32x4 a = *reinterpret_cast<const u32x4*>(vt + t * 32 * VROW + off);
           oacc[t] = mfma16<PVBF>(a, pb[s], oacc[t]);
         }
       }
     }
-    l_half = alpha * l_half + psum;
-    m_run = m_new;
     if (write_dbg && lane == 0) dbg_row[j * kWavesPerBlock] = code;
+  };
+
+  Acc s_a[2], s_b[2];
+  if (cnt > 0) {
+    issue_k(list[0], 0);
+    issue_v(list[0], 0);
+    if (cnt > 1) issue_k(list[1], 1);
+    wait_vmem();
+    __syncthreads();
+    qk(kbuf[0], s_a);
   }
+  int n = 0;
+  for (; n + 1 < cnt; n += 2) {           // unrolled by two so the score buffers swap roles
+    step(n, s_a, s_b);
+    step(n + 1, s_b, s_a);
+  }
+  if (n < cnt) step(n, s_a, s_b);
+  const int n_qk = cnt;
 
   // ---- epilogue: O / l ----
-  const float l_tot = l_half + xor32(l_half);
+  const float l_tot = sum_halves(l_half);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qvalid && p.out_f32) {
     float* ob = static_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)qrow * p.o_sn;
@@ -429,10 +450,16 @@ __global__ __launch_bounds__(kThreads) void transpose_v(AttnArgs p) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int dv = tid / 8 + 32 * r, kc = tid % 8;
+    // positions 8kc..8kc+7 of the row; inside each group of 16 keys the
+    // middle quarters are swapped, so the 16 bytes at positions 8h..8h+7 hold
+    // keys {4h..4h+3, 8+4h..8+4h+3}: the 8 keys one lane half feeds one MFMA
+    const int base = 16 * (kc / 2) + 4 * (kc % 2);
     u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (unsigned int)tile[8 * kc + 2 * e][dv] | ((unsigned int)tile[8 * kc + 2 * e + 1][dv] << 16);
+    for (int e = 0; e < 4; ++e) {
+      const int key = base + (e < 2 ? 2 * e : 8 + 2 * (e - 2));
+      w[e] = (unsigned int)tile[key][dv] | ((unsigned int)tile[key + 1][dv] << 16);
+    }
     *reinterpret_cast<u32x4*>(out + (long long)(dt * 64 + dv) * p.Np + kt * 64 + 8 * kc) = w;
   }
 }
