@@ -24,9 +24,8 @@
 //   with one barrier per tile.  The 16-byte granules of each LDS row are
 //   XOR-swizzled by row so the MFMA operand reads hit distinct banks.
 // * The key blocks come from the compacted ascending list of M_g's ones.
-// * Grid order: heaviest query blocks (largest i) first; when the number of
-//   (batch, kv head) pairs is a multiple of 8, all query heads of one kv head
-//   land on one XCD (workgroup id % 8), so their K/V tiles share that XCD's L2.
+// * Grid order: heaviest query blocks (largest i) first, in phases of a few
+//   kv heads with one kv head per XCD (see map_block).
 #include <type_traits>
 
 #include "common.hpp"
@@ -86,22 +85,27 @@ __device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* l
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_dst, 16, 0, 0);
 }
 
-// Workgroup id -> (b, h, i); returns false for padding workgroups.
+// Workgroup id -> (b, h, i).  Workgroups are dispatched to the 8 XCDs round
+// robin (id % 8).  When the query heads of 8 / G kv heads fill one row of 8
+// slots (G = H / H_kv), the grid runs in phases of 8 / G kv heads: slot s of
+// every row is XCD s, which always serves query head s % G of kv head
+// s / G of the phase, heaviest block rows first.  Each XCD's L2 then sees one
+// kv head, and only 8 / G kv heads (a few tens of MB to a few hundred MB of
+// K and V) are live in the Infinity Cache at a time.  Other shapes fall back
+// to block rows outermost, heaviest first.
 __device__ __forceinline__ bool map_block(const AttnArgs& p, int& b, int& h, int& i) {
   const int group = p.H / p.Hkv;
   const int pairs = p.B * p.Hkv;
   const long long id = blockIdx.x;
-  if ((pairs & 7) == 0) {
-    const int per_xcd = pairs >> 3;
-    const int xcd = (int)(id & 7);
+  if ((8 % group) == 0 && (pairs % (8 / group)) == 0) {
+    const int per_phase = 8 / group;
+    const int slot = (int)(id & 7);
     const long long k = id >> 3;
-    const long long per_i = (long long)per_xcd * group;
-    const int irank = (int)(k / per_i);
-    const int rem = (int)(k % per_i);
-    const int pp = rem / group, g = rem % group;
-    const int pair = xcd + 8 * pp;
+    const int phase = (int)(k / p.Tm);
+    const int irank = (int)(k % p.Tm);
+    const int pair = phase * per_phase + slot / group;
     b = pair / p.Hkv;
-    h = (pair % p.Hkv) * group + g;
+    h = (pair % p.Hkv) * group + slot % group;
     i = p.Tm - 1 - irank;
   } else {
     const long long bh = (long long)p.B * p.H;
