@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=40,
+    ap.add_argument("--cpu-blocks", type=int, default=150,
                     help="query blocks of head 0 the CPU oracle attends (sample size)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
@@ -60,6 +60,17 @@ def dense_equiv_flops(N, d, H, causal):
 
 def executed_flops(c, d, bq=128, bk=64, rows=32):
     return c["qk_exec"] * 2.0 * bq * bk * d + c["pv_exec"] * 2.0 * rows * bk * d
+
+
+def attn_source_digest() -> str:
+    """sha256 over the attention kernel's sources: HBM counters taken on an
+    older kernel no longer describe this one."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("k_attn.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "free_block_sparse_mask_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def cpu_baseline(w, q, k, v, nblocks):
@@ -159,7 +170,8 @@ def main():
         try:
             with open(args.traffic_json) as f:
                 tj = json.load(f)
-            traffic = tj.get("attn_fwd_bytes_per_launch")
+            if tj.get("kernel_source_sha256") == attn_source_digest():
+                traffic = tj.get("attn_fwd_bytes_per_launch")
         except Exception:
             traffic = None
     result = {
