@@ -100,6 +100,10 @@ Workspace carve_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t
   w.list_cnt = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * H * Tm)));
   w.list_idx = reinterpret_cast<uint16_t*>(take(2 * (size_t)(B * H * Tm * Tn)));
   w.vt = reinterpret_cast<unsigned short*>(take(2 * (size_t)(B * Hkv * d * Tn * kBk)));
+  w.row_m = reinterpret_cast<float*>(take(4 * (size_t)(B * H * N)));
+  w.row_l = reinterpret_cast<float*>(take(4 * (size_t)(B * H * N)));
+  w.ulist = reinterpret_cast<uint32_t*>(take(4 * (size_t)(B * H * Tm * Tn)));
+  w.ucnt = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * H * Tm)));
   w.total = off;
   return w;
 }
@@ -364,6 +368,10 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
   Workspace w = carve_workspace(base, a.B, a.H, a.Hkv, a.N, a.d);
   a.vt = w.vt;
   a.Np = (int64_t)a.Tn * kBk;
+  a.row_m = w.row_m;
+  a.row_l = w.row_l;
+  a.ulist = w.ulist;
+  a.ucnt = w.ucnt;
   hipError_t e = launch_zero_counts(a.counts, SPARGE_NUM_COUNTERS, st);
   if (e != hipSuccess) return hip_fail(e, "counter reset");
   if (need_lists) {

@@ -43,6 +43,12 @@ struct Workspace {
   int32_t* list_cnt;   // [B,H,Tm]
   uint16_t* list_idx;  // [B,H,Tm,Tn]
   unsigned short* vt;  // [B,Hkv,d,Tn*64] 16-bit V^T, zero past N
+  // attention pass 1 -> pass 2: per-row softmax statistics and, per query
+  // block, the listed tiles on which at least one wavefront ran P~V
+  float* row_m;        // [B,H,N] final running max (log2 units)
+  float* row_l;        // [B,H,N] final row sum l
+  uint32_t* ulist;     // [B,H,Tm,Tn] j | (wavefront mask << 16), ascending j
+  int32_t* ucnt;       // [B,H,Tm]
   size_t total;
 };
 
@@ -60,6 +66,10 @@ struct AttnArgs {
   void* o;
   unsigned short* vt;  // workspace V^T [B,Hkv,d,Np]
   int64_t Np;          // padded token count of V^T rows (Tn * 64)
+  float* row_m;        // workspace: pass 1 final max per row (log2 units)
+  float* row_l;        // workspace: pass 1 row sum per row
+  uint32_t* ulist;     // workspace: executed-tile lists (j | mask << 16)
+  int32_t* ucnt;       // workspace: their lengths
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;

@@ -6,7 +6,28 @@
 // formulas" eqs. (1)-(3), the sparse warp online softmax paragraph and
 // "Algorithm 1" (steps 6-17).
 //
-// Design (CDNA4 first, not the pages' CUDA warp layout):
+// Two kernels, one pass over the listed tiles each:
+//
+// attn_stats (pass 1) runs the online softmax of eq. (1) over the listed key
+//   blocks of one query block in ascending order: S = Q K^T, the running max
+//   m, the row sum l, and the lambda vote of every wavefront on every tile.
+//   The vote only needs the running max, so pass 1 decides exactly which
+//   (tile, wavefront) pairs run P~V without touching V.  It writes m and l of
+//   every row and, per query block, the ascending list of tiles on which at
+//   least one wavefront voted to run P~V, with the wavefront mask.
+// attn_pv (pass 2) visits only those tiles.  A wavefront that voted on a
+//   tile recomputes its S (the same MFMA sequence, so the same values) and
+//   adds exp(S - m_final) V to O; O / l is stored at the end.  Unrolling the
+//   rescaling of eq. (1) gives the same sum: a tile's P~ = exp(S - m_t) is
+//   multiplied by exp(m_t - m_final) through the later rescales, and a
+//   skipped group leaves m unchanged.
+//
+// At the workloads this path is built for, about one listed tile in eight
+// has a voting wavefront, so V (half of the bytes of a K/V pass) is read for
+// a small fraction of the tiles, and pass 1 can give all its LDS to a deep
+// ring of K tiles.
+//
+// Layout (CDNA4 first, not the pages' CUDA warp layout):
 // * One workgroup of 4 wavefronts per query block i of 128 rows; wavefront w
 //   owns rows [32w, 32w + 32) of the block, so the lambda vote is one ballot
 //   over a 64-lane wavefront (both lane halves hold the same 32 rows).
@@ -18,12 +39,12 @@
 // * O^T = V_j^T P~^T with V^T from a once-per-call transposed copy of V whose
 //   keys are ordered so that the A operand (the 8 keys one lane half feeds
 //   one MFMA) is a single 16-byte LDS read.
-// * K_j and V_j^T tiles go from global memory straight into LDS
-//   (global_load_lds_dwordx4, no staging registers) into two alternating
-//   buffers: the next listed tile streams in while the current one is used,
-//   with one barrier per tile.  The 16-byte granules of each LDS row are
+// * Tiles go from global memory straight into LDS (global_load_lds_dwordx4)
+//   into a ring of slots.  These loads are issued as inline assembly: the
+//   compiler neither tracks them nor adds waits for them, and every wait on
+//   them is explicit (a vmcnt that leaves the younger tiles in flight,
+//   followed by a barrier).  The 16-byte granules of each LDS row are
 //   XOR-swizzled by row so the MFMA operand reads hit distinct banks.
-// * The key blocks come from the compacted ascending list of M_g's ones.
 // * Grid order: heaviest query blocks (largest i) first, in phases of a few
 //   kv heads with one kv head per XCD (see map_block).
 #include <type_traits>
@@ -35,8 +56,6 @@ namespace sparge {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
 // in the other, so combining the two gives every lane the pair (l, l ^ 32).
@@ -77,12 +96,50 @@ __device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// LDS byte address of a pointer into shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-// 16 bytes per lane from global memory straight into LDS: lane L's bytes land
-// at lds_dst + 16 L (lds_dst must be the same for the whole wavefront).
-__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_dst, 16, 0, 0);
+__device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<const unsigned char*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
+// 16 bytes per lane from sbase + voff (sbase wavefront-uniform) into LDS at
+// lds + 16 * lane (lds wavefront-uniform).  M0 carries the LDS address; no
+// other code in these kernels uses M0 (no LDS-DMA builtins, no indirect
+// register indexing, no messages).  The instruction writes no register, so
+// nothing the compiler allocates is pending when the statement ends.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const unsigned char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Waits until at most N vector-memory operations of this wavefront are in
+// flight and its LDS operations are done, then joins the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// the same with N = pending * PER, pending (wavefront-uniform) clamped to [0, P]
+template <int PER, int P>
+__device__ __forceinline__ void wait_pending(int pending) {
+  if constexpr (P <= 0) {
+    wait_barrier<0>();
+  } else {
+    if (pending >= P)
+      wait_barrier<P * PER>();
+    else
+      wait_pending<PER, P - 1>(pending);
+  }
 }
 
 // Workgroup id -> (b, h, i).  Workgroups are dispatched to the 8 XCDs round
@@ -118,186 +175,238 @@ __device__ __forceinline__ bool map_block(const AttnArgs& p, int& b, int& h, int
   return i >= 0 && b < p.B;
 }
 
-// KIND: 0 f16, 1 bf16, 2 int8 QK + f16 PV, 3 int8 QK + bf16 PV
+// ---------------------------------------------------------------------------
+// Geometry shared by both passes
+// ---------------------------------------------------------------------------
+template <int D, int KIND>
+struct Geo {
+  static constexpr bool I8 = KIND >= 2;
+  static constexpr bool PVBF = (KIND == 1 || KIND == 3);
+  static constexpr int KROW = I8 ? D : 2 * D;          // bytes per K row
+  static constexpr int KG = KROW / 16;                 // 16-byte granules per K row
+  static constexpr int KSW = 16 / KG;                  // rows sharing one swizzle step
+  static constexpr int K_BYTES = kBk * KROW;
+  static constexpr int KCW = K_BYTES / 1024 / kWavesPerBlock;   // 1 KB chunks per wave
+  static constexpr int KR = 1024 / KROW;               // K rows per 1 KB chunk
+  static constexpr int KGRP = 16 / KR;
+  static constexpr int VROW = kBk * 2;                 // bytes per V^T row (64 keys)
+  static constexpr int V_BYTES = D * VROW;
+  static constexpr int VCW = V_BYTES / 1024 / kWavesPerBlock;
+  static constexpr int VR = 1024 / VROW;
+  static constexpr int VGRP = 16 / VR;
+  static constexpr int QS = I8 ? D / 32 : D / 16;      // k-steps of the QK^T MFMA
+  static constexpr int OT = D / 32;                    // 32-column tiles of O^T
+  static constexpr int EPM = 32 / (2 * QS);            // scores per lane per QK^T MFMA
+  // pass 1: K ring slots (64 KB or less, so two workgroups fit a CU with the lists)
+  static constexpr int NSLOT = I8 ? 4 : (K_BYTES >= 16384 ? 4 : 8);
+  // pass 2: (K, V^T) slots
+  static constexpr int E_BYTES = K_BYTES + V_BYTES;
+  static constexpr int NS2 = (65536 / E_BYTES) >= 4 ? 4 : 2;
+  static_assert(KCW >= 1 && VCW >= 1, "tile must span every wave");
+  static_assert(EPM * 2 * QS == 32, "scores must split evenly over the MFMAs");
+};
+
+template <int D, int KIND>
+size_t stats_lds_bytes(int Tn) {
+  using G = Geo<D, KIND>;
+  return (size_t)G::NSLOT * G::K_BYTES + (((size_t)2 * Tn + 15) & ~(size_t)15) + (size_t)4 * Tn +
+         (G::I8 ? (size_t)4 * Tn : 0);
+}
+template <int D, int KIND>
+size_t pv_lds_bytes(int Tn) {
+  using G = Geo<D, KIND>;
+  return (size_t)G::NS2 * G::E_BYTES + (size_t)4 * Tn + (G::I8 ? (size_t)4 * Tn : 0);
+}
+
+// Per-lane pieces common to both passes: Q fragment, K DMA offsets, read bases.
+template <int D, int KIND>
+struct Lane {
+  using G = Geo<D, KIND>;
+  int b, h, i, hk, tid, wave, lane, l32, hl, q0, qrow;
+  bool qvalid;
+  long long row_id;
+  u32x4 qf[G::QS];
+  float qscale;
+  const unsigned char* kbase;
+  long long k_sn_bytes;
+  int k_row0;
+  uint32_t k_gran, k_off;
+  uint32_t k_rd;
+
+  __device__ __forceinline__ void init(const AttnArgs& p, int b_, int h_, int i_) {
+    b = b_;
+    h = h_;
+    i = i_;
+    hk = h / (p.H / p.Hkv);
+    tid = threadIdx.x;
+    wave = tid >> 6;
+    lane = tid & 63;
+    l32 = lane & 31;
+    hl = lane >> 5;
+    q0 = i * kBq + wave * kRowsPerWave;
+    qrow = q0 + l32;
+    qvalid = qrow < p.N;
+    row_id = (long long)(b * p.H + h) * p.Tm + i;
+    if constexpr (G::I8) {
+      const int8_t* qb = static_cast<const int8_t*>(p.q) + ((long long)(b * p.H + h) * p.N) * D;
+#pragma unroll
+      for (int s = 0; s < G::QS; ++s)
+        qf[s] = qvalid ? *reinterpret_cast<const u32x4*>(qb + (long long)qrow * D + 32 * s + 16 * hl)
+                       : u32x4{0, 0, 0, 0};
+      qscale = p.q_scale[row_id];
+      kbase = static_cast<const unsigned char*>(p.k) + ((long long)(b * p.Hkv + hk) * p.N) * D;
+      k_sn_bytes = D;
+    } else {
+      const unsigned short* qb = static_cast<const unsigned short*>(p.q) + b * p.q_sb + h * p.q_sh;
+#pragma unroll
+      for (int s = 0; s < G::QS; ++s)
+        qf[s] = qvalid ? *reinterpret_cast<const u32x4*>(qb + (long long)qrow * p.q_sn + 16 * s + 8 * hl)
+                       : u32x4{0, 0, 0, 0};
+      qscale = 1.0f;
+      kbase = static_cast<const unsigned char*>(p.k) + (b * p.k_sb + hk * p.k_sh) * 2;
+      k_sn_bytes = p.k_sn * 2;
+    }
+    // A 1 KB chunk holds KR consecutive K rows.  The swizzle repeats every 16
+    // rows, so chunk c of wavefront w is placed at rows
+    // 16 (c (4/KGRP) + w / KGRP) + KR (w % KGRP) + lane / KG: every chunk of a
+    // wavefront then has the same lane offset and the chunk only moves the
+    // uniform bases.
+    k_row0 = 16 * (wave / G::KGRP) + G::KR * (wave % G::KGRP) + lane / G::KG;
+    k_gran = (uint32_t)(((lane % G::KG) ^ ((k_row0 / G::KSW) % G::KG)) * 16);
+    k_off = (uint32_t)(k_row0 * k_sn_bytes) + k_gran;
+    // LDS read base: the swizzled offset of k-step s is k_rd ^ (32 s), and the
+    // second 32-row tile sits 32 rows further
+    const int ksw = (l32 / G::KSW) % G::KG;
+    k_rd = (uint32_t)(l32 * G::KROW) + (uint32_t)((ksw & ~1) * 16) + (uint32_t)((hl ^ (ksw & 1)) * 16);
+  }
+
+  // this wavefront's KCW chunks of K tile j into the LDS tile at `slot_lds`
+  __device__ __forceinline__ void issue_k(const AttnArgs& p, int j, uint32_t slot_lds) const {
+    const unsigned char* tb = uniform_ptr(kbase + (long long)j * kBk * k_sn_bytes);
+    const bool ragged = j * kBk + kBk > p.N;
+    const int lim = p.N - 1 - j * kBk;   // last row of tile j inside N (>= 0: j is live)
+    const uint32_t wl = (uint32_t)((16 * (wave / G::KGRP) + G::KR * (wave % G::KGRP)) * G::KROW);
+#pragma unroll
+    for (int c = 0; c < G::KCW; ++c) {
+      const int row_c = 16 * c * (4 / G::KGRP);
+      uint32_t voff = k_off + (uint32_t)(row_c * k_sn_bytes);
+      // rows past N re-read row N-1 (their scores are masked)
+      if (ragged) voff = (uint32_t)(min(row_c + k_row0, lim) * k_sn_bytes) + k_gran;
+      dma16(tb, voff, (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot_lds + row_c * G::KROW + wl)));
+    }
+  }
+
+  // S^T of one tile: two 32-key x 32-row MFMA accumulators (raw dot products)
+  template <typename Acc>
+  __device__ __forceinline__ void read_k(const unsigned char* kt, u32x4 (&kf)[2][G::QS]) const {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < G::QS; ++s)
+        kf[t][s] = *reinterpret_cast<const u32x4*>(kt + t * 32 * G::KROW + (k_rd ^ (32u * s)));
+  }
+};
+
+template <int KIND>
+__device__ __forceinline__ auto mfma_qk(u32x4 a, u32x4 b,
+                                        typename std::conditional<(KIND >= 2), i32x16, f32x16>::type c) {
+  if constexpr (KIND >= 2)
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c,
+                                                 0, 0, 0);
+  else
+    return mfma16<KIND == 1>(a, b, c);
+}
+
+// Scores of one tile as floats with the dead ones at -inf: keys beyond N,
+// causal future, rows beyond N (only diagonal and ragged tiles need it).
+template <bool CAUSAL, typename Acc>
+__device__ __forceinline__ void scores(const AttnArgs& p, const Acc (&acc)[2], float (&sv)[2][16], int j,
+                                       int q0, int qrow, bool qvalid, int hl) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
+  const bool need_mask = (j * kBk + kBk > p.N) || (q0 + kRowsPerWave > p.N) || (CAUSAL && j * kBk + kBk - 1 > q0);
+  if (need_mask) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j * kBk + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool dead = !qvalid || key >= p.N || (CAUSAL && key > qrow);
+        sv[t][r] = dead ? kNegInf : sv[t][r];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: running max, row sums, lambda votes; K only
+// ---------------------------------------------------------------------------
 template <int D, int KIND, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_fwd(AttnArgs p) {
-  constexpr bool I8 = KIND >= 2;
-  constexpr bool PVBF = (KIND == 1 || KIND == 3);
-  constexpr int KROW = I8 ? D : 2 * D;          // bytes per K row
-  constexpr int KG = KROW / 16;                 // 16-byte granules per K row
-  constexpr int KSW = 16 / KG;                  // rows sharing one swizzle step
-  constexpr int K_BYTES = kBk * KROW;
-  constexpr int VROW = kBk * 2;                 // bytes per V^T row (64 keys)
-  constexpr int V_BYTES = D * VROW;
-  constexpr int KCW = K_BYTES / 1024 / kWavesPerBlock;   // 1 KB chunks per wave
-  constexpr int VCW = V_BYTES / 1024 / kWavesPerBlock;
-  constexpr int QS = I8 ? D / 32 : D / 16;      // k-steps of the QK^T MFMA
-  constexpr int OT = D / 32;                    // 32-column tiles of O^T
-  static_assert(KCW >= 1 && VCW >= 1, "tile must span every wave");
-
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2][K_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2][V_BYTES];
+void attn_stats(AttnArgs p) {
+  using G = Geo<D, KIND>;
+  using Acc = typename std::conditional<G::I8, i32x16, f32x16>::type;
+  constexpr int NSLOT = G::NSLOT;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ unsigned long long red[kWavesPerBlock][4];
 
   int b, h, i;
   if (!map_block(p, b, h, i)) return;
-  const int group = p.H / p.Hkv;
-  const int hk = h / group;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int q0 = i * kBq + wave * kRowsPerWave;
-  const int qrow = q0 + l32;
-  const bool qvalid = qrow < p.N;
+  Lane<D, KIND> L;
+  L.init(p, b, h, i);
+  const int tid = L.tid, wave = L.wave, lane = L.lane;
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
   const int n_live = CAUSAL ? min(p.Tn, last_q / kBk + 1) : p.Tn;
-
-  // ---- Q fragment (B operand of S^T = K Q^T), kept in registers ----
-  u32x4 qf[QS];
-  if constexpr (I8) {
-    const int8_t* qb = static_cast<const int8_t*>(p.q) + ((long long)(b * p.H + h) * p.N) * D;
-#pragma unroll
-    for (int s = 0; s < QS; ++s)
-      qf[s] = qvalid ? *reinterpret_cast<const u32x4*>(qb + (long long)qrow * D + 32 * s + 16 * hl)
-                     : u32x4{0, 0, 0, 0};
-  } else {
-    const unsigned short* qb = static_cast<const unsigned short*>(p.q) + b * p.q_sb + h * p.q_sh;
-#pragma unroll
-    for (int s = 0; s < QS; ++s)
-      qf[s] = qvalid ? *reinterpret_cast<const u32x4*>(qb + (long long)qrow * p.q_sn + 16 * s + 8 * hl)
-                     : u32x4{0, 0, 0, 0};
-  }
-  float qscale = 1.0f;
-  if constexpr (I8) qscale = p.q_scale[(long long)(b * p.H + h) * p.Tm + i];
-
-  const unsigned char* kbase;
-  long long k_sn_bytes;
-  if constexpr (I8) {
-    kbase = static_cast<const unsigned char*>(p.k) + ((long long)(b * p.Hkv + hk) * p.N) * D;
-    k_sn_bytes = D;
-  } else {
-    kbase = static_cast<const unsigned char*>(p.k) + (b * p.k_sb + hk * p.k_sh) * 2;
-    k_sn_bytes = p.k_sn * 2;
-  }
-  const unsigned char* vtbase =
-      reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + hk) * D) * p.Np * 2;
-  const float* kscale_row = I8 ? p.k_scale + (long long)(b * p.Hkv + hk) * p.Tn : nullptr;
-
-  const long long row_id = (long long)(b * p.H + h) * p.Tm + i;
+  const long long row_id = L.row_id;
   const int cnt = p.row_cnt[row_id];
-  const uint16_t* list = p.row_idx + row_id * p.Tn;
+  const uint16_t* glist = p.row_idx + row_id * p.Tn;
+  const float* kscale_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
 
-  // ---- global -> LDS tile loads (one 1 KB chunk per wave instruction) ----
-  // A chunk holds R = 1024 / row_bytes consecutive rows.  The swizzle repeats
-  // every 16 rows, so chunk c of wavefront w is placed at rows
-  // 16 (c (4/G) + w / G) + R (w % G) + lane / granules_per_row, G = 16 / R:
-  // every chunk of a wavefront then has the same lane offset (one register),
-  // and the chunk only moves the uniform base.
-  constexpr int KR = 1024 / KROW, KGRP = 16 / KR;
-  constexpr int VR = 1024 / VROW, VGRP = 16 / VR;
-  const int k_row0 = 16 * (wave / KGRP) + KR * (wave % KGRP) + lane / KG;
-  const uint32_t k_off = (uint32_t)(k_row0 * k_sn_bytes) + (uint32_t)(((lane % KG) ^ ((k_row0 / KSW) % KG)) * 16);
-  const int v_row0 = 16 * (wave / VGRP) + VR * (wave % VGRP) + lane / 8;
-  const uint32_t v_off = (uint32_t)(v_row0 * p.Np * 2) + (uint32_t)(((lane % 8) ^ ((v_row0 / 2) % 8)) * 16);
-  auto issue_k = [&](int j, int st) {
-    const bool ragged = j * kBk + kBk > p.N;
-#pragma unroll
-    for (int c = 0; c < KCW; ++c) {
-      const int row_c = 16 * c * (4 / KGRP);                  // rows added by chunk c
-      const unsigned char* src = kbase + ((long long)j * kBk + row_c) * k_sn_bytes + k_off;
-      if (ragged) {
-        // rows past N re-read row N-1 (their scores are masked); the address is
-        // formed from the clamped key in signed 64-bit arithmetic
-        const long long key = (long long)j * kBk + row_c + min(k_row0, p.N - 1 - j * kBk - row_c);
-        src = kbase + key * k_sn_bytes + (k_off - (uint32_t)(k_row0 * k_sn_bytes));
-      }
-      dma16(src, &kbuf[st][(row_c + 16 * (wave / KGRP) + KR * (wave % KGRP)) * KROW]);
-    }
-  };
-  auto issue_v = [&](int j, int st) {
-#pragma unroll
-    for (int c = 0; c < VCW; ++c) {
-      const int row_c = 16 * c * (4 / VGRP);
-      const unsigned char* base = vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2;
-      dma16(base + v_off, &vbuf[st][(row_c + 16 * (wave / VGRP) + VR * (wave % VGRP)) * VROW]);
-    }
-  };
+  unsigned char* ring = smem;
+  uint16_t* lst = reinterpret_cast<uint16_t*>(smem + NSLOT * G::K_BYTES);
+  uint32_t* code = reinterpret_cast<uint32_t*>(smem + NSLOT * G::K_BYTES + ((2 * p.Tn + 15) & ~15));
+  float* ksc = reinterpret_cast<float*>(code + p.Tn);
+  // the list (and the int8 K scales) in LDS; one vote byte per wavefront per entry
+  for (int e = tid; e < cnt; e += kThreads) {
+    const int j = glist[e];
+    lst[e] = (uint16_t)j;
+    code[e] = 0u;
+    if constexpr (G::I8) ksc[e] = kscale_row[j];
+  }
+  __syncthreads();
+  const uint32_t ring_lds = lds_addr(ring);
 
-  // LDS read bases: the swizzled offset of k-step s is base ^ (32 s), and the
-  // second 32-row tile sits a fixed distance further (see the layout above).
-  const int ksw = (l32 / KSW) % KG;
-  uint32_t k_rd = (uint32_t)(l32 * KROW) + (uint32_t)((ksw & ~1) * 16) + (uint32_t)((hl ^ (ksw & 1)) * 16);
-  const int vsw = (l32 / 2) % 8;
-  uint32_t v_rd = (uint32_t)(l32 * VROW) + (uint32_t)((vsw & ~1) * 16) + (uint32_t)((hl ^ (vsw & 1)) * 16);
-
-  // S^T of one tile: two 32-key x 32-row MFMA accumulators (raw dot products)
-  using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
-  auto qk = [&](const unsigned char* kt, Acc (&acc)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      acc[t] = Acc{};
-#pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kt + t * 32 * KROW + (k_rd ^ (32u * s)));
-        if constexpr (I8)
-          acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
-                                                        __builtin_bit_cast(i32x4, qf[s]), acc[t], 0, 0, 0);
-        else
-          acc[t] = mfma16<KIND == 1>(a, qf[s], acc[t]);
-      }
-    }
-  };
-
-  f32x16 oacc[OT];
-#pragma unroll
-  for (int t = 0; t < OT; ++t) oacc[t] = f32x16{};
+  f32x16 zero16 = f32x16{};
   float m_run = kNegInf;      // running max, log2 units
   float l_half = 0.0f;        // this lane half's share of the row sum
-  // per-wavefront tallies (wave-uniform; one workgroup visits at most Tn tiles)
   int n_exec = 0, n_skip = 0, n_void = 0;
-  uint8_t* dbg_row = p.dbg != nullptr ? p.dbg + row_id * p.Tn * kWavesPerBlock + wave : nullptr;
-  const bool write_dbg = dbg_row != nullptr && q0 < p.N;
+  unsigned char* votes = reinterpret_cast<unsigned char*>(code);
 
-  // Software pipeline: while the softmax of listed tile n runs on the VALU,
-  // the QK^T MFMAs of tile n+1 are already in flight.  K_{n+2} and V_{n+1}
-  // stream into the buffers that tiles n and n-1 have released.  The MFMAs of
-  // the next tile and the whole softmax of this one form one branch-free
-  // block, so the scheduler can interleave them; only P~V sits behind the
-  // wavefront's vote.  After the last tile the next-tile MFMAs recompute a
-  // stale buffer and are discarded.
+  // Software pipeline: step n runs the softmax of listed tile n on the VALU
+  // while the QK^T MFMAs of tile n+1 run; K_{n+2} .. K_{n+NSLOT-1} are in
+  // flight and K_{n+NSLOT} is issued into the slot tile n used.  The scores,
+  // MFMAs and exponentials form one branch-free block so the scheduler can
+  // interleave them.  After the last tile the next-tile MFMAs read a stale
+  // slot and are discarded.
+  int jd_v = 0;   // list entry of the next refill (read one step early)
+  int jn_v = 0;   // list entry of the next step
   auto step = [&](int n, Acc (&cur)[2], Acc (&nxt)[2]) {
-    const int j = list[n];
-    wait_vmem();                          // K_{n+1} and V_n have landed (this wave's part)
-    __syncthreads();                      // everyone's have; everyone is done with tile n-1
-    asm volatile("" : "+v"(k_rd), "+v"(v_rd));
-    if (n + 2 < cnt) issue_k(list[n + 2], n & 1);
-    if (n + 1 < cnt) issue_v(list[n + 1], (n + 1) & 1);
-    const unsigned char* vt = vbuf[n & 1];
-    const unsigned char* kn = kbuf[(n + 1) & 1];
-
+    const int pend = min(cnt - 1, n + NSLOT - 1) - (n + 1);   // tiles issued after K_{n+1}
+    wait_pending<G::KCW, NSLOT - 2>(pend);
+    if (n + NSLOT < cnt)
+      L.issue_k(p, __builtin_amdgcn_readfirstlane(jd_v), ring_lds + (uint32_t)((n & (NSLOT - 1)) * G::K_BYTES));
+    const int j = __builtin_amdgcn_readfirstlane(jn_v);
+    jd_v = lst[min(n + 1 + NSLOT, p.Tn - 1)];
+    jn_v = lst[min(n + 1, p.Tn - 1)];
     float c_scale = p.scale_log2;
-    if constexpr (I8) c_scale = qscale * kscale_row[j] * p.scale_log2;
-    float sv[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sv[t][r] = (float)cur[t][r];
-    // masking: keys beyond N, causal future, rows beyond N (diagonal and ragged tiles only)
-    const bool need_mask = (j * kBk + kBk > p.N) || (q0 + kRowsPerWave > p.N) ||
-                           (CAUSAL && j * kBk + kBk - 1 > q0);
-    if (need_mask) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * kBk + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool dead = !qvalid || key >= p.N || (CAUSAL && key > qrow);
-          sv[t][r] = dead ? kNegInf : sv[t][r];
-        }
-    }
+    if constexpr (G::I8) c_scale = L.qscale * ksc[n] * p.scale_log2;
 
-    // ---- next tile's S^T on the matrix cores ----
-    qk(kn, nxt);
+    u32x4 kf[2][G::QS];
+    L.template read_k<Acc>(ring + ((n + 1) & (NSLOT - 1)) * G::K_BYTES, kf);
+
+    float sv[2][16];
+    scores<CAUSAL>(p, cur, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
 
     // ---- online softmax (eq. 1) in log2 units; the scale is folded into an FMA ----
     float mx = kNegInf;
@@ -315,52 +424,59 @@ void attn_fwd(AttnArgs p) {
     const bool exec = __any(wants_pv);
     const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
     const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
-    // P~ (eq. 1); it always feeds l (Algorithm 1 computes it before the M_pv
-    // test) and is packed in the P~V input type as the B operand of 4 k-steps
-    float psum = 0.0f;
-    u32x4 pb[4];
+
+    // next tile's S^T on the matrix cores, interleaved with this tile's exponentials
+    float ps[2 * G::QS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int tt = s >> 1, r0 = 8 * (s & 1);
+    for (int t = 0; t < 2; ++t) nxt[t] = Acc{};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = fast_exp2(fmaf(sv[tt][r0 + 2 * e], c_scale, neg_m));
-        const float x1 = fast_exp2(fmaf(sv[tt][r0 + 2 * e + 1], c_scale, neg_m));
-        psum += x0 + x1;
-        pb[s][e] = pack2<PVBF>(x0, x1);
+    for (int s = 0; s < G::QS; ++s) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        nxt[t] = mfma_qk<KIND>(kf[t][s], L.qf[s], nxt[t]);
+        const int u = 2 * s + t;
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < G::EPM; ++e) {
+          const int idx = u * G::EPM + e;
+          acc += fast_exp2(fmaf(sv[idx >> 4][idx & 15], c_scale, neg_m));
+        }
+        ps[u] = acc;
       }
     }
+    float psum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2 * G::QS; ++u) psum += ps[u];
+    // P~ always feeds l (Algorithm 1 computes it before the M_pv test)
     l_half = alpha * l_half + psum;
     m_run = m_new;
-    const unsigned char code = exec ? 1 : (any_finite ? 2 : 3);
+    // keep this tile's exponentials inside this step (next to the MFMAs they
+    // overlap) instead of letting them sink into the next one
+    asm volatile("" : "+v"(l_half));
+    const unsigned char c = exec ? 1 : (any_finite ? 2 : 3);
     n_exec += exec ? 1 : 0;
     n_skip += (!exec && any_finite) ? 1 : 0;
     n_void += any_finite ? 0 : 1;
-    if (exec) {
-#pragma unroll
-      for (int t = 0; t < OT; ++t) oacc[t] *= alpha;
-      // ---- O^T += V_j^T P~^T ----
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t off = v_rd ^ (32u * s);
-#pragma unroll
-        for (int t = 0; t < OT; ++t) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vt + t * 32 * VROW + off);
-          oacc[t] = mfma16<PVBF>(a, pb[s], oacc[t]);
-        }
-      }
-    }
-    if (write_dbg && lane == 0) dbg_row[j * kWavesPerBlock] = code;
+    votes[n * kWavesPerBlock + wave] = c;
   };
+  (void)zero16;
 
   Acc s_a[2], s_b[2];
   if (cnt > 0) {
-    issue_k(list[0], 0);
-    issue_v(list[0], 0);
-    if (cnt > 1) issue_k(list[1], 1);
-    wait_vmem();
-    __syncthreads();
-    qk(kbuf[0], s_a);
+    const int pre = min(cnt, NSLOT);
+    for (int t = 0; t < pre; ++t)
+      L.issue_k(p, __builtin_amdgcn_readfirstlane((int)lst[t]), ring_lds + (uint32_t)(t * G::K_BYTES));
+    wait_pending<G::KCW, NSLOT - 1>(pre - 1);   // K_0 has landed everywhere
+    u32x4 kf[2][G::QS];
+    L.template read_k<Acc>(ring, kf);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s_a[t] = Acc{};
+#pragma unroll
+      for (int s = 0; s < G::QS; ++s) s_a[t] = mfma_qk<KIND>(kf[t][s], L.qf[s], s_a[t]);
+    }
+    jn_v = lst[0];
+    jd_v = lst[min(NSLOT, p.Tn - 1)];
   }
   int n = 0;
   for (; n + 1 < cnt; n += 2) {           // unrolled by two so the score buffers swap roles
@@ -368,43 +484,43 @@ void attn_fwd(AttnArgs p) {
     step(n + 1, s_b, s_a);
   }
   if (n < cnt) step(n, s_a, s_b);
-  const int n_qk = cnt;
+  wait_barrier<0>();                       // every vote byte is written
 
-  // ---- epilogue: O / l ----
+  // ---- the executed-tile list: listed tiles with at least one voting wavefront ----
+  if (wave == 0) {
+    uint32_t* ul = p.ulist + row_id * p.Tn;
+    int U = 0;
+    for (int base = 0; base < cnt; base += 64) {
+      const int e = base + lane;
+      uint32_t m = 0;
+      if (e < cnt) {
+        const uint32_t cw = code[e];
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) m |= (((cw >> (8 * w)) & 0xffu) == 1u ? 1u : 0u) << w;
+      }
+      const unsigned long long bal = __ballot(m != 0);
+      const int pos = U + (int)__popcll(bal & ((1ull << lane) - 1ull));
+      if (m != 0) ul[pos] = (uint32_t)lst[e] | (m << 16);
+      U += (int)__popcll(bal);
+    }
+    if (lane == 0) p.ucnt[row_id] = U;
+  }
   const float l_tot = sum_halves(l_half);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qvalid && p.out_f32) {
-    float* ob = static_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)qrow * p.o_sn;
-#pragma unroll
-    for (int t = 0; t < OT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x4 w = {__float_as_uint(oacc[t][4 * g + 0] * inv), __float_as_uint(oacc[t][4 * g + 1] * inv),
-                   __float_as_uint(oacc[t][4 * g + 2] * inv), __float_as_uint(oacc[t][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x4*>(ob + 32 * t + 8 * g + 4 * hl) = w;
-      }
-  } else if (qvalid) {
-    // each float32 quotient is materialised (the empty asm keeps the compiler
-    // from fusing multiply and narrowing into one differently rounded op), so
-    // this output is exactly the float32 output rounded to the 16-bit type
-    unsigned short* ob = static_cast<unsigned short*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)qrow * p.o_sn;
-#pragma unroll
-    for (int t = 0; t < OT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[e] = oacc[t][4 * g + e] * inv;
-          asm volatile("" : "+v"(y[e]));
-        }
-        u32x2 w = {pack2<PVBF>(y[0], y[1]), pack2<PVBF>(y[2], y[3])};
-        *reinterpret_cast<u32x2*>(ob + 32 * t + 8 * g + 4 * hl) = w;
-      }
+  if (L.qvalid && L.hl == 0) {
+    const long long r = (long long)(b * p.H + h) * p.N + L.qrow;
+    p.row_m[r] = m_run;
+    p.row_l[r] = l_tot;
+  }
+  if (p.dbg != nullptr) {
+    uint8_t* drow = p.dbg + row_id * p.Tn * kWavesPerBlock;
+    for (int e = tid; e < cnt * kWavesPerBlock; e += kThreads) {
+      const int w = e & (kWavesPerBlock - 1);
+      if (i * kBq + w * kRowsPerWave < p.N) drow[(int)lst[e / kWavesPerBlock] * kWavesPerBlock + w] = votes[e];
+    }
   }
 
   // ---- counters ----
-  const bool empty = qvalid && hl == 0 && !(l_tot > 0.0f);
+  const bool empty = L.qvalid && L.hl == 0 && !(l_tot > 0.0f);
   const unsigned long long n_empty = __popcll(__ballot(empty));
   if (lane == 0) {
     red[wave][0] = (unsigned long long)n_exec;
@@ -424,13 +540,158 @@ void attn_fwd(AttnArgs p) {
       em += red[w][3];
     }
     atomicAdd(p.counts + SPARGE_CNT_LIVE, (unsigned long long)n_live);
-    atomicAdd(p.counts + SPARGE_CNT_QK_EXEC, (unsigned long long)n_qk);
-    atomicAdd(p.counts + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - n_qk));
+    atomicAdd(p.counts + SPARGE_CNT_QK_EXEC, (unsigned long long)cnt);
+    atomicAdd(p.counts + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - cnt));
     atomicAdd(p.counts + SPARGE_CNT_PV_EXEC, e);
     atomicAdd(p.counts + SPARGE_CNT_PV_SKIP, s);
     atomicAdd(p.counts + SPARGE_CNT_PV_VOID, v);
     atomicAdd(p.counts + SPARGE_CNT_EMPTY_ROWS, em);
     atomicAdd(p.counts + SPARGE_CNT_ROWS, (unsigned long long)(last_q - i * kBq + 1));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: P~V on the executed tiles, then O / l
+// ---------------------------------------------------------------------------
+template <int D, int KIND, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_pv(AttnArgs p) {
+  using G = Geo<D, KIND>;
+  using Acc = typename std::conditional<G::I8, i32x16, f32x16>::type;
+  constexpr int NS = G::NS2;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  int b, h, i;
+  if (!map_block(p, b, h, i)) return;
+  Lane<D, KIND> L;
+  L.init(p, b, h, i);
+  const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
+  const long long row_id = L.row_id;
+  const int U = p.ucnt[row_id];
+  const uint32_t* gul = p.ulist + row_id * p.Tn;
+  const float* kscale_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
+  uint32_t* ent = reinterpret_cast<uint32_t*>(smem + NS * G::E_BYTES);
+  float* ksc = reinterpret_cast<float*>(ent + p.Tn);
+  for (int e = tid; e < U; e += kThreads) {
+    const uint32_t en = gul[e];
+    ent[e] = en;
+    if constexpr (G::I8) ksc[e] = kscale_row[en & 0xffffu];
+  }
+  const long long srow = (long long)(b * p.H + h) * p.N + L.qrow;
+  const float m_row = L.qvalid ? p.row_m[srow] : kNegInf;
+  const float l_row = L.qvalid ? p.row_l[srow] : 0.0f;
+  __syncthreads();
+
+  const unsigned char* vtbase =
+      reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + L.hk) * D) * p.Np * 2;
+  const int v_row0 = 16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP) + lane / 8;
+  const uint32_t v_off = (uint32_t)(v_row0 * p.Np * 2) + (uint32_t)(((lane % 8) ^ ((v_row0 / 2) % 8)) * 16);
+  const uint32_t v_wl = (uint32_t)((16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP)) * G::VROW);
+  const int vsw = (l32 / 2) % 8;
+  const uint32_t v_rd = (uint32_t)(l32 * G::VROW) + (uint32_t)((vsw & ~1) * 16) + (uint32_t)((hl ^ (vsw & 1)) * 16);
+  const uint32_t ring_lds = lds_addr(smem);
+
+  // entry e -> slot: its K tile, then its V^T tile (KCW + VCW loads per wavefront)
+  auto issue = [&](int e, int slot) {
+    const int j = __builtin_amdgcn_readfirstlane((int)(ent[e] & 0xffffu));
+    const uint32_t sl = ring_lds + (uint32_t)(slot * G::E_BYTES);
+    L.issue_k(p, j, sl);
+#pragma unroll
+    for (int c = 0; c < G::VCW; ++c) {
+      const int row_c = 16 * c * (4 / G::VGRP);
+      const unsigned char* base = uniform_ptr(vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2);
+      dma16(base, v_off,
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + row_c * G::VROW + v_wl)));
+    }
+  };
+
+  f32x16 oacc[G::OT];
+#pragma unroll
+  for (int t = 0; t < G::OT; ++t) oacc[t] = f32x16{};
+  const float neg_m = (m_row == kNegInf) ? 0.0f : -m_row;
+
+  // Entry e is used in step e; entries e+1 .. e+NS-2 are in flight when step
+  // e starts, and step e refills the slot entry e-1 used with entry e+NS-1.
+  const int pre = min(U, NS - 1);
+  for (int t = 0; t < pre; ++t) issue(t, t);
+  for (int e = 0; e < U; ++e) {
+    const int pend = min(U - 1, e + NS - 2) - e;    // entries issued after entry e
+    wait_pending<G::KCW + G::VCW, NS - 2>(pend);
+    if (e + NS - 1 < U) issue(e + NS - 1, (e + NS - 1) % NS);
+    const uint32_t en = (uint32_t)__builtin_amdgcn_readfirstlane((int)ent[e]);
+    const int j = (int)(en & 0xffffu);
+    if ((en >> (16 + wave)) & 1u) {       // this wavefront's group ran P~V on tile j
+      const unsigned char* kt = smem + (e % NS) * G::E_BYTES;
+      const unsigned char* vt = kt + G::K_BYTES;
+      u32x4 kf[2][G::QS];
+      L.template read_k<Acc>(kt, kf);
+      Acc acc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        acc[t] = Acc{};
+#pragma unroll
+        for (int s = 0; s < G::QS; ++s) acc[t] = mfma_qk<KIND>(kf[t][s], L.qf[s], acc[t]);
+      }
+      float c_scale = p.scale_log2;
+      if constexpr (G::I8) c_scale = L.qscale * ksc[e] * p.scale_log2;
+      float sv[2][16];
+      scores<CAUSAL>(p, acc, sv, j, L.q0, L.qrow, L.qvalid, hl);
+      // P = exp(S - m_final), packed in the P~V input type as the B operand of 4 k-steps
+      u32x4 pb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int tt = s >> 1, r0 = 8 * (s & 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = fast_exp2(fmaf(sv[tt][r0 + 2 * q], c_scale, neg_m));
+          const float x1 = fast_exp2(fmaf(sv[tt][r0 + 2 * q + 1], c_scale, neg_m));
+          pb[s][q] = pack2<G::PVBF>(x0, x1);
+        }
+      }
+      // ---- O^T += V_j^T P^T ----
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t off = v_rd ^ (32u * s);
+#pragma unroll
+        for (int t = 0; t < G::OT; ++t) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(vt + t * 32 * G::VROW + off);
+          oacc[t] = mfma16<G::PVBF>(a, pb[s], oacc[t]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O / l ----
+  const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+  if (L.qvalid && p.out_f32) {
+    float* ob = static_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)L.qrow * p.o_sn;
+#pragma unroll
+    for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x4 w = {__float_as_uint(oacc[t][4 * g + 0] * inv), __float_as_uint(oacc[t][4 * g + 1] * inv),
+                   __float_as_uint(oacc[t][4 * g + 2] * inv), __float_as_uint(oacc[t][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x4*>(ob + 32 * t + 8 * g + 4 * hl) = w;
+      }
+  } else if (L.qvalid) {
+    // each float32 quotient is materialised (the empty asm keeps the compiler
+    // from fusing multiply and narrowing into one differently rounded op), so
+    // this output is exactly the float32 output rounded to the 16-bit type
+    unsigned short* ob =
+        static_cast<unsigned short*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)L.qrow * p.o_sn;
+#pragma unroll
+    for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          y[q] = oacc[t][4 * g + q] * inv;
+          asm volatile("" : "+v"(y[q]));
+        }
+        u32x2 w = {pack2<G::PVBF>(y[0], y[1]), pack2<G::PVBF>(y[2], y[3])};
+        *reinterpret_cast<u32x2*>(ob + 32 * t + 8 * g + 4 * hl) = w;
+      }
   }
 }
 
@@ -472,14 +733,27 @@ __global__ void zero_u64(unsigned long long* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
 }
 
+template <int D, int KIND, bool CAUSAL>
+hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
+  const long long blocks = (long long)a.B * a.H * a.Tm;
+  const size_t lds1 = stats_lds_bytes<D, KIND>(a.Tn);
+  const size_t lds2 = pv_lds_bytes<D, KIND>(a.Tn);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pv<D, KIND, CAUSAL>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds1, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_pv<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds2, st, a);
+  return hipGetLastError();
+}
+
 template <int D, int KIND>
 hipError_t launch_d_kind(const AttnArgs& a, hipStream_t st) {
-  const long long blocks = (long long)a.B * a.H * a.Tm;
-  if (a.causal)
-    hipLaunchKernelGGL((attn_fwd<D, KIND, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_fwd<D, KIND, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  return a.causal ? launch_passes<D, KIND, true>(a, st) : launch_passes<D, KIND, false>(a, st);
 }
 
 template <int D>

@@ -175,7 +175,9 @@ int sparge_predict_mask(const void* q, const sparge_tensor* qs, const void* k,
  *   sparge_predict_mask) are optional: if both are NULL the row lists are
  *   built from mg in the workspace.  Only live tiles are visited.
  * workspace (sparge_workspace_size bytes) is required: it holds a
- *   transposed copy of V (and the row lists built from mg).
+ *   transposed copy of V, the per-row softmax statistics and executed-tile
+ *   lists passed from the first to the second attention kernel, and the row
+ *   lists built from mg.
  * lambda < 0 (-inf disables the rule).
  * counts: int64[SPARGE_NUM_COUNTERS], overwritten (see SPARGE_CNT_*).
  * pv_dbg: optional uint8 [B,H,Tm,Tn,SPARGE_BQ/sparge_rows_per_wave()] with
