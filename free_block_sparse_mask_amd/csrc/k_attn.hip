@@ -56,6 +56,8 @@ namespace sparge {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+// attention pass 1: query blocks per workgroup (4 wavefronts each)
+constexpr int kStatsUnits = 2;
 
 // v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
 // in the other, so combining the two gives every lane the pair (l, l ^ 32).
@@ -142,15 +144,16 @@ __device__ __forceinline__ void wait_pending(int pending) {
   }
 }
 
-// Workgroup id -> (b, h, i).  Workgroups are dispatched to the 8 XCDs round
-// robin (id % 8).  When the query heads of 8 / G kv heads fill one row of 8
-// slots (G = H / H_kv), the grid runs in phases of 8 / G kv heads: slot s of
-// every row is XCD s, which always serves query head s % G of kv head
-// s / G of the phase, heaviest block rows first.  Each XCD's L2 then sees one
-// kv head, and only 8 / G kv heads (a few tens of MB to a few hundred MB of
-// K and V) are live in the Infinity Cache at a time.  Other shapes fall back
-// to block rows outermost, heaviest first.
-__device__ __forceinline__ bool map_block(const AttnArgs& p, int& b, int& h, int& i) {
+// Workgroup id -> (b, h, r) for T row groups per head (r = T - 1 for the
+// heaviest).  Workgroups are dispatched to the 8 XCDs round robin (id % 8).
+// When the query heads of 8 / G kv heads fill one row of 8 slots
+// (G = H / H_kv), the grid runs in phases of 8 / G kv heads: slot s of every
+// row is XCD s, which always serves query head s % G of kv head s / G of the
+// phase, heaviest rows first.  Each XCD's L2 then sees one kv head, and only
+// 8 / G kv heads (a few tens of MB to a few hundred MB of K and V) are live
+// in the Infinity Cache at a time.  Other shapes fall back to rows
+// outermost, heaviest first.
+__device__ __forceinline__ bool map_block(const AttnArgs& p, int T, int& b, int& h, int& r) {
   const int group = p.H / p.Hkv;
   const int pairs = p.B * p.Hkv;
   const long long id = blockIdx.x;
@@ -158,21 +161,21 @@ __device__ __forceinline__ bool map_block(const AttnArgs& p, int& b, int& h, int
     const int per_phase = 8 / group;
     const int slot = (int)(id & 7);
     const long long k = id >> 3;
-    const int phase = (int)(k / p.Tm);
-    const int irank = (int)(k % p.Tm);
+    const int phase = (int)(k / T);
+    const int rank = (int)(k % T);
     const int pair = phase * per_phase + slot / group;
     b = pair / p.Hkv;
     h = (pair % p.Hkv) * group + slot % group;
-    i = p.Tm - 1 - irank;
+    r = T - 1 - rank;
   } else {
     const long long bh = (long long)p.B * p.H;
-    const int irank = (int)(id / bh);
+    const int rank = (int)(id / bh);
     const int rem = (int)(id % bh);
     b = rem / p.H;
     h = rem % p.H;
-    i = p.Tm - 1 - irank;
+    r = T - 1 - rank;
   }
-  return i >= 0 && b < p.B;
+  return r >= 0 && b < p.B;
 }
 
 // ---------------------------------------------------------------------------
@@ -186,9 +189,8 @@ struct Geo {
   static constexpr int KG = KROW / 16;                 // 16-byte granules per K row
   static constexpr int KSW = 16 / KG;                  // rows sharing one swizzle step
   static constexpr int K_BYTES = kBk * KROW;
-  static constexpr int KCW = K_BYTES / 1024 / kWavesPerBlock;   // 1 KB chunks per wave
+  static constexpr int KCH = K_BYTES / 1024;           // 1 KB chunks per K tile
   static constexpr int KR = 1024 / KROW;               // K rows per 1 KB chunk
-  static constexpr int KGRP = 16 / KR;
   static constexpr int VROW = kBk * 2;                 // bytes per V^T row (64 keys)
   static constexpr int V_BYTES = D * VROW;
   static constexpr int VCW = V_BYTES / 1024 / kWavesPerBlock;
@@ -197,20 +199,23 @@ struct Geo {
   static constexpr int QS = I8 ? D / 32 : D / 16;      // k-steps of the QK^T MFMA
   static constexpr int OT = D / 32;                    // 32-column tiles of O^T
   static constexpr int EPM = 32 / (2 * QS);            // scores per lane per QK^T MFMA
-  // pass 1: K ring slots (64 KB or less, so two workgroups fit a CU with the lists)
-  static constexpr int NSLOT = I8 ? 4 : (K_BYTES >= 16384 ? 4 : 8);
+  // pass 1: K ring slots
+  static constexpr int NSLOT = 4;
+  // pass 1: query blocks (of 4 wavefronts) per workgroup sharing one K ring
+  static constexpr int UNITS = kStatsUnits;
   // pass 2: (K, V^T) slots
   static constexpr int E_BYTES = K_BYTES + V_BYTES;
   static constexpr int NS2 = (65536 / E_BYTES) >= 4 ? 4 : 2;
-  static_assert(KCW >= 1 && VCW >= 1, "tile must span every wave");
+  static_assert(VCW >= 1, "tile must span every wave");
   static_assert(EPM * 2 * QS == 32, "scores must split evenly over the MFMAs");
 };
 
 template <int D, int KIND>
 size_t stats_lds_bytes(int Tn) {
   using G = Geo<D, KIND>;
-  return (size_t)G::NSLOT * G::K_BYTES + (((size_t)2 * Tn + 15) & ~(size_t)15) + (size_t)4 * Tn +
-         (G::I8 ? (size_t)4 * Tn : 0);
+  const size_t nw = (size_t)kWavesPerBlock * G::UNITS;
+  return (size_t)G::NSLOT * G::K_BYTES + (size_t)4 * ((Tn + 3) / 4) + (size_t)2 * ((Tn + 1) & ~1) +
+         (size_t)4 * nw * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
 }
 template <int D, int KIND>
 size_t pv_lds_bytes(int Tn) {
@@ -219,21 +224,32 @@ size_t pv_lds_bytes(int Tn) {
 }
 
 // Per-lane pieces common to both passes: Q fragment, K DMA offsets, read bases.
-template <int D, int KIND>
+// NW wavefronts share the loads of a K tile: its 1 KB chunk q (rows
+// KR q .. KR q + KR - 1) is loaded by wavefront q % NW, so chunk c of
+// wavefront w holds rows KR (c NW + w) + lane / KG.  The XOR swizzle of a row
+// repeats every 16 rows and KR NW is a multiple of 16, so all chunks of a
+// wavefront share one lane offset.
+template <int D, int KIND, int NW>
 struct Lane {
   using G = Geo<D, KIND>;
+  static constexpr int KCW = G::KCH >= NW ? G::KCH / NW : 1;   // chunks per loading wavefront
+  static_assert((G::KR * NW) % 16 == 0, "chunk rows must keep the swizzle phase");
   int b, h, i, hk, tid, wave, lane, l32, hl, q0, qrow;
-  bool qvalid;
+  bool qvalid, loads_k;
   long long row_id;
   u32x4 qf[G::QS];
   float qscale;
   const unsigned char* kbase;
   long long k_sn_bytes;
   int k_row0;
-  uint32_t k_gran, k_off;
+  uint32_t k_gran;
+  uint32_t k_voff[KCW];      // lane offset of chunk c inside a full tile
+  uint32_t k_wl;             // this wavefront's LDS offset inside a tile (uniform)
   uint32_t k_rd;
 
-  __device__ __forceinline__ void init(const AttnArgs& p, int b_, int h_, int i_) {
+  // wq: wavefront index inside its query block (0..3); has_rows: false for
+  // a workgroup slot past the last query block
+  __device__ __forceinline__ void init(const AttnArgs& p, int b_, int h_, int i_, int wq, bool has_rows) {
     b = b_;
     h = h_;
     i = i_;
@@ -243,9 +259,9 @@ struct Lane {
     lane = tid & 63;
     l32 = lane & 31;
     hl = lane >> 5;
-    q0 = i * kBq + wave * kRowsPerWave;
+    q0 = i * kBq + wq * kRowsPerWave;
     qrow = q0 + l32;
-    qvalid = qrow < p.N;
+    qvalid = has_rows && qrow < p.N;
     row_id = (long long)(b * p.H + h) * p.Tm + i;
     if constexpr (G::I8) {
       const int8_t* qb = static_cast<const int8_t*>(p.q) + ((long long)(b * p.H + h) * p.N) * D;
@@ -253,7 +269,7 @@ struct Lane {
       for (int s = 0; s < G::QS; ++s)
         qf[s] = qvalid ? *reinterpret_cast<const u32x4*>(qb + (long long)qrow * D + 32 * s + 16 * hl)
                        : u32x4{0, 0, 0, 0};
-      qscale = p.q_scale[row_id];
+      qscale = has_rows ? p.q_scale[row_id] : 1.0f;
       kbase = static_cast<const unsigned char*>(p.k) + ((long long)(b * p.Hkv + hk) * p.N) * D;
       k_sn_bytes = D;
     } else {
@@ -266,38 +282,39 @@ struct Lane {
       kbase = static_cast<const unsigned char*>(p.k) + (b * p.k_sb + hk * p.k_sh) * 2;
       k_sn_bytes = p.k_sn * 2;
     }
-    // A 1 KB chunk holds KR consecutive K rows.  The swizzle repeats every 16
-    // rows, so chunk c of wavefront w is placed at rows
-    // 16 (c (4/KGRP) + w / KGRP) + KR (w % KGRP) + lane / KG: every chunk of a
-    // wavefront then has the same lane offset and the chunk only moves the
-    // uniform bases.
-    k_row0 = 16 * (wave / G::KGRP) + G::KR * (wave % G::KGRP) + lane / G::KG;
+    loads_k = wave < G::KCH;
+    k_row0 = G::KR * wave + lane / G::KG;
     k_gran = (uint32_t)(((lane % G::KG) ^ ((k_row0 / G::KSW) % G::KG)) * 16);
-    k_off = (uint32_t)(k_row0 * k_sn_bytes) + k_gran;
+#pragma unroll
+    for (int c = 0; c < KCW; ++c)
+      k_voff[c] = (uint32_t)((k_row0 + c * G::KR * NW) * k_sn_bytes) + k_gran;
+    k_wl = (uint32_t)__builtin_amdgcn_readfirstlane((int)(G::KR * wave * G::KROW));
     // LDS read base: the swizzled offset of k-step s is k_rd ^ (32 s), and the
     // second 32-row tile sits 32 rows further
     const int ksw = (l32 / G::KSW) % G::KG;
     k_rd = (uint32_t)(l32 * G::KROW) + (uint32_t)((ksw & ~1) * 16) + (uint32_t)((hl ^ (ksw & 1)) * 16);
   }
 
-  // this wavefront's KCW chunks of K tile j into the LDS tile at `slot_lds`
+  // this wavefront's chunks of K tile j into the LDS tile at `slot_lds`
+  // (j and slot_lds wavefront-uniform); KCW loads, or none
   __device__ __forceinline__ void issue_k(const AttnArgs& p, int j, uint32_t slot_lds) const {
+    if (!loads_k) return;
     const unsigned char* tb = uniform_ptr(kbase + (long long)j * kBk * k_sn_bytes);
-    const bool ragged = j * kBk + kBk > p.N;
-    const int lim = p.N - 1 - j * kBk;   // last row of tile j inside N (>= 0: j is live)
-    const uint32_t wl = (uint32_t)((16 * (wave / G::KGRP) + G::KR * (wave % G::KGRP)) * G::KROW);
+    if (j * kBk + kBk <= p.N) {
 #pragma unroll
-    for (int c = 0; c < G::KCW; ++c) {
-      const int row_c = 16 * c * (4 / G::KGRP);
-      uint32_t voff = k_off + (uint32_t)(row_c * k_sn_bytes);
-      // rows past N re-read row N-1 (their scores are masked)
-      if (ragged) voff = (uint32_t)(min(row_c + k_row0, lim) * k_sn_bytes) + k_gran;
-      dma16(tb, voff, (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot_lds + row_c * G::KROW + wl)));
+      for (int c = 0; c < KCW; ++c)
+        dma16(tb, k_voff[c], slot_lds + (uint32_t)(c * NW * 1024) + k_wl);
+    } else {
+      // ragged last tile: rows past N re-read row N-1 (their scores are masked)
+      const int lim = p.N - 1 - j * kBk;   // >= 0: tile j is live
+#pragma unroll
+      for (int c = 0; c < KCW; ++c)
+        dma16(tb, (uint32_t)(min(k_row0 + c * G::KR * NW, lim) * k_sn_bytes) + k_gran,
+              slot_lds + (uint32_t)(c * NW * 1024) + k_wl);
     }
   }
 
-  // S^T of one tile: two 32-key x 32-row MFMA accumulators (raw dot products)
-  template <typename Acc>
+  // the A operands of S^T = K Q^T for one tile: 2 x QS 16-byte LDS reads
   __device__ __forceinline__ void read_k(const unsigned char* kt, u32x4 (&kf)[2][G::QS]) const {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -317,24 +334,23 @@ __device__ __forceinline__ auto mfma_qk(u32x4 a, u32x4 b,
     return mfma16<KIND == 1>(a, b, c);
 }
 
-// Scores of one tile as floats with the dead ones at -inf: keys beyond N,
-// causal future, rows beyond N (only diagonal and ragged tiles need it).
-template <bool CAUSAL, typename Acc>
-__device__ __forceinline__ void scores(const AttnArgs& p, const Acc (&acc)[2], float (&sv)[2][16], int j,
-                                       int q0, int qrow, bool qvalid, int hl) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
+// Dead scores of one tile set to -inf in place: keys beyond N, causal future,
+// rows beyond N (only diagonal and ragged tiles need it).
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_scores(const AttnArgs& p, f32x16 (&sv)[2], int j, int q0, int qrow, bool qvalid,
+                                            int hl) {
   const bool need_mask = (j * kBk + kBk > p.N) || (q0 + kRowsPerWave > p.N) || (CAUSAL && j * kBk + kBk - 1 > q0);
   if (need_mask) {
+    // key = j*64 + 4*hl + off(t, r) is dead iff key > last, the last visible
+    // key of this row (-1 for a row beyond N): off > last - j*64 - 4*hl
+    const int last = !qvalid ? -1 : (CAUSAL ? min(qrow, p.N - 1) : p.N - 1);
+    const int thr = last - j * kBk - 4 * hl;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j * kBk + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool dead = !qvalid || key >= p.N || (CAUSAL && key > qrow);
-        sv[t][r] = dead ? kNegInf : sv[t][r];
+        const int off = 32 * t + 8 * (r >> 2) + (r & 3);
+        sv[t][r] = off > thr ? kNegInf : sv[t][r];
       }
   }
 }
@@ -342,168 +358,224 @@ __device__ __forceinline__ void scores(const AttnArgs& p, const Acc (&acc)[2], f
 // ---------------------------------------------------------------------------
 // Pass 1: running max, row sums, lambda votes; K only
 // ---------------------------------------------------------------------------
+// One workgroup holds UNITS query blocks of one head (consecutive block rows,
+// 4 wavefronts each).  Their key lists are merged into one ascending union
+// list: each union entry's K tile is loaded once into the ring and used by
+// the wavefronts of every block that lists it.  Visiting a block's own tiles
+// in ascending order inside the union order keeps eq. (1) and the vote
+// exactly as for a lone block.  A wavefront keeps only the scores of the
+// current tile, so four wavefronts fit a SIMD and hide each other's MFMA,
+// exponential and LDS latencies.
 template <int D, int KIND, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads * kStatsUnits) __attribute__((amdgpu_waves_per_eu(4)))
 void attn_stats(AttnArgs p) {
   using G = Geo<D, KIND>;
   using Acc = typename std::conditional<G::I8, i32x16, f32x16>::type;
+  constexpr int U = G::UNITS;
+  constexpr int NW = kWavesPerBlock * U;
   constexpr int NSLOT = G::NSLOT;
+  using LN = Lane<D, KIND, NW>;
+  constexpr int KCW = LN::KCW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ unsigned long long red[kWavesPerBlock][4];
+  __shared__ unsigned long long red[NW][4];
+  __shared__ int s_ucnt;
 
-  int b, h, i;
-  if (!map_block(p, b, h, i)) return;
-  Lane<D, KIND> L;
-  L.init(p, b, h, i);
-  const int tid = L.tid, wave = L.wave, lane = L.lane;
-  const int last_q = min(p.N, (i + 1) * kBq) - 1;
-  const int n_live = CAUSAL ? min(p.Tn, last_q / kBk + 1) : p.Tn;
+  const int Tg = (p.Tm + U - 1) / U;
+  int b, h, g;
+  if (!map_block(p, Tg, b, h, g)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int unit = wave / kWavesPerBlock, wq = wave % kWavesPerBlock;
+  const int i = g * U + unit;                 // this wavefront's query block
+  const bool has_rows = i < p.Tm;
+  LN L;
+  L.init(p, b, h, i, wq, has_rows);
   const long long row_id = L.row_id;
-  const int cnt = p.row_cnt[row_id];
-  const uint16_t* glist = p.row_idx + row_id * p.Tn;
+  const int last_q = has_rows ? min(p.N, (i + 1) * kBq) - 1 : 0;
+  const int n_live = !has_rows ? 0 : (CAUSAL ? min(p.Tn, last_q / kBk + 1) : p.Tn);
+  const int cnt = has_rows ? p.row_cnt[row_id] : 0;
   const float* kscale_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
 
+  // LDS: K ring | tile flags (one byte per tile: blocks listing it) | union
+  // list (j | block mask << 12) | votes (2 bits per wavefront and entry) |
+  // int8 K scales of the union entries
+  const int nwords = (p.Tn + 15) / 16;
   unsigned char* ring = smem;
-  uint16_t* lst = reinterpret_cast<uint16_t*>(smem + NSLOT * G::K_BYTES);
-  uint32_t* code = reinterpret_cast<uint32_t*>(smem + NSLOT * G::K_BYTES + ((2 * p.Tn + 15) & ~15));
-  float* ksc = reinterpret_cast<float*>(code + p.Tn);
-  // the list (and the int8 K scales) in LDS; one vote byte per wavefront per entry
-  for (int e = tid; e < cnt; e += kThreads) {
-    const int j = glist[e];
-    lst[e] = (uint16_t)j;
-    code[e] = 0u;
-    if constexpr (G::I8) ksc[e] = kscale_row[j];
+  uint32_t* flags = reinterpret_cast<uint32_t*>(smem + NSLOT * G::K_BYTES);
+  uint16_t* ulst = reinterpret_cast<uint16_t*>(flags + (p.Tn + 3) / 4);
+  uint32_t* votes = reinterpret_cast<uint32_t*>(ulst + ((p.Tn + 1) & ~1));
+  float* ksc = reinterpret_cast<float*>(votes + NW * nwords);
+  for (int e = tid; e < (p.Tn + 3) / 4; e += kThreads * U) flags[e] = 0u;
+  for (int e = tid; e < NW * nwords; e += kThreads * U) votes[e] = 0u;
+  __syncthreads();
+  {
+    const uint16_t* gl = p.row_idx + row_id * p.Tn;
+    for (int e = tid - unit * kThreads; e < cnt; e += kThreads) {
+      const int j = gl[e];
+      atomicOr(&flags[j >> 2], 1u << (8 * (j & 3) + unit));
+    }
   }
   __syncthreads();
+  // union list in ascending j (wavefront 0, 64 tiles at a time)
+  if (wave == 0) {
+    int n = 0;
+    const unsigned char* fb = reinterpret_cast<const unsigned char*>(flags);
+    for (int base = 0; base < p.Tn; base += 64) {
+      const int j = base + lane;
+      const uint32_t m = j < p.Tn ? (uint32_t)fb[j] : 0u;
+      const unsigned long long bal = __ballot(m != 0);
+      if (m != 0) {
+        const int pos = n + (int)__popcll(bal & ((1ull << lane) - 1ull));
+        ulst[pos] = (uint16_t)(j | (m << 12));
+        if constexpr (G::I8) ksc[pos] = kscale_row[j];
+      }
+      n += (int)__popcll(bal);
+    }
+    if (lane == 0) s_ucnt = n;
+  }
+  __syncthreads();
+  const int UC = s_ucnt;
   const uint32_t ring_lds = lds_addr(ring);
 
-  f32x16 zero16 = f32x16{};
   float m_run = kNegInf;      // running max, log2 units
   float l_half = 0.0f;        // this lane half's share of the row sum
   int n_exec = 0, n_skip = 0, n_void = 0;
-  unsigned char* votes = reinterpret_cast<unsigned char*>(code);
+  uint32_t vw = 0;            // votes of the current 16 entries
 
-  // Software pipeline: step n runs the softmax of listed tile n on the VALU
-  // while the QK^T MFMAs of tile n+1 run; K_{n+2} .. K_{n+NSLOT-1} are in
-  // flight and K_{n+NSLOT} is issued into the slot tile n used.  The scores,
-  // MFMAs and exponentials form one branch-free block so the scheduler can
-  // interleave them.  After the last tile the next-tile MFMAs read a stale
-  // slot and are discarded.
-  int jd_v = 0;   // list entry of the next refill (read one step early)
-  int jn_v = 0;   // list entry of the next step
-  auto step = [&](int n, Acc (&cur)[2], Acc (&nxt)[2]) {
-    const int pend = min(cnt - 1, n + NSLOT - 1) - (n + 1);   // tiles issued after K_{n+1}
-    wait_pending<G::KCW, NSLOT - 2>(pend);
-    if (n + NSLOT < cnt)
-      L.issue_k(p, __builtin_amdgcn_readfirstlane(jd_v), ring_lds + (uint32_t)((n & (NSLOT - 1)) * G::K_BYTES));
-    const int j = __builtin_amdgcn_readfirstlane(jn_v);
-    jd_v = lst[min(n + 1 + NSLOT, p.Tn - 1)];
-    jn_v = lst[min(n + 1, p.Tn - 1)];
-    float c_scale = p.scale_log2;
-    if constexpr (G::I8) c_scale = L.qscale * ksc[n] * p.scale_log2;
-
-    u32x4 kf[2][G::QS];
-    L.template read_k<Acc>(ring + ((n + 1) & (NSLOT - 1)) * G::K_BYTES, kf);
-
-    float sv[2][16];
-    scores<CAUSAL>(p, cur, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
-
-    // ---- online softmax (eq. 1) in log2 units; the scale is folded into an FMA ----
-    float mx = kNegInf;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
-    mx = max_halves(mx);
-    const float mloc = mx * c_scale;                 // c_scale > 0: max commutes with the scale
-    const float m_new = fmaxf(m_run, mloc);
-    const bool finite_row = mloc > kNegInf;
-    // lambda vote over the wavefront's 32 rows
-    const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
-    const bool any_finite = __any(finite_row);
-    const bool exec = __any(wants_pv);
-    const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
-    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
-
-    // next tile's S^T on the matrix cores, interleaved with this tile's exponentials
-    float ps[2 * G::QS];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) nxt[t] = Acc{};
-#pragma unroll
-    for (int s = 0; s < G::QS; ++s) {
+  // Entry e is used in step e; entries e+1 .. e+NSLOT-2 are in flight when
+  // step e starts, and step e refills the slot entry e-1 used with entry
+  // e+NSLOT-1.  The slot of entry e is the compile-time SL = e % NSLOT.
+  int jd_v = 0;   // tile of the next refill (read one step early)
+  int en_v = 0;   // union entry of the next step
+  auto step = [&](int e, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const int pend = min(UC - 1, e + NSLOT - 2) - e;    // entries issued after entry e
+    wait_pending<KCW, NSLOT - 2>(pend);
+    if (e + NSLOT - 1 < UC)
+      L.issue_k(p, __builtin_amdgcn_readfirstlane(jd_v), ring_lds + (uint32_t)(((SL + NSLOT - 1) % NSLOT) * G::K_BYTES));
+    const int en = __builtin_amdgcn_readfirstlane(en_v);
+    jd_v = ulst[min(e + NSLOT, p.Tn - 1)] & 0xfff;
+    en_v = ulst[min(e + 1, p.Tn - 1)];
+    uint32_t code = 0;
+    if ((en >> (12 + unit)) & 1) {          // this block lists the tile
+      const int j = en & 0xfff;
+      float c_scale = p.scale_log2;
+      if constexpr (G::I8) c_scale = L.qscale * ksc[e] * p.scale_log2;
+      u32x4 kf[2][G::QS];
+      L.read_k(ring + SL * G::K_BYTES, kf);
+      Acc acc[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        nxt[t] = mfma_qk<KIND>(kf[t][s], L.qf[s], nxt[t]);
-        const int u = 2 * s + t;
-        float acc = 0.0f;
+        acc[t] = Acc{};
 #pragma unroll
-        for (int e = 0; e < G::EPM; ++e) {
-          const int idx = u * G::EPM + e;
-          acc += fast_exp2(fmaf(sv[idx >> 4][idx & 15], c_scale, neg_m));
-        }
-        ps[u] = acc;
+        for (int s = 0; s < G::QS; ++s) acc[t] = mfma_qk<KIND>(kf[t][s], L.qf[s], acc[t]);
       }
-    }
-    float psum = 0.0f;
+      // the scores as floats, masked in place (the raw accumulator is dead after)
+      f32x16 sv[2];
+      if constexpr (G::I8) {
 #pragma unroll
-    for (int u = 0; u < 2 * G::QS; ++u) psum += ps[u];
-    // P~ always feeds l (Algorithm 1 computes it before the M_pv test)
-    l_half = alpha * l_half + psum;
-    m_run = m_new;
-    // keep this tile's exponentials inside this step (next to the MFMAs they
-    // overlap) instead of letting them sink into the next one
-    asm volatile("" : "+v"(l_half));
-    const unsigned char c = exec ? 1 : (any_finite ? 2 : 3);
-    n_exec += exec ? 1 : 0;
-    n_skip += (!exec && any_finite) ? 1 : 0;
-    n_void += any_finite ? 0 : 1;
-    votes[n * kWavesPerBlock + wave] = c;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
+      } else {
+        sv[0] = acc[0];
+        sv[1] = acc[1];
+      }
+      mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
+      // ---- online softmax (eq. 1) in log2 units; the scale is folded into an FMA ----
+      // row max: 4 independent chains of 8 values starting from -inf, then 4 -> 1
+      float mq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = 8 * (q & 1);
+        float m = kNegInf;
+#pragma unroll
+        for (int x = 0; x < 8; x += 2) m = fmaxf(fmaxf(m, sv[q >> 1][o + x]), sv[q >> 1][o + x + 1]);
+        mq[q] = m;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(mq[0], mq[1]), mq[2]), mq[3]);
+      mx = max_halves(mx);
+      const float mloc = mx * c_scale;               // c_scale > 0: max commutes with the scale
+      const float m_new = fmaxf(m_run, mloc);
+      const bool finite_row = mloc > kNegInf;
+      // lambda vote over the wavefront's 32 rows
+      const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
+      const bool any_finite = __any(finite_row);
+      const bool exec = __any(wants_pv);
+      const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
+      // P~ always feeds l (Algorithm 1 computes it before the M_pv test)
+      float ps[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x16& vv = sv[q >> 2];
+        const int o = 4 * (q & 3);
+        ps[q] = (fast_exp2(fmaf(vv[o], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 1], c_scale, neg_m))) +
+                (fast_exp2(fmaf(vv[o + 2], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 3], c_scale, neg_m)));
+      }
+      const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+      l_half = alpha * l_half + psum;
+      m_run = m_new;
+      code = exec ? 1u : (any_finite ? 2u : 3u);
+      n_exec += exec ? 1 : 0;
+      n_skip += (!exec && any_finite) ? 1 : 0;
+      n_void += any_finite ? 0 : 1;
+    }
+    vw |= code << (2 * (e & 15));
+    if ((e & 15) == 15 || e == UC - 1) {
+      votes[wave * nwords + (e >> 4)] = vw;
+      vw = 0;
+    }
   };
-  (void)zero16;
 
-  Acc s_a[2], s_b[2];
-  if (cnt > 0) {
-    const int pre = min(cnt, NSLOT);
-    for (int t = 0; t < pre; ++t)
-      L.issue_k(p, __builtin_amdgcn_readfirstlane((int)lst[t]), ring_lds + (uint32_t)(t * G::K_BYTES));
-    wait_pending<G::KCW, NSLOT - 1>(pre - 1);   // K_0 has landed everywhere
-    u32x4 kf[2][G::QS];
-    L.template read_k<Acc>(ring, kf);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s_a[t] = Acc{};
-#pragma unroll
-      for (int s = 0; s < G::QS; ++s) s_a[t] = mfma_qk<KIND>(kf[t][s], L.qf[s], s_a[t]);
-    }
-    jn_v = lst[0];
-    jd_v = lst[min(NSLOT, p.Tn - 1)];
+  const int pre = min(UC, NSLOT - 1);
+  for (int t = 0; t < pre; ++t)
+    L.issue_k(p, __builtin_amdgcn_readfirstlane((int)(ulst[t] & 0xfff)), ring_lds + (uint32_t)(t * G::K_BYTES));
+  if (UC > 0) {
+    en_v = ulst[0];
+    jd_v = ulst[min(NSLOT - 1, p.Tn - 1)] & 0xfff;
   }
-  int n = 0;
-  for (; n + 1 < cnt; n += 2) {           // unrolled by two so the score buffers swap roles
-    step(n, s_a, s_b);
-    step(n + 1, s_b, s_a);
+  static_assert(NSLOT == 4, "the step loop is unrolled by the ring depth");
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  int e = 0;
+  for (; e + 4 <= UC; e += 4) {
+    step(e, I0{});
+    step(e + 1, I1{});
+    step(e + 2, I2{});
+    step(e + 3, I3{});
   }
-  if (n < cnt) step(n, s_a, s_b);
-  wait_barrier<0>();                       // every vote byte is written
+  if (e < UC) step(e, I0{});
+  if (e + 1 < UC) step(e + 1, I1{});
+  if (e + 2 < UC) step(e + 2, I2{});
+  wait_barrier<0>();                       // every vote word is written
 
-  // ---- the executed-tile list: listed tiles with at least one voting wavefront ----
-  if (wave == 0) {
+  // ---- per block: its executed-tile list (listed tiles with a voting wavefront) ----
+  const unsigned char umask = (unsigned char)(1u << unit);
+  if (wq == 0 && has_rows) {
     uint32_t* ul = p.ulist + row_id * p.Tn;
-    int U = 0;
-    for (int base = 0; base < cnt; base += 64) {
-      const int e = base + lane;
-      uint32_t m = 0;
-      if (e < cnt) {
-        const uint32_t cw = code[e];
+    int n = 0;
+    for (int base = 0; base < UC; base += 64) {
+      const int x = base + lane;
+      uint32_t m = 0, j = 0;
+      if (x < UC) {
+        const uint32_t en = ulst[x];
+        j = en & 0xfffu;
+        if ((en >> 12) & umask) {
 #pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) m |= (((cw >> (8 * w)) & 0xffu) == 1u ? 1u : 0u) << w;
+          for (int w = 0; w < kWavesPerBlock; ++w) {
+            const uint32_t c = (votes[(unit * kWavesPerBlock + w) * nwords + (x >> 4)] >> (2 * (x & 15))) & 3u;
+            m |= (c == 1u ? 1u : 0u) << w;
+          }
+        }
       }
       const unsigned long long bal = __ballot(m != 0);
-      const int pos = U + (int)__popcll(bal & ((1ull << lane) - 1ull));
-      if (m != 0) ul[pos] = (uint32_t)lst[e] | (m << 16);
-      U += (int)__popcll(bal);
+      const int pos = n + (int)__popcll(bal & ((1ull << lane) - 1ull));
+      if (m != 0) ul[pos] = j | (m << 16);
+      n += (int)__popcll(bal);
     }
-    if (lane == 0) p.ucnt[row_id] = U;
+    if (lane == 0) p.ucnt[row_id] = n;
   }
   const float l_tot = sum_halves(l_half);
   if (L.qvalid && L.hl == 0) {
@@ -511,11 +583,14 @@ void attn_stats(AttnArgs p) {
     p.row_m[r] = m_run;
     p.row_l[r] = l_tot;
   }
-  if (p.dbg != nullptr) {
+  if (p.dbg != nullptr && has_rows) {
     uint8_t* drow = p.dbg + row_id * p.Tn * kWavesPerBlock;
-    for (int e = tid; e < cnt * kWavesPerBlock; e += kThreads) {
-      const int w = e & (kWavesPerBlock - 1);
-      if (i * kBq + w * kRowsPerWave < p.N) drow[(int)lst[e / kWavesPerBlock] * kWavesPerBlock + w] = votes[e];
+    for (int x = tid - unit * kThreads; x < UC * kWavesPerBlock; x += kThreads) {
+      const int e2 = x / kWavesPerBlock, w = x % kWavesPerBlock;
+      const uint32_t en = ulst[e2];
+      if (((en >> 12) & umask) && i * kBq + w * kRowsPerWave < p.N)
+        drow[(int)(en & 0xfffu) * kWavesPerBlock + w] =
+            (uint8_t)((votes[(unit * kWavesPerBlock + w) * nwords + (e2 >> 4)] >> (2 * (e2 & 15))) & 3u);
     }
   }
 
@@ -529,22 +604,22 @@ void attn_stats(AttnArgs p) {
     red[wave][3] = n_empty;
   }
   __syncthreads();
-  if (tid == 0 && p.counts != nullptr) {
-    unsigned long long e = 0, s = 0, v = 0, em = 0;
+  if (wq == 0 && lane == 0 && has_rows && p.counts != nullptr) {
+    unsigned long long ex = 0, sk = 0, vo = 0, em = 0;
     for (int w = 0; w < kWavesPerBlock; ++w) {
       // waves whose 32 rows all lie beyond N hold no group
       if (i * kBq + w * kRowsPerWave >= p.N) continue;
-      e += red[w][0];
-      s += red[w][1];
-      v += red[w][2];
-      em += red[w][3];
+      ex += red[unit * kWavesPerBlock + w][0];
+      sk += red[unit * kWavesPerBlock + w][1];
+      vo += red[unit * kWavesPerBlock + w][2];
+      em += red[unit * kWavesPerBlock + w][3];
     }
     atomicAdd(p.counts + SPARGE_CNT_LIVE, (unsigned long long)n_live);
     atomicAdd(p.counts + SPARGE_CNT_QK_EXEC, (unsigned long long)cnt);
     atomicAdd(p.counts + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - cnt));
-    atomicAdd(p.counts + SPARGE_CNT_PV_EXEC, e);
-    atomicAdd(p.counts + SPARGE_CNT_PV_SKIP, s);
-    atomicAdd(p.counts + SPARGE_CNT_PV_VOID, v);
+    atomicAdd(p.counts + SPARGE_CNT_PV_EXEC, ex);
+    atomicAdd(p.counts + SPARGE_CNT_PV_SKIP, sk);
+    atomicAdd(p.counts + SPARGE_CNT_PV_VOID, vo);
     atomicAdd(p.counts + SPARGE_CNT_EMPTY_ROWS, em);
     atomicAdd(p.counts + SPARGE_CNT_ROWS, (unsigned long long)(last_q - i * kBq + 1));
   }
@@ -562,9 +637,9 @@ void attn_pv(AttnArgs p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   int b, h, i;
-  if (!map_block(p, b, h, i)) return;
-  Lane<D, KIND> L;
-  L.init(p, b, h, i);
+  if (!map_block(p, p.Tm, b, h, i)) return;
+  Lane<D, KIND, kWavesPerBlock> L;
+  L.init(p, b, h, i, (int)(threadIdx.x >> 6), true);
   const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
   const long long row_id = L.row_id;
   const int U = p.ucnt[row_id];
@@ -616,7 +691,7 @@ void attn_pv(AttnArgs p) {
   for (int t = 0; t < pre; ++t) issue(t, t);
   for (int e = 0; e < U; ++e) {
     const int pend = min(U - 1, e + NS - 2) - e;    // entries issued after entry e
-    wait_pending<G::KCW + G::VCW, NS - 2>(pend);
+    wait_pending<Lane<D, KIND, kWavesPerBlock>::KCW + G::VCW, NS - 2>(pend);
     if (e + NS - 1 < U) issue(e + NS - 1, (e + NS - 1) % NS);
     const uint32_t en = (uint32_t)__builtin_amdgcn_readfirstlane((int)ent[e]);
     const int j = (int)(en & 0xffffu);
@@ -624,7 +699,7 @@ void attn_pv(AttnArgs p) {
       const unsigned char* kt = smem + (e % NS) * G::E_BYTES;
       const unsigned char* vt = kt + G::K_BYTES;
       u32x4 kf[2][G::QS];
-      L.template read_k<Acc>(kt, kf);
+      L.read_k(kt, kf);
       Acc acc[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -634,8 +709,12 @@ void attn_pv(AttnArgs p) {
       }
       float c_scale = p.scale_log2;
       if constexpr (G::I8) c_scale = L.qscale * ksc[e] * p.scale_log2;
-      float sv[2][16];
-      scores<CAUSAL>(p, acc, sv, j, L.q0, L.qrow, L.qvalid, hl);
+      f32x16 sv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
+      mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, hl);
       // P = exp(S - m_final), packed in the P~V input type as the B operand of 4 k-steps
       u32x4 pb[4];
 #pragma unroll
@@ -736,6 +815,8 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 template <int D, int KIND, bool CAUSAL>
 hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
   const long long blocks = (long long)a.B * a.H * a.Tm;
+  constexpr int U = Geo<D, KIND>::UNITS;
+  const long long groups = (long long)a.B * a.H * ((a.Tm + U - 1) / U);
   const size_t lds1 = stats_lds_bytes<D, KIND>(a.Tn);
   const size_t lds2 = pv_lds_bytes<D, KIND>(a.Tn);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL>),
@@ -744,7 +825,7 @@ hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pv<D, KIND, CAUSAL>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds1, st, a);
+  hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL>), dim3((unsigned)groups), dim3(kThreads * U), lds1, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_pv<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds2, st, a);
