@@ -58,6 +58,9 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 // attention pass 1: query blocks per workgroup (4 wavefronts each)
 constexpr int kStatsUnits = 2;
+// log2-units distance below the running max past which a whole tile's
+// exponentials cannot change a float32 row sum (see attn_stats)
+constexpr float kFarLog2 = 40.0f;
 
 // v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
 // in the other, so combining the two gives every lane the pair (l, l ^ 32).
@@ -441,20 +444,13 @@ void attn_stats(AttnArgs p) {
   int n_exec = 0, n_skip = 0, n_void = 0;
   uint32_t vw = 0;            // votes of the current 16 entries
 
-  // Entry e is used in step e; entries e+1 .. e+NSLOT-2 are in flight when
-  // step e starts, and step e refills the slot entry e-1 used with entry
-  // e+NSLOT-1.  The slot of entry e is the compile-time SL = e % NSLOT.
-  int jd_v = 0;   // tile of the next refill (read one step early)
-  int en_v = 0;   // union entry of the next step
-  auto step = [&](int e, auto slot_c) {
+  int jd_v = 0;   // tiles of the next refill (read one pair early)
+  int en_v = 0;
+  // tile(e): entry e's scores and softmax for this wavefront (the tile has
+  // landed and the workgroup has passed the barrier that covers it)
+  auto tile = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    const int pend = min(UC - 1, e + NSLOT - 2) - e;    // entries issued after entry e
-    wait_pending<KCW, NSLOT - 2>(pend);
-    if (e + NSLOT - 1 < UC)
-      L.issue_k(p, __builtin_amdgcn_readfirstlane(jd_v), ring_lds + (uint32_t)(((SL + NSLOT - 1) % NSLOT) * G::K_BYTES));
-    const int en = __builtin_amdgcn_readfirstlane(en_v);
-    jd_v = ulst[min(e + NSLOT, p.Tn - 1)] & 0xfff;
-    en_v = ulst[min(e + 1, p.Tn - 1)];
+    const int en = __builtin_amdgcn_readfirstlane((int)ulst[e]);
     uint32_t code = 0;
     if ((en >> (12 + unit)) & 1) {          // this block lists the tile
       const int j = en & 0xfff;
@@ -501,19 +497,26 @@ void attn_stats(AttnArgs p) {
       const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
       const bool any_finite = __any(finite_row);
       const bool exec = __any(wants_pv);
-      const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
-      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
-      // P~ always feeds l (Algorithm 1 computes it before the M_pv test)
-      float ps[8];
+      // P~ always feeds l (Algorithm 1 computes it before the M_pv test).  When
+      // every row's tile maximum lies more than kFarLog2 below its running max,
+      // m does not move and each P~ is below 2^-kFarLog2: the tile adds less
+      // than 64 * 2^-40 to l >= 1, which a float32 sum of l cannot hold, so
+      // its exponentials are not evaluated.
+      const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
+      if (!far) {
+        const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+        const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
+        float ps[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x16& vv = sv[q >> 2];
-        const int o = 4 * (q & 3);
-        ps[q] = (fast_exp2(fmaf(vv[o], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 1], c_scale, neg_m))) +
-                (fast_exp2(fmaf(vv[o + 2], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 3], c_scale, neg_m)));
+        for (int q = 0; q < 8; ++q) {
+          const f32x16& vv = sv[q >> 2];
+          const int o = 4 * (q & 3);
+          ps[q] = (fast_exp2(fmaf(vv[o], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 1], c_scale, neg_m))) +
+                  (fast_exp2(fmaf(vv[o + 2], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 3], c_scale, neg_m)));
+        }
+        const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+        l_half = alpha * l_half + psum;
       }
-      const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-      l_half = alpha * l_half + psum;
       m_run = m_new;
       code = exec ? 1u : (any_finite ? 2u : 3u);
       n_exec += exec ? 1 : 0;
@@ -527,28 +530,48 @@ void attn_stats(AttnArgs p) {
     }
   };
 
-  const int pre = min(UC, NSLOT - 1);
-  for (int t = 0; t < pre; ++t)
+  // Two entries per barrier: the pair (e, e+1) uses slots SL, SL+1; at its
+  // barrier everything issued has landed, and the pair before it is done, so
+  // its slots are refilled with e+2, e+3 (loaded while this pair runs).
+  static_assert(NSLOT == 4, "two pairs of slots");
+  auto sync2 = [&](int e, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    wait_barrier<0>();
+    const int j2 = __builtin_amdgcn_readfirstlane(jd_v);
+    const int j3 = __builtin_amdgcn_readfirstlane(en_v);
+    if (e + 2 < UC) L.issue_k(p, j2, ring_lds + (uint32_t)(((SL + 2) % NSLOT) * G::K_BYTES));
+    if (e + 3 < UC) L.issue_k(p, j3, ring_lds + (uint32_t)(((SL + 3) % NSLOT) * G::K_BYTES));
+    jd_v = ulst[min(e + 4, p.Tn - 1)] & 0xfff;
+    en_v = ulst[min(e + 5, p.Tn - 1)] & 0xfff;
+  };
+  for (int t = 0; t < min(UC, 2); ++t)
     L.issue_k(p, __builtin_amdgcn_readfirstlane((int)(ulst[t] & 0xfff)), ring_lds + (uint32_t)(t * G::K_BYTES));
   if (UC > 0) {
-    en_v = ulst[0];
-    jd_v = ulst[min(NSLOT - 1, p.Tn - 1)] & 0xfff;
+    jd_v = ulst[min(2, p.Tn - 1)] & 0xfff;
+    en_v = ulst[min(3, p.Tn - 1)] & 0xfff;
   }
-  static_assert(NSLOT == 4, "the step loop is unrolled by the ring depth");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   int e = 0;
   for (; e + 4 <= UC; e += 4) {
-    step(e, I0{});
-    step(e + 1, I1{});
-    step(e + 2, I2{});
-    step(e + 3, I3{});
+    sync2(e, I0{});
+    tile(e, I0{});
+    tile(e + 1, I1{});
+    sync2(e + 2, I2{});
+    tile(e + 2, I2{});
+    tile(e + 3, I3{});
   }
-  if (e < UC) step(e, I0{});
-  if (e + 1 < UC) step(e + 1, I1{});
-  if (e + 2 < UC) step(e + 2, I2{});
+  if (e < UC) {
+    sync2(e, I0{});
+    tile(e, I0{});
+    if (e + 1 < UC) tile(e + 1, I1{});
+    if (e + 2 < UC) {
+      sync2(e + 2, I2{});
+      tile(e + 2, I2{});
+    }
+  }
   wait_barrier<0>();                       // every vote word is written
 
   // ---- per block: its executed-tile list (listed tiles with a voting wavefront) ----
