@@ -57,7 +57,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 // attention pass 1: query blocks per workgroup (4 wavefronts each)
-constexpr int kStatsUnits = 2;
+constexpr int kStatsUnits = 1;
 // log2-units distance below the running max past which a whole tile's
 // exponentials cannot change a float32 row sum (see attn_stats)
 constexpr float kFarLog2 = 40.0f;
@@ -202,8 +202,9 @@ struct Geo {
   static constexpr int QS = I8 ? D / 32 : D / 16;      // k-steps of the QK^T MFMA
   static constexpr int OT = D / 32;                    // 32-column tiles of O^T
   static constexpr int EPM = 32 / (2 * QS);            // scores per lane per QK^T MFMA
-  // pass 1: K ring slots
-  static constexpr int NSLOT = 4;
+  // pass 1: K ring slots (two when a workgroup holds one block, so four
+  // workgroups fit a CU)
+  static constexpr int NSLOT = kStatsUnits == 1 ? 2 : 4;
   // pass 1: query blocks (of 4 wavefronts) per workgroup sharing one K ring
   static constexpr int UNITS = kStatsUnits;
   // pass 2: (K, V^T) slots
@@ -456,15 +457,30 @@ void attn_stats(AttnArgs p) {
       const int j = en & 0xfff;
       float c_scale = p.scale_log2;
       if constexpr (G::I8) c_scale = L.qscale * ksc[e] * p.scale_log2;
-      u32x4 kf[2][G::QS];
-      L.read_k(ring + SL * G::K_BYTES, kf);
-      Acc acc[2];
+      // K operands in k-step order, both 32-key halves per step, so the two
+      // accumulator chains alternate and each operand is read a few steps
+      // before its MFMA
+      const unsigned char* kt = ring + SL * G::K_BYTES;
+      u32x4 kf[G::QS][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        acc[t] = Acc{};
+      for (int s = 0; s < G::QS; ++s)
 #pragma unroll
-        for (int s = 0; s < G::QS; ++s) acc[t] = mfma_qk<KIND>(kf[t][s], L.qf[s], acc[t]);
+        for (int t = 0; t < 2; ++t)
+          kf[s][t] = *reinterpret_cast<const u32x4*>(kt + t * 32 * G::KROW + (L.k_rd ^ (32u * s)));
+      Acc acc[2] = {Acc{}, Acc{}};
+#pragma unroll
+      for (int s = 0; s < G::QS; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma_qk<KIND>(kf[s][t], L.qf[s], acc[t]);
+      // issue order: the reads run KLA k-steps ahead of the MFMAs that use them
+      constexpr int KLA = 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KLA, 0);
+#pragma unroll
+      for (int s = 0; s < G::QS - KLA; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KLA, 0);
       // the scores as floats, masked in place (the raw accumulator is dead after)
       f32x16 sv[2];
       if constexpr (G::I8) {
@@ -533,43 +549,73 @@ void attn_stats(AttnArgs p) {
   // Two entries per barrier: the pair (e, e+1) uses slots SL, SL+1; at its
   // barrier everything issued has landed, and the pair before it is done, so
   // its slots are refilled with e+2, e+3 (loaded while this pair runs).
-  static_assert(NSLOT == 4, "two pairs of slots");
-  auto sync2 = [&](int e, auto slot_c) {
-    constexpr int SL = decltype(slot_c)::value;
-    wait_barrier<0>();
-    const int j2 = __builtin_amdgcn_readfirstlane(jd_v);
-    const int j3 = __builtin_amdgcn_readfirstlane(en_v);
-    if (e + 2 < UC) L.issue_k(p, j2, ring_lds + (uint32_t)(((SL + 2) % NSLOT) * G::K_BYTES));
-    if (e + 3 < UC) L.issue_k(p, j3, ring_lds + (uint32_t)(((SL + 3) % NSLOT) * G::K_BYTES));
-    jd_v = ulst[min(e + 4, p.Tn - 1)] & 0xfff;
-    en_v = ulst[min(e + 5, p.Tn - 1)] & 0xfff;
-  };
-  for (int t = 0; t < min(UC, 2); ++t)
-    L.issue_k(p, __builtin_amdgcn_readfirstlane((int)(ulst[t] & 0xfff)), ring_lds + (uint32_t)(t * G::K_BYTES));
-  if (UC > 0) {
-    jd_v = ulst[min(2, p.Tn - 1)] & 0xfff;
-    en_v = ulst[min(3, p.Tn - 1)] & 0xfff;
-  }
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  int e = 0;
-  for (; e + 4 <= UC; e += 4) {
-    sync2(e, I0{});
-    tile(e, I0{});
-    tile(e + 1, I1{});
-    sync2(e + 2, I2{});
-    tile(e + 2, I2{});
-    tile(e + 3, I3{});
-  }
-  if (e < UC) {
-    sync2(e, I0{});
-    tile(e, I0{});
-    if (e + 1 < UC) tile(e + 1, I1{});
-    if (e + 2 < UC) {
+  if constexpr (NSLOT == 2) {
+    // one barrier per entry: entry e has landed (the only load in flight),
+    // every wavefront is done with entry e-1, whose slot takes entry e+1
+    if (UC > 0) {
+      L.issue_k(p, __builtin_amdgcn_readfirstlane((int)(ulst[0] & 0xfff)), ring_lds);
+      jd_v = ulst[min(1, p.Tn - 1)] & 0xfff;
+    }
+    auto sync1 = [&](int e, auto slot_c) {
+      constexpr int SL = decltype(slot_c)::value;
+      wait_barrier<0>();
+      const int j1 = __builtin_amdgcn_readfirstlane(jd_v);
+      if (e + 1 < UC) L.issue_k(p, j1, ring_lds + (uint32_t)((1 - SL) * G::K_BYTES));
+      jd_v = ulst[min(e + 2, p.Tn - 1)] & 0xfff;
+    };
+    int e = 0;
+    for (; e + 2 <= UC; e += 2) {
+      sync1(e, I0{});
+      tile(e, I0{});
+      sync1(e + 1, I1{});
+      tile(e + 1, I1{});
+    }
+    if (e < UC) {
+      sync1(e, I0{});
+      tile(e, I0{});
+    }
+  } else {
+    static_assert(NSLOT == 4, "two pairs of slots");
+    // Two entries per barrier: the pair (e, e+1) uses slots SL, SL+1; at its
+    // barrier everything issued has landed, and the pair before it is done,
+    // so its slots are refilled with e+2, e+3 (loaded while this pair runs).
+    auto sync2 = [&](int e, auto slot_c) {
+      constexpr int SL = decltype(slot_c)::value;
+      wait_barrier<0>();
+      const int j2 = __builtin_amdgcn_readfirstlane(jd_v);
+      const int j3 = __builtin_amdgcn_readfirstlane(en_v);
+      if (e + 2 < UC) L.issue_k(p, j2, ring_lds + (uint32_t)(((SL + 2) % NSLOT) * G::K_BYTES));
+      if (e + 3 < UC) L.issue_k(p, j3, ring_lds + (uint32_t)(((SL + 3) % NSLOT) * G::K_BYTES));
+      jd_v = ulst[min(e + 4, p.Tn - 1)] & 0xfff;
+      en_v = ulst[min(e + 5, p.Tn - 1)] & 0xfff;
+    };
+    for (int t = 0; t < min(UC, 2); ++t)
+      L.issue_k(p, __builtin_amdgcn_readfirstlane((int)(ulst[t] & 0xfff)), ring_lds + (uint32_t)(t * G::K_BYTES));
+    if (UC > 0) {
+      jd_v = ulst[min(2, p.Tn - 1)] & 0xfff;
+      en_v = ulst[min(3, p.Tn - 1)] & 0xfff;
+    }
+    int e = 0;
+    for (; e + 4 <= UC; e += 4) {
+      sync2(e, I0{});
+      tile(e, I0{});
+      tile(e + 1, I1{});
       sync2(e + 2, I2{});
       tile(e + 2, I2{});
+      tile(e + 3, I3{});
+    }
+    if (e < UC) {
+      sync2(e, I0{});
+      tile(e, I0{});
+      if (e + 1 < UC) tile(e + 1, I1{});
+      if (e + 2 < UC) {
+        sync2(e + 2, I2{});
+        tile(e + 2, I2{});
+      }
     }
   }
   wait_barrier<0>();                       // every vote word is written
