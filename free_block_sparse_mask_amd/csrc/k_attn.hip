@@ -24,8 +24,8 @@
 //
 // At the workloads this path is built for, about one listed tile in eight
 // has a voting wavefront, so V (half of the bytes of a K/V pass) is read for
-// a small fraction of the tiles, and pass 1 can give all its LDS to a deep
-// ring of K tiles.
+// a small fraction of the tiles, and pass 1 holds only K: a two-slot ring
+// small enough that four workgroups share a CU.
 //
 // Layout (CDNA4 first, not the pages' CUDA warp layout):
 // * One workgroup of 4 wavefronts per query block i of 128 rows; wavefront w
@@ -56,8 +56,6 @@ namespace sparge {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-// attention pass 1: query blocks per workgroup (4 wavefronts each)
-constexpr int kStatsUnits = 1;
 // log2-units distance below the running max past which a whole tile's
 // exponentials cannot change a float32 row sum (see attn_stats)
 constexpr float kFarLog2 = 40.0f;
@@ -202,11 +200,8 @@ struct Geo {
   static constexpr int QS = I8 ? D / 32 : D / 16;      // k-steps of the QK^T MFMA
   static constexpr int OT = D / 32;                    // 32-column tiles of O^T
   static constexpr int EPM = 32 / (2 * QS);            // scores per lane per QK^T MFMA
-  // pass 1: K ring slots (two when a workgroup holds one block, so four
-  // workgroups fit a CU)
-  static constexpr int NSLOT = kStatsUnits == 1 ? 2 : 4;
-  // pass 1: query blocks (of 4 wavefronts) per workgroup sharing one K ring
-  static constexpr int UNITS = kStatsUnits;
+  // pass 1: K ring slots
+  static constexpr int NSLOT = 2;
   // pass 2: (K, V^T) slots
   static constexpr int E_BYTES = K_BYTES + V_BYTES;
   static constexpr int NS2 = (65536 / E_BYTES) >= 4 ? 4 : 2;
@@ -217,9 +212,8 @@ struct Geo {
 template <int D, int KIND>
 size_t stats_lds_bytes(int Tn) {
   using G = Geo<D, KIND>;
-  const size_t nw = (size_t)kWavesPerBlock * G::UNITS;
-  return (size_t)G::NSLOT * G::K_BYTES + (size_t)4 * ((Tn + 3) / 4) + (size_t)2 * ((Tn + 1) & ~1) +
-         (size_t)4 * nw * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
+  return (size_t)G::NSLOT * G::K_BYTES + (size_t)2 * ((Tn + 1) & ~1) +
+         (size_t)4 * kWavesPerBlock * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
 }
 template <int D, int KIND>
 size_t pv_lds_bytes(int Tn) {
@@ -286,6 +280,12 @@ struct Lane {
       kbase = static_cast<const unsigned char*>(p.k) + (b * p.k_sb + hk * p.k_sh) * 2;
       k_sn_bytes = p.k_sn * 2;
     }
+    // The Q loads complete here.  The compiler counts only the loads it
+    // emitted, so a wait it placed at their first use inside a tile loop
+    // would run every iteration, and vmcnt also counts the K tiles in flight
+    // through LDS-DMA: each tile would wait for the next one to land.
+#pragma unroll
+    for (int s = 0; s < G::QS; ++s) asm volatile("" : "+v"(qf[s]));
     loads_k = wave < G::KCH;
     k_row0 = G::KR * wave + lane / G::KG;
     k_gran = (uint32_t)(((lane % G::KG) ^ ((k_row0 / G::KSW) % G::KG)) * 16);
@@ -362,82 +362,48 @@ __device__ __forceinline__ void mask_scores(const AttnArgs& p, f32x16 (&sv)[2], 
 // ---------------------------------------------------------------------------
 // Pass 1: running max, row sums, lambda votes; K only
 // ---------------------------------------------------------------------------
-// One workgroup holds UNITS query blocks of one head (consecutive block rows,
-// 4 wavefronts each).  Their key lists are merged into one ascending union
-// list: each union entry's K tile is loaded once into the ring and used by
-// the wavefronts of every block that lists it.  Visiting a block's own tiles
-// in ascending order inside the union order keeps eq. (1) and the vote
-// exactly as for a lone block.  A wavefront keeps only the scores of the
-// current tile, so four wavefronts fit a SIMD and hide each other's MFMA,
-// exponential and LDS latencies.
+// One workgroup of 4 wavefronts per query block.  The block's listed K tiles
+// stream through a two-slot LDS ring, one barrier per tile.  A wavefront
+// keeps only the scores of the current tile (128 VGPRs), and the LDS of a
+// workgroup (two 16 KB slots, the list, the votes) stays under a quarter of
+// the CU's 160 KB, so four workgroups share a CU: four wavefronts per SIMD
+// hide each other's MFMA, exponential and LDS latencies.
 template <int D, int KIND, bool CAUSAL>
-__global__ __launch_bounds__(kThreads * kStatsUnits) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void attn_stats(AttnArgs p) {
   using G = Geo<D, KIND>;
   using Acc = typename std::conditional<G::I8, i32x16, f32x16>::type;
-  constexpr int U = G::UNITS;
-  constexpr int NW = kWavesPerBlock * U;
-  constexpr int NSLOT = G::NSLOT;
-  using LN = Lane<D, KIND, NW>;
-  constexpr int KCW = LN::KCW;
+  using LN = Lane<D, KIND, kWavesPerBlock>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ unsigned long long red[NW][4];
-  __shared__ int s_ucnt;
+  __shared__ unsigned long long red[kWavesPerBlock][4];
 
-  const int Tg = (p.Tm + U - 1) / U;
-  int b, h, g;
-  if (!map_block(p, Tg, b, h, g)) return;
+  int b, h, i;
+  if (!map_block(p, p.Tm, b, h, i)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int unit = wave / kWavesPerBlock, wq = wave % kWavesPerBlock;
-  const int i = g * U + unit;                 // this wavefront's query block
-  const bool has_rows = i < p.Tm;
   LN L;
-  L.init(p, b, h, i, wq, has_rows);
+  L.init(p, b, h, i, wave, true);
   const long long row_id = L.row_id;
-  const int last_q = has_rows ? min(p.N, (i + 1) * kBq) - 1 : 0;
-  const int n_live = !has_rows ? 0 : (CAUSAL ? min(p.Tn, last_q / kBk + 1) : p.Tn);
-  const int cnt = has_rows ? p.row_cnt[row_id] : 0;
-  const float* kscale_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
+  const int last_q = min(p.N, (i + 1) * kBq) - 1;
+  const int n_live = CAUSAL ? min(p.Tn, last_q / kBk + 1) : p.Tn;
+  const int UC = p.row_cnt[row_id];
 
-  // LDS: K ring | tile flags (one byte per tile: blocks listing it) | union
-  // list (j | block mask << 12) | votes (2 bits per wavefront and entry) |
-  // int8 K scales of the union entries
+  // LDS: K ring | the block's list | votes (2 bits per wavefront and entry) |
+  // int8 K scales of the listed tiles
   const int nwords = (p.Tn + 15) / 16;
   unsigned char* ring = smem;
-  uint32_t* flags = reinterpret_cast<uint32_t*>(smem + NSLOT * G::K_BYTES);
-  uint16_t* ulst = reinterpret_cast<uint16_t*>(flags + (p.Tn + 3) / 4);
-  uint32_t* votes = reinterpret_cast<uint32_t*>(ulst + ((p.Tn + 1) & ~1));
-  float* ksc = reinterpret_cast<float*>(votes + NW * nwords);
-  for (int e = tid; e < (p.Tn + 3) / 4; e += kThreads * U) flags[e] = 0u;
-  for (int e = tid; e < NW * nwords; e += kThreads * U) votes[e] = 0u;
-  __syncthreads();
+  uint16_t* lst = reinterpret_cast<uint16_t*>(smem + G::NSLOT * G::K_BYTES);
+  uint32_t* votes = reinterpret_cast<uint32_t*>(lst + ((p.Tn + 1) & ~1));
+  float* ksc = reinterpret_cast<float*>(votes + kWavesPerBlock * nwords);
   {
     const uint16_t* gl = p.row_idx + row_id * p.Tn;
-    for (int e = tid - unit * kThreads; e < cnt; e += kThreads) {
+    const float* kscale_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
+    for (int e = tid; e < UC; e += kThreads) {
       const int j = gl[e];
-      atomicOr(&flags[j >> 2], 1u << (8 * (j & 3) + unit));
+      lst[e] = (uint16_t)j;
+      if constexpr (G::I8) ksc[e] = kscale_row[j];
     }
   }
   __syncthreads();
-  // union list in ascending j (wavefront 0, 64 tiles at a time)
-  if (wave == 0) {
-    int n = 0;
-    const unsigned char* fb = reinterpret_cast<const unsigned char*>(flags);
-    for (int base = 0; base < p.Tn; base += 64) {
-      const int j = base + lane;
-      const uint32_t m = j < p.Tn ? (uint32_t)fb[j] : 0u;
-      const unsigned long long bal = __ballot(m != 0);
-      if (m != 0) {
-        const int pos = n + (int)__popcll(bal & ((1ull << lane) - 1ull));
-        ulst[pos] = (uint16_t)(j | (m << 12));
-        if constexpr (G::I8) ksc[pos] = kscale_row[j];
-      }
-      n += (int)__popcll(bal);
-    }
-    if (lane == 0) s_ucnt = n;
-  }
-  __syncthreads();
-  const int UC = s_ucnt;
   const uint32_t ring_lds = lds_addr(ring);
 
   float m_run = kNegInf;      // running max, log2 units
@@ -445,100 +411,94 @@ void attn_stats(AttnArgs p) {
   int n_exec = 0, n_skip = 0, n_void = 0;
   uint32_t vw = 0;            // votes of the current 16 entries
 
-  int jd_v = 0;   // tiles of the next refill (read one pair early)
-  int en_v = 0;
   // tile(e): entry e's scores and softmax for this wavefront (the tile has
-  // landed and the workgroup has passed the barrier that covers it)
+  // landed in slot SL and the workgroup has passed the barrier that covers it)
   auto tile = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    const int en = __builtin_amdgcn_readfirstlane((int)ulst[e]);
-    uint32_t code = 0;
-    if ((en >> (12 + unit)) & 1) {          // this block lists the tile
-      const int j = en & 0xfff;
-      float c_scale = p.scale_log2;
-      if constexpr (G::I8) c_scale = L.qscale * ksc[e] * p.scale_log2;
-      // K operands in k-step order, both 32-key halves per step, so the two
-      // accumulator chains alternate and each operand is read a few steps
-      // before its MFMA
-      const unsigned char* kt = ring + SL * G::K_BYTES;
-      u32x4 kf[G::QS][2];
+    const int j = __builtin_amdgcn_readfirstlane((int)lst[e]);
+    float c_scale = p.scale_log2;
+    if constexpr (G::I8) c_scale = L.qscale * ksc[e] * p.scale_log2;
+    // K operands in k-step order, both 32-key halves per step, so the two
+    // accumulator chains alternate and each operand is read a few steps
+    // before its MFMA
+    const unsigned char* kt = ring + SL * G::K_BYTES;
+    u32x4 kf[G::QS][2];
 #pragma unroll
-      for (int s = 0; s < G::QS; ++s)
+    for (int s = 0; s < G::QS; ++s)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          kf[s][t] = *reinterpret_cast<const u32x4*>(kt + t * 32 * G::KROW + (L.k_rd ^ (32u * s)));
-      Acc acc[2] = {Acc{}, Acc{}};
+      for (int t = 0; t < 2; ++t)
+        kf[s][t] = *reinterpret_cast<const u32x4*>(kt + t * 32 * G::KROW + (L.k_rd ^ (32u * s)));
+    Acc acc[2] = {Acc{}, Acc{}};
 #pragma unroll
-      for (int s = 0; s < G::QS; ++s)
+    for (int s = 0; s < G::QS; ++s)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t] = mfma_qk<KIND>(kf[s][t], L.qf[s], acc[t]);
-      // issue order: the reads run KLA k-steps ahead of the MFMAs that use them
-      constexpr int KLA = 2;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KLA, 0);
+      for (int t = 0; t < 2; ++t) acc[t] = mfma_qk<KIND>(kf[s][t], L.qf[s], acc[t]);
+    // issue order: the reads run KLA k-steps ahead of the MFMAs that use them
+    constexpr int KLA = 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KLA, 0);
 #pragma unroll
-      for (int s = 0; s < G::QS - KLA; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KLA, 0);
-      // the scores as floats, masked in place (the raw accumulator is dead after)
-      f32x16 sv[2];
-      if constexpr (G::I8) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
-      } else {
-        sv[0] = acc[0];
-        sv[1] = acc[1];
-      }
-      mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
-      // ---- online softmax (eq. 1) in log2 units; the scale is folded into an FMA ----
-      // row max: 4 independent chains of 8 values starting from -inf, then 4 -> 1
-      float mq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int o = 8 * (q & 1);
-        float m = kNegInf;
-#pragma unroll
-        for (int x = 0; x < 8; x += 2) m = fmaxf(fmaxf(m, sv[q >> 1][o + x]), sv[q >> 1][o + x + 1]);
-        mq[q] = m;
-      }
-      float mx = fmaxf(fmaxf(fmaxf(mq[0], mq[1]), mq[2]), mq[3]);
-      mx = max_halves(mx);
-      const float mloc = mx * c_scale;               // c_scale > 0: max commutes with the scale
-      const float m_new = fmaxf(m_run, mloc);
-      const bool finite_row = mloc > kNegInf;
-      // lambda vote over the wavefront's 32 rows
-      const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
-      const bool any_finite = __any(finite_row);
-      const bool exec = __any(wants_pv);
-      // P~ always feeds l (Algorithm 1 computes it before the M_pv test).  When
-      // every row's tile maximum lies more than kFarLog2 below its running max,
-      // m does not move and each P~ is below 2^-kFarLog2: the tile adds less
-      // than 64 * 2^-40 to l >= 1, which a float32 sum of l cannot hold, so
-      // its exponentials are not evaluated.
-      const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
-      if (!far) {
-        const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
-        const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
-        float ps[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const f32x16& vv = sv[q >> 2];
-          const int o = 4 * (q & 3);
-          ps[q] = (fast_exp2(fmaf(vv[o], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 1], c_scale, neg_m))) +
-                  (fast_exp2(fmaf(vv[o + 2], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 3], c_scale, neg_m)));
-        }
-        const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-        l_half = alpha * l_half + psum;
-      }
-      m_run = m_new;
-      code = exec ? 1u : (any_finite ? 2u : 3u);
-      n_exec += exec ? 1 : 0;
-      n_skip += (!exec && any_finite) ? 1 : 0;
-      n_void += any_finite ? 0 : 1;
+    for (int s = 0; s < G::QS - KLA; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KLA, 0);
+    // the scores as floats, masked in place (the raw accumulator is dead after)
+    f32x16 sv[2];
+    if constexpr (G::I8) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
+    } else {
+      sv[0] = acc[0];
+      sv[1] = acc[1];
+    }
+    mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
+    // ---- online softmax (eq. 1) in log2 units; the scale is folded into an FMA ----
+    // row max: 4 independent chains of 8 values starting from -inf, then 4 -> 1
+    float mq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int o = 8 * (q & 1);
+      float m = kNegInf;
+#pragma unroll
+      for (int x = 0; x < 8; x += 2) m = fmaxf(fmaxf(m, sv[q >> 1][o + x]), sv[q >> 1][o + x + 1]);
+      mq[q] = m;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(mq[0], mq[1]), mq[2]), mq[3]);
+    mx = max_halves(mx);
+    const float mloc = mx * c_scale;               // c_scale > 0: max commutes with the scale
+    const float m_new = fmaxf(m_run, mloc);
+    const bool finite_row = mloc > kNegInf;
+    // lambda vote over the wavefront's 32 rows
+    const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
+    const bool any_finite = __any(finite_row);
+    const bool exec = __any(wants_pv);
+    // P~ always feeds l (Algorithm 1 computes it before the M_pv test).  When
+    // every row's tile maximum lies more than kFarLog2 below its running max,
+    // m does not move and each P~ is below 2^-kFarLog2: the tile adds less
+    // than 64 * 2^-40 to l >= 1, which a float32 sum of l cannot hold, so
+    // its exponentials are not evaluated.
+    const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
+    if (!far) {
+      const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
+      float ps[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x16& vv = sv[q >> 2];
+        const int o = 4 * (q & 3);
+        ps[q] = (fast_exp2(fmaf(vv[o], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 1], c_scale, neg_m))) +
+                (fast_exp2(fmaf(vv[o + 2], c_scale, neg_m)) + fast_exp2(fmaf(vv[o + 3], c_scale, neg_m)));
+      }
+      const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+      l_half = alpha * l_half + psum;
+    }
+    m_run = m_new;
+    const uint32_t code = exec ? 1u : (any_finite ? 2u : 3u);
+    n_exec += exec ? 1 : 0;
+    n_skip += (!exec && any_finite) ? 1 : 0;
+    n_void += any_finite ? 0 : 1;
     vw |= code << (2 * (e & 15));
     if ((e & 15) == 15 || e == UC - 1) {
       votes[wave * nwords + (e >> 4)] = vw;
@@ -546,97 +506,49 @@ void attn_stats(AttnArgs p) {
     }
   };
 
-  // Two entries per barrier: the pair (e, e+1) uses slots SL, SL+1; at its
-  // barrier everything issued has landed, and the pair before it is done, so
-  // its slots are refilled with e+2, e+3 (loaded while this pair runs).
+  // One barrier per entry: at entry e's barrier its tile (the only load in
+  // flight) has landed and every wavefront is done with entry e-1, whose
+  // slot then takes entry e+1.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  if constexpr (NSLOT == 2) {
-    // one barrier per entry: entry e has landed (the only load in flight),
-    // every wavefront is done with entry e-1, whose slot takes entry e+1
-    if (UC > 0) {
-      L.issue_k(p, __builtin_amdgcn_readfirstlane((int)(ulst[0] & 0xfff)), ring_lds);
-      jd_v = ulst[min(1, p.Tn - 1)] & 0xfff;
-    }
-    auto sync1 = [&](int e, auto slot_c) {
-      constexpr int SL = decltype(slot_c)::value;
-      wait_barrier<0>();
-      const int j1 = __builtin_amdgcn_readfirstlane(jd_v);
-      if (e + 1 < UC) L.issue_k(p, j1, ring_lds + (uint32_t)((1 - SL) * G::K_BYTES));
-      jd_v = ulst[min(e + 2, p.Tn - 1)] & 0xfff;
-    };
-    int e = 0;
-    for (; e + 2 <= UC; e += 2) {
-      sync1(e, I0{});
-      tile(e, I0{});
-      sync1(e + 1, I1{});
-      tile(e + 1, I1{});
-    }
-    if (e < UC) {
-      sync1(e, I0{});
-      tile(e, I0{});
-    }
-  } else {
-    static_assert(NSLOT == 4, "two pairs of slots");
-    // Two entries per barrier: the pair (e, e+1) uses slots SL, SL+1; at its
-    // barrier everything issued has landed, and the pair before it is done,
-    // so its slots are refilled with e+2, e+3 (loaded while this pair runs).
-    auto sync2 = [&](int e, auto slot_c) {
-      constexpr int SL = decltype(slot_c)::value;
-      wait_barrier<0>();
-      const int j2 = __builtin_amdgcn_readfirstlane(jd_v);
-      const int j3 = __builtin_amdgcn_readfirstlane(en_v);
-      if (e + 2 < UC) L.issue_k(p, j2, ring_lds + (uint32_t)(((SL + 2) % NSLOT) * G::K_BYTES));
-      if (e + 3 < UC) L.issue_k(p, j3, ring_lds + (uint32_t)(((SL + 3) % NSLOT) * G::K_BYTES));
-      jd_v = ulst[min(e + 4, p.Tn - 1)] & 0xfff;
-      en_v = ulst[min(e + 5, p.Tn - 1)] & 0xfff;
-    };
-    for (int t = 0; t < min(UC, 2); ++t)
-      L.issue_k(p, __builtin_amdgcn_readfirstlane((int)(ulst[t] & 0xfff)), ring_lds + (uint32_t)(t * G::K_BYTES));
-    if (UC > 0) {
-      jd_v = ulst[min(2, p.Tn - 1)] & 0xfff;
-      en_v = ulst[min(3, p.Tn - 1)] & 0xfff;
-    }
-    int e = 0;
-    for (; e + 4 <= UC; e += 4) {
-      sync2(e, I0{});
-      tile(e, I0{});
-      tile(e + 1, I1{});
-      sync2(e + 2, I2{});
-      tile(e + 2, I2{});
-      tile(e + 3, I3{});
-    }
-    if (e < UC) {
-      sync2(e, I0{});
-      tile(e, I0{});
-      if (e + 1 < UC) tile(e + 1, I1{});
-      if (e + 2 < UC) {
-        sync2(e + 2, I2{});
-        tile(e + 2, I2{});
-      }
-    }
+  int jd_v = 0;               // tile of the next refill (read one entry early)
+  if (UC > 0) {
+    L.issue_k(p, __builtin_amdgcn_readfirstlane((int)lst[0]), ring_lds);
+    jd_v = lst[min(1, UC - 1)];
+  }
+  auto sync1 = [&](int e, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    wait_barrier<0>();
+    const int j1 = __builtin_amdgcn_readfirstlane(jd_v);
+    if (e + 1 < UC) L.issue_k(p, j1, ring_lds + (uint32_t)((1 - SL) * G::K_BYTES));
+    jd_v = lst[min(e + 2, UC - 1)];
+  };
+  int e = 0;
+  for (; e + 2 <= UC; e += 2) {
+    sync1(e, I0{});
+    tile(e, I0{});
+    sync1(e + 1, I1{});
+    tile(e + 1, I1{});
+  }
+  if (e < UC) {
+    sync1(e, I0{});
+    tile(e, I0{});
   }
   wait_barrier<0>();                       // every vote word is written
 
-  // ---- per block: its executed-tile list (listed tiles with a voting wavefront) ----
-  const unsigned char umask = (unsigned char)(1u << unit);
-  if (wq == 0 && has_rows) {
+  // ---- the block's executed-tile list (listed tiles with a voting wavefront) ----
+  if (wave == 0) {
     uint32_t* ul = p.ulist + row_id * p.Tn;
     int n = 0;
     for (int base = 0; base < UC; base += 64) {
       const int x = base + lane;
       uint32_t m = 0, j = 0;
       if (x < UC) {
-        const uint32_t en = ulst[x];
-        j = en & 0xfffu;
-        if ((en >> 12) & umask) {
+        j = lst[x];
 #pragma unroll
-          for (int w = 0; w < kWavesPerBlock; ++w) {
-            const uint32_t c = (votes[(unit * kWavesPerBlock + w) * nwords + (x >> 4)] >> (2 * (x & 15))) & 3u;
-            m |= (c == 1u ? 1u : 0u) << w;
-          }
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+          const uint32_t c = (votes[w * nwords + (x >> 4)] >> (2 * (x & 15))) & 3u;
+          m |= (c == 1u ? 1u : 0u) << w;
         }
       }
       const unsigned long long bal = __ballot(m != 0);
@@ -652,14 +564,13 @@ void attn_stats(AttnArgs p) {
     p.row_m[r] = m_run;
     p.row_l[r] = l_tot;
   }
-  if (p.dbg != nullptr && has_rows) {
+  if (p.dbg != nullptr) {
     uint8_t* drow = p.dbg + row_id * p.Tn * kWavesPerBlock;
-    for (int x = tid - unit * kThreads; x < UC * kWavesPerBlock; x += kThreads) {
+    for (int x = tid; x < UC * kWavesPerBlock; x += kThreads) {
       const int e2 = x / kWavesPerBlock, w = x % kWavesPerBlock;
-      const uint32_t en = ulst[e2];
-      if (((en >> 12) & umask) && i * kBq + w * kRowsPerWave < p.N)
-        drow[(int)(en & 0xfffu) * kWavesPerBlock + w] =
-            (uint8_t)((votes[(unit * kWavesPerBlock + w) * nwords + (e2 >> 4)] >> (2 * (e2 & 15))) & 3u);
+      if (i * kBq + w * kRowsPerWave < p.N)
+        drow[(int)lst[e2] * kWavesPerBlock + w] =
+            (uint8_t)((votes[w * nwords + (e2 >> 4)] >> (2 * (e2 & 15))) & 3u);
     }
   }
 
@@ -673,19 +584,19 @@ void attn_stats(AttnArgs p) {
     red[wave][3] = n_empty;
   }
   __syncthreads();
-  if (wq == 0 && lane == 0 && has_rows && p.counts != nullptr) {
+  if (tid == 0 && p.counts != nullptr) {
     unsigned long long ex = 0, sk = 0, vo = 0, em = 0;
     for (int w = 0; w < kWavesPerBlock; ++w) {
       // waves whose 32 rows all lie beyond N hold no group
       if (i * kBq + w * kRowsPerWave >= p.N) continue;
-      ex += red[unit * kWavesPerBlock + w][0];
-      sk += red[unit * kWavesPerBlock + w][1];
-      vo += red[unit * kWavesPerBlock + w][2];
-      em += red[unit * kWavesPerBlock + w][3];
+      ex += red[w][0];
+      sk += red[w][1];
+      vo += red[w][2];
+      em += red[w][3];
     }
     atomicAdd(p.counts + SPARGE_CNT_LIVE, (unsigned long long)n_live);
-    atomicAdd(p.counts + SPARGE_CNT_QK_EXEC, (unsigned long long)cnt);
-    atomicAdd(p.counts + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - cnt));
+    atomicAdd(p.counts + SPARGE_CNT_QK_EXEC, (unsigned long long)UC);
+    atomicAdd(p.counts + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - UC));
     atomicAdd(p.counts + SPARGE_CNT_PV_EXEC, ex);
     atomicAdd(p.counts + SPARGE_CNT_PV_SKIP, sk);
     atomicAdd(p.counts + SPARGE_CNT_PV_VOID, vo);
@@ -722,8 +633,11 @@ void attn_pv(AttnArgs p) {
     if constexpr (G::I8) ksc[e] = kscale_row[en & 0xffffu];
   }
   const long long srow = (long long)(b * p.H + h) * p.N + L.qrow;
-  const float m_row = L.qvalid ? p.row_m[srow] : kNegInf;
-  const float l_row = L.qvalid ? p.row_l[srow] : 0.0f;
+  float m_row = L.qvalid ? p.row_m[srow] : kNegInf;
+  float l_row = L.qvalid ? p.row_l[srow] : 0.0f;
+  // both loads complete before the first tile is issued (a wait the compiler
+  // placed at their first use would also wait for that tile)
+  asm volatile("" : "+v"(m_row), "+v"(l_row));
   __syncthreads();
 
   const unsigned char* vtbase =
@@ -884,8 +798,6 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 template <int D, int KIND, bool CAUSAL>
 hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
   const long long blocks = (long long)a.B * a.H * a.Tm;
-  constexpr int U = Geo<D, KIND>::UNITS;
-  const long long groups = (long long)a.B * a.H * ((a.Tm + U - 1) / U);
   const size_t lds1 = stats_lds_bytes<D, KIND>(a.Tn);
   const size_t lds2 = pv_lds_bytes<D, KIND>(a.Tn);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL>),
@@ -894,7 +806,7 @@ hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pv<D, KIND, CAUSAL>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL>), dim3((unsigned)groups), dim3(kThreads * U), lds1, st, a);
+  hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds1, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_pv<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds2, st, a);
