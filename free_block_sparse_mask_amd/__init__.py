@@ -11,6 +11,8 @@ Entry points (names follow the C ABI in include/sparge.h):
   quant_qk_int8(q, k)                           -> (q8, k8, q_scale, k_scale)
   hilbert_index(T, H, W)                        -> (perm, inv) as numpy int32 (host)
   hilbert_permute(x, perm, inverse)             -> y
+  grid_order(T, H, W, order)                    -> (perm, inv): Hilbert, raster or time-fastest
+  l1_sums(o, ref) / l1_error(o, ref)            -> relative L1 of O' against O
   sparge_attention(q, k, v, tau, theta, lam, causal, ...) -> the whole path
 """
 from __future__ import annotations
@@ -31,6 +33,7 @@ SPARGE_EUNSUPPORTED = -2
 SPARGE_EWORKSPACE = -3
 SPARGE_EHIP = -4
 F16, BF16, I8, F32 = 0, 1, 2, 3
+ORDER_HILBERT, ORDER_ROWMAJOR, ORDER_TIMEMAJOR = 0, 1, 2
 BQ, BK = 128, 64
 COUNTER_NAMES = ("live_tiles", "qk_exec", "qk_skip", "pv_exec", "pv_skip", "pv_void",
                  "empty_rows", "rows")
@@ -65,6 +68,10 @@ _SIGNATURES = {
     "sparge_attn": (ctypes.c_int, [_vp, _TP, _vp, _TP, _vp, _TP, _vp, _TP, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int,
                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "sparge_grid_order": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
+    "sparge_l1_workspace_size": (ctypes.c_size_t, []),
+    "sparge_l1_sums": (ctypes.c_int, [_vp, _TP, ctypes.c_int, _vp, _TP, ctypes.c_int, _vp, _vp,
+                                      ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -244,6 +251,43 @@ def hilbert_permute(x, perm, inverse: bool = False, out=None):
                                       _dtype_code(x), _ptr(perm), int(bool(inverse)), _stream(x.device))
     _check("sparge_hilbert_permute", rc)
     return y
+
+
+def grid_order(T: int, H: int, W: int, order: int):
+    """Host-side token order of a T x H x W grid (sparge_grid_order):
+    ORDER_HILBERT, ORDER_ROWMAJOR or ORDER_TIMEMAJOR; (perm, inv) int32 numpy."""
+    n = T * H * W
+    perm = np.empty(n, dtype=np.int32)
+    inv = np.empty(n, dtype=np.int32)
+    rc = lib().sparge_grid_order(T, H, W, order, perm.ctypes.data, inv.ctypes.data)
+    _check("sparge_grid_order", rc)
+    return perm, inv
+
+
+def l1_sums(o, ref, out=None):
+    """Device float64 [sum|o - ref|, sum|ref|] (sparge_l1_sums), same bits on every call."""
+    import torch
+    dev = o.device
+    out = torch.empty(2, dtype=torch.float64, device=dev) if out is None else out
+    need = lib().sparge_l1_workspace_size()
+    ws = _l1_ws.get(dev)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        _l1_ws[dev] = ws
+    rc = lib().sparge_l1_sums(_ptr(o), ctypes.byref(desc(o)), _dtype_code(o), _ptr(ref),
+                              ctypes.byref(desc(ref)), _dtype_code(ref), _ptr(out), _ptr(ws),
+                              ws.numel(), _stream(dev))
+    _check("sparge_l1_sums", rc)
+    return out
+
+
+_l1_ws = {}
+
+
+def l1_error(o, ref) -> float:
+    """Relative L1 error sum|o - ref| / sum|ref| (0 when ref is all zero)."""
+    s = l1_sums(o, ref).cpu().tolist()
+    return s[0] / s[1] if s[1] > 0 else 0.0
 
 
 def counts_dict(counts) -> dict:

@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparge.so")
-SOURCES = ["api.cpp", "hilbert.cpp", "k_attn.hip", "k_predict.hip", "k_quant.hip", "k_permute.hip"]
+SOURCES = ["api.cpp", "hilbert.cpp", "k_attn.hip", "k_predict.hip", "k_quant.hip", "k_permute.hip",
+           "k_reduce.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept out of every kernel: the compiler is told the

@@ -135,6 +135,59 @@ int sparge_hilbert_index(int T, int H, int W, int32_t* perm, int32_t* inv) {
   return ok();
 }
 
+int sparge_grid_order(int T, int H, int W, int order, int32_t* perm, int32_t* inv) {
+  if (T <= 0 || H <= 0 || W <= 0) return fail(SPARGE_EINVAL, "grid sizes must be positive");
+  if (perm == nullptr || inv == nullptr) return fail(SPARGE_EINVAL, "null output");
+  if (order != SPARGE_ORDER_HILBERT && order != SPARGE_ORDER_ROWMAJOR && order != SPARGE_ORDER_TIMEMAJOR)
+    return fail(SPARGE_EINVAL, "unknown order %d", order);
+  if ((int64_t)T * H * W >= (1LL << 31)) return fail(SPARGE_EUNSUPPORTED, "grid too large");
+  if (order == SPARGE_ORDER_HILBERT) return sparge_hilbert_index(T, H, W, perm, inv);
+  simple_order(T, H, W, order, perm, inv);
+  return ok();
+}
+
+size_t sparge_l1_workspace_size(void) { return (size_t)16 * kL1Blocks + 256; }
+
+int sparge_l1_sums(const void* o, const sparge_tensor* os, int dtype_o, const void* ref,
+                   const sparge_tensor* rs, int dtype_ref, double* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const int eo = dtype_o == SPARGE_I8 ? 0 : elem_size(dtype_o);
+  const int er = dtype_ref == SPARGE_I8 ? 0 : elem_size(dtype_ref);
+  if (eo == 0 || er == 0) return fail(SPARGE_EINVAL, "dtypes must be F16, BF16 or F32");
+  int r = check_tensor("o", os, eo);
+  if (r) return r;
+  r = check_tensor("ref", rs, er);
+  if (r) return r;
+  if (os->B != rs->B || os->H != rs->H || os->N != rs->N || os->d != rs->d)
+    return fail(SPARGE_EINVAL, "o and ref differ in shape");
+  if (out == nullptr) return fail(SPARGE_EINVAL, "null output");
+  if (workspace == nullptr || workspace_bytes < sparge_l1_workspace_size())
+    return fail(SPARGE_EWORKSPACE, "workspace needs %zu bytes", sparge_l1_workspace_size());
+  const bool empty = empty_problem(os);
+  if (!empty && (o == nullptr || ref == nullptr)) return fail(SPARGE_EINVAL, "null pointer");
+  if (!empty && (!aligned16(o) || !aligned16(ref))) return fail(SPARGE_EINVAL, "o and ref must be 16-byte aligned");
+  L1Args a{};
+  a.o = o;
+  a.r = ref;
+  a.o_sb = os->sb;
+  a.o_sh = os->sh;
+  a.o_sn = os->sn;
+  a.r_sb = rs->sb;
+  a.r_sh = rs->sh;
+  a.r_sn = rs->sn;
+  a.B = empty ? 0 : os->B;   // an empty tensor still writes (0, 0)
+  a.H = os->H;
+  a.N = os->N;
+  a.d = os->d;
+  a.dtype_o = dtype_o;
+  a.dtype_r = dtype_ref;
+  a.partial = reinterpret_cast<double*>(align256((size_t)workspace));
+  a.out = out;
+  const hipError_t e = launch_l1(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "l1 launch");
+  return ok();
+}
+
 int sparge_hilbert_permute(const void* x, const sparge_tensor* xs, void* y, const sparge_tensor* ys,
                            int dtype, const int32_t* perm, int inverse, void* stream) {
   const int es = elem_size(dtype);

@@ -11,7 +11,8 @@
 // top bit down, Gray-encoding across axes, and a final correction; the index
 // is the transposed bits read level by level (axis 0 = t most significant).
 // Points of a T x H x W grid are indexed on the enclosing 2^b cube and sorted
-// by index (indices are distinct, so the order is unique).
+// by index (indices are distinct, so the order is unique).  The raster and
+// time-fastest orders it is compared with are generated here too.
 #include <algorithm>
 #include <cstdint>
 #include <numeric>
@@ -71,6 +72,22 @@ int hilbert_order(int T, int H, int W, int32_t* perm, int32_t* inv) {
     inv[order[(size_t)p]] = (int32_t)p;
   }
   return 0;
+}
+
+// Raster and time-fastest orders of the permutation comparison ([Review]
+// Table 4).  Raster index of (t, h, w) is (t H + h) W + w.
+void simple_order(int T, int H, int W, int order, int32_t* perm, int32_t* inv) {
+  int64_t p = 0;
+  if (order == SPARGE_ORDER_ROWMAJOR) {
+    for (int t = 0; t < T; ++t)
+      for (int h = 0; h < H; ++h)
+        for (int w = 0; w < W; ++w, ++p) perm[p] = (int32_t)(((int64_t)t * H + h) * W + w);
+  } else {
+    for (int h = 0; h < H; ++h)
+      for (int w = 0; w < W; ++w)
+        for (int t = 0; t < T; ++t, ++p) perm[p] = (int32_t)(((int64_t)t * H + h) * W + w);
+  }
+  for (int64_t q = 0; q < p; ++q) inv[perm[q]] = (int32_t)q;
 }
 
 }  // namespace sparge

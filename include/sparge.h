@@ -192,6 +192,44 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
                 double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/*
+ * Token orders of a T x H x W grid of visual tokens (host), the alternatives
+ * the permutation comparison of [Review] (Table 4: random, row-major,
+ * time-major, HilbertCurve) sets against each other.  Grid token (t, h, w)
+ * has raster index (t H + h) W + w.  perm[p] is the raster index of the
+ * token at position p; inv is its inverse.  Both are host int32[T H W]
+ * owned by the caller.
+ *   SPARGE_ORDER_HILBERT:   as sparge_hilbert_index.
+ *   SPARGE_ORDER_ROWMAJOR:  raster order, w fastest, then h, then t (the
+ *                           identity).
+ *   SPARGE_ORDER_TIMEMAJOR: t fastest, then w, then h: the frames of one
+ *                           pixel are adjacent.
+ * A random order is the caller's (any permutation works with
+ * sparge_hilbert_permute).  Errors: SPARGE_EINVAL for non-positive sizes, an
+ * unknown order or null outputs; SPARGE_EUNSUPPORTED past 2^31 tokens.
+ */
+#define SPARGE_ORDER_HILBERT 0
+#define SPARGE_ORDER_ROWMAJOR 1
+#define SPARGE_ORDER_TIMEMAJOR 2
+int sparge_grid_order(int T, int H, int W, int order, int32_t* perm, int32_t* inv);
+
+/*
+ * The two sums of the relative L1 error that bounds the hyper-parameter
+ * search of [Review] ("hyper-parameter determination": L1 = sum|O - O'| /
+ * sum|O|, O the full-attention output, O' the sparse one):
+ * out[0] = sum |o - ref|, out[1] = sum |ref|, over every element.
+ * o, ref: [B,H,N,d] of the same sizes, element types dtype_o / dtype_ref
+ *   (SPARGE_F16, SPARGE_BF16 or SPARGE_F32), d contiguous.
+ * out: device double[2], overwritten.  The sums are taken in float64 in a
+ *   fixed order: the same inputs give the same bits on every call.
+ * workspace: device scratch of at least sparge_l1_workspace_size() bytes.
+ * An empty tensor gives (0, 0).
+ */
+size_t sparge_l1_workspace_size(void);
+int sparge_l1_sums(const void* o, const sparge_tensor* os, int dtype_o, const void* ref,
+                   const sparge_tensor* rs, int dtype_ref, double* out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -548,6 +548,32 @@ def hilbert_permutation(T: int, Hg: int, Wg: int) -> Tuple[np.ndarray, np.ndarra
     return perm, inv
 
 
+def raster_order(T: int, Hg: int, Wg: int) -> np.ndarray:
+    """Row-major order of the permutation comparison ([Review] Table 4):
+    tokens in (t, h, w) order with w fastest, i.e. the raster index itself."""
+    return np.arange(T * Hg * Wg, dtype=np.int32)
+
+
+def time_major_order(T: int, Hg: int, Wg: int) -> np.ndarray:
+    """Time-major order ([Review] Table 4, read as: the frames of one pixel
+    adjacent): position p = ((h * Wg) + w) * T + t holds raster token
+    (t * Hg + h) * Wg + w."""
+    perm = np.empty(T * Hg * Wg, dtype=np.int32)
+    p = 0
+    for h in range(Hg):
+        for w in range(Wg):
+            for t in range(T):
+                perm[p] = (t * Hg + h) * Wg + w
+                p += 1
+    return perm
+
+
+def block_self_similarity(X: np.ndarray, b: int) -> float:
+    """Sim-q / Sim-k of [Review] Table 4: the mean CosSim (eq. 6) over the
+    b-token blocks of X [N, d] (the last block may be ragged)."""
+    return float(np.mean(block_cossim(X, b)))
+
+
 def permute_tokens(X: np.ndarray, perm: np.ndarray) -> np.ndarray:
     """X' [..., p, :] = X[..., perm[p], :] (gather along the token axis)."""
     return X[..., perm, :]

@@ -167,3 +167,35 @@ def test_hilbert_index_rejects_bad_grids():
     assert L.sparge_hilbert_index(2, 2, 2, None, buf.ctypes.data) == fb.SPARGE_EINVAL
     assert L.sparge_hilbert_index(1 << 11, 1 << 11, 1 << 10, buf.ctypes.data,
                                   buf.ctypes.data) == fb.SPARGE_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("grid", [(12, 48, 80), (1, 6, 6), (3, 5, 7), (2, 64, 1), (5, 1, 1)])
+def test_grid_orders_match_oracle(grid):
+    T, Hg, Wg = grid
+    refs = {fb.ORDER_HILBERT: O.hilbert_permutation(T, Hg, Wg)[0],
+            fb.ORDER_ROWMAJOR: O.raster_order(T, Hg, Wg),
+            fb.ORDER_TIMEMAJOR: O.time_major_order(T, Hg, Wg)}
+    for order, ref in refs.items():
+        perm, inv = fb.grid_order(T, Hg, Wg, order)
+        assert np.array_equal(perm, ref), order
+        assert np.array_equal(inv[perm], np.arange(perm.size)), order
+
+
+def test_grid_order_and_l1_reject_bad_arguments():
+    L = fb.lib()
+    buf = np.zeros(8, dtype=np.int32)
+    assert L.sparge_grid_order(2, 2, 2, 3, buf.ctypes.data, buf.ctypes.data) == fb.SPARGE_EINVAL
+    assert L.sparge_grid_order(2, 0, 2, 1, buf.ctypes.data, buf.ctypes.data) == fb.SPARGE_EINVAL
+    assert L.sparge_grid_order(2, 2, 2, 1, None, buf.ctypes.data) == fb.SPARGE_EINVAL
+    x = _t(1, 2, 10, 64)
+    FAKE = ctypes.c_void_p(1 << 20)
+    ws = L.sparge_l1_workspace_size()
+    assert ws >= 16 * 1024
+    assert L.sparge_l1_sums(FAKE, ctypes.byref(x), fb.I8, FAKE, ctypes.byref(x), fb.F16, FAKE, FAKE, ws,
+                            None) == fb.SPARGE_EINVAL
+    assert L.sparge_l1_sums(FAKE, ctypes.byref(x), fb.F16, FAKE, ctypes.byref(_t(1, 2, 11, 64)), fb.F16, FAKE,
+                            FAKE, ws, None) == fb.SPARGE_EINVAL
+    assert L.sparge_l1_sums(FAKE, ctypes.byref(x), fb.F16, FAKE, ctypes.byref(x), fb.F16, None, FAKE, ws,
+                            None) == fb.SPARGE_EINVAL
+    assert L.sparge_l1_sums(FAKE, ctypes.byref(x), fb.F16, FAKE, ctypes.byref(x), fb.F16, FAKE, FAKE, ws - 1,
+                            None) == fb.SPARGE_EWORKSPACE

@@ -467,3 +467,34 @@ def test_gqa_grouping_is_contiguous():
     pa = O.predict_mask(Q, K, 0.7, 0.0, True)
     pb = O.predict_mask(Q, Krep, 0.7, 0.0, True)
     assert np.array_equal(pa["mg"], pb["mg"])
+
+
+# ---------------------------------------------------------------------------
+# token orders and block self-similarity of the permutation comparison
+# ([Review] Table 4)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("grid", [(1, 4, 6), (5, 1, 1), (3, 4, 5), (12, 6, 10)])
+def test_time_major_order_closed_form(grid):
+    T, Hg, Wg = grid
+    perm = O.time_major_order(T, Hg, Wg)
+    assert np.array_equal(np.sort(perm), np.arange(T * Hg * Wg))
+    p = np.arange(perm.size)
+    # run r = p // T is pixel (h, w) = divmod(r, Wg); inside it t = p % T
+    t, pix = perm // (Hg * Wg), perm % (Hg * Wg)
+    assert np.array_equal(t, p % T)
+    assert np.array_equal(pix, p // T)
+    if T == 1 or Hg * Wg == 1:
+        assert np.array_equal(perm, O.raster_order(T, Hg, Wg))
+
+
+def test_block_self_similarity_closed_forms():
+    d, b = 16, 8
+    same = np.tile(np.arange(1.0, d + 1.0), (2 * b, 1))
+    assert abs(O.block_self_similarity(same, b) - 1.0) < 1e-15
+    ortho = np.vstack([np.eye(d)[:b], np.eye(d)[:b]])
+    # each block: cosine matrix = identity, mean 1/b
+    assert abs(O.block_self_similarity(ortho, b) - 1.0 / b) < 1e-15
+    # a ragged last block of 3 identical tokens averages in as 1
+    X = np.vstack([np.eye(d)[:b], np.ones((3, d))])
+    assert abs(O.block_self_similarity(X, b) - 0.5 * (1.0 / b + 1.0)) < 1e-15
