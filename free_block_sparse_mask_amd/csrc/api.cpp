@@ -7,7 +7,7 @@
 #include <cstring>
 #include <string>
 
-#include "common.hpp"
+#include "support.hpp"
 
 namespace sparge {
 

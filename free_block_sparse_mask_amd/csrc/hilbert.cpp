@@ -18,7 +18,7 @@
 #include <numeric>
 #include <vector>
 
-#include "common.hpp"
+#include "support.hpp"
 
 namespace sparge {
 

@@ -10,7 +10,7 @@
 // l1_final sums the kL1Blocks partials in a fixed order.  The inputs are
 // read once (HBM-bound; the search calls it a few dozen times on
 // calibration-sized tensors).
-#include "common.hpp"
+#include "support.hpp"
 
 namespace sparge {
 
