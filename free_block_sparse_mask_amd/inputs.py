@@ -211,6 +211,13 @@ def draw_v(w: Workload, b: int, h: int) -> np.ndarray:
     return _rng(w.wid, TENSOR_V, b, h).standard_normal((w.N, w.d))
 
 
+def random_order(n: int, seed: int = 0) -> np.ndarray:
+    """A seeded random token order (int32 permutation of n), the "random"
+    entry of the permutation comparison; both sides take it as an input."""
+    rng = np.random.Generator(np.random.Philox(np.random.SeedSequence([BASE_SEED, 1000, seed])))
+    return rng.permutation(n).astype(np.int32)
+
+
 def make_tensor(w: Workload, tensor: int, dtype: Optional[str] = None, heads: Optional[int] = None,
                 workers: int = 8) -> np.ndarray:
     """Returns uint16 bits [B, heads, N, d] of Q (tensor 0), K (1) or V (2)."""
