@@ -413,7 +413,11 @@ void attn_stats(AttnArgs p) {
 
   // tile(e): entry e's scores and softmax for this wavefront (the tile has
   // landed in slot SL and the workgroup has passed the barrier that covers it)
-  auto tile = [&](int e, auto slot_c) {
+  // The refill of the other slot is issued after this tile's first operand
+  // reads, so its address arithmetic runs in the shadow of the MFMAs instead
+  // of delaying them.
+  constexpr int KLA = 2;      // k-steps the operand reads run ahead of the MFMAs
+  auto tile = [&](int e, auto slot_c, auto&& refill) {
     constexpr int SL = decltype(slot_c)::value;
     const int j = __builtin_amdgcn_readfirstlane((int)lst[e]);
     float c_scale = p.scale_log2;
@@ -424,17 +428,18 @@ void attn_stats(AttnArgs p) {
     const unsigned char* kt = ring + SL * G::K_BYTES;
     u32x4 kf[G::QS][2];
 #pragma unroll
-    for (int s = 0; s < G::QS; ++s)
+    for (int s = 0; s < G::QS; ++s) {
+      if (s == 1) refill();
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         kf[s][t] = *reinterpret_cast<const u32x4*>(kt + t * 32 * G::KROW + (L.k_rd ^ (32u * s)));
+    }
     Acc acc[2] = {Acc{}, Acc{}};
 #pragma unroll
     for (int s = 0; s < G::QS; ++s)
 #pragma unroll
       for (int t = 0; t < 2; ++t) acc[t] = mfma_qk<KIND>(kf[s][t], L.qf[s], acc[t]);
     // issue order: the reads run KLA k-steps ahead of the MFMAs that use them
-    constexpr int KLA = 2;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * KLA, 0);
 #pragma unroll
     for (int s = 0; s < G::QS - KLA; ++s) {
@@ -516,24 +521,22 @@ void attn_stats(AttnArgs p) {
     L.issue_k(p, __builtin_amdgcn_readfirstlane((int)lst[0]), ring_lds);
     jd_v = lst[min(1, UC - 1)];
   }
-  auto sync1 = [&](int e, auto slot_c) {
+  // step(e): the barrier, then tile e, which refills the other slot with e+1
+  auto step = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
     wait_barrier<0>();
-    const int j1 = __builtin_amdgcn_readfirstlane(jd_v);
-    if (e + 1 < UC) L.issue_k(p, j1, ring_lds + (uint32_t)((1 - SL) * G::K_BYTES));
-    jd_v = lst[min(e + 2, UC - 1)];
+    tile(e, slot_c, [&]() {
+      const int j1 = __builtin_amdgcn_readfirstlane(jd_v);
+      if (e + 1 < UC) L.issue_k(p, j1, ring_lds + (uint32_t)((1 - SL) * G::K_BYTES));
+      jd_v = lst[min(e + 2, UC - 1)];
+    });
   };
   int e = 0;
   for (; e + 2 <= UC; e += 2) {
-    sync1(e, I0{});
-    tile(e, I0{});
-    sync1(e + 1, I1{});
-    tile(e + 1, I1{});
+    step(e, I0{});
+    step(e + 1, I1{});
   }
-  if (e < UC) {
-    sync1(e, I0{});
-    tile(e, I0{});
-  }
+  if (e < UC) step(e, I0{});
   wait_barrier<0>();                       // every vote word is written
 
   // ---- the block's executed-tile list (listed tiles with a voting wavefront) ----
