@@ -17,9 +17,9 @@
 //                 tiles staged through LDS (tiles wholly in the causal future
 //                 are skipped).
 //   mask_rows     one workgroup per query block row: softmax over the live
-//                 selective columns, a bitonic sort in LDS by (P desc, j asc),
-//                 a workgroup prefix scan for TopCdf, eq. 9 forcing, then the
-//                 M_g row and its compacted ascending list.
+//                 selective columns, the TopCdf cut by a radix select over
+//                 the probabilities with fixed-point sums (no sort), eq. 9
+//                 forcing, then the M_g row and its compacted ascending list.
 #include "common.hpp"
 
 namespace sparge {
@@ -88,6 +88,19 @@ __device__ double block_reduce_sum(double v, double* lds) {
     __syncthreads();
   }
   const double r = lds[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ uint64_t block_reduce_u64(uint64_t v, unsigned long long* lds) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) lds[tid] += lds[tid + off];
+    __syncthreads();
+  }
+  const uint64_t r = lds[0];
   __syncthreads();
   return r;
 }
@@ -272,14 +285,19 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
 // ---------------------------------------------------------------------------
 // mask_rows: eqs. (7)-(9) for one query block row, then its compacted list
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int npad_max) {
+__global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int cap) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  double* pv = reinterpret_cast<double*>(dyn);                        // [npad_max]
-  int* pj = reinterpret_cast<int*>(dyn + 8 * (size_t)npad_max);         // [npad_max]
-  uint8_t* flag = dyn + 12 * (size_t)npad_max;                        // [Tn]: bit0 fix_k, bit1 kept
+  double* pv = reinterpret_cast<double*>(dyn);                        // [cap >= Tn]
+  int* pj = reinterpret_cast<int*>(dyn + 8 * (size_t)cap);              // [cap]
+  uint8_t* flag = dyn + 12 * (size_t)cap;                             // [Tn]: bit0 fix_k, bit1 kept
   __shared__ double dred[kThreads];
   __shared__ int ired[kThreads];
-  __shared__ int cut;
+  __shared__ unsigned long long ured[kThreads];
+  __shared__ unsigned int hcnt[256];
+  __shared__ unsigned long long hsum[256];
+  __shared__ int s_digit;
+  __shared__ uint64_t s_above;
+  static_assert(kThreads == 256, "one histogram bin per thread");
 
   const long long row = blockIdx.x;               // (b*H + h)*Tm + i
   const int i = (int)(row % a.Tm);
@@ -311,8 +329,6 @@ __global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int npad_ma
       }
     __syncthreads();
     if (m > 0) {
-      int npad = 1;
-      while (npad < m) npad <<= 1;
       // softmax over the m finite entries (eq. 8's P^[i])
       double mx = kNegInfD;
       for (int r = tid; r < m; r += kThreads) mx = fmax(mx, pv[r]);
@@ -324,58 +340,89 @@ __global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int npad_ma
         se += e;
       }
       se = block_reduce_sum(se, dred);
-      for (int r = tid; r < npad; r += kThreads) {
-        if (r < m) {
-          pv[r] = pv[r] / se;
-        } else {
-          pv[r] = -1.0;                         // padding sorts after every probability
-          pj[r] = 0x7fffffff;
-        }
-      }
-      __syncthreads();
-      // bitonic sort into the order (P descending, j ascending)
-      for (int k = 2; k <= npad; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-          for (int x = tid; x < npad; x += kThreads) {
-            const int y = x ^ jj;
-            if (y > x) {
-              const double px = pv[x], py = pv[y];
-              const int jx = pj[x], jy = pj[y];
-              const bool y_first = py > px || (py == px && jy < jx);
-              const bool x_first = px > py || (px == py && jx < jy);
-              const bool swap = ((x & k) == 0) ? y_first : x_first;
-              if (swap) {
-                pv[x] = py;
-                pv[y] = px;
-                pj[x] = jy;
-                pj[y] = jx;
-              }
-            }
-          }
-          __syncthreads();
-        }
-      }
-      // TopCdf: keep sorted position r iff its exclusive prefix < tau * sum
+      // ---- TopCdf (eq. 8) without a sort.  In the order (P desc, j asc) the
+      // kept entries are the prefix up to and including the first entry whose
+      // inclusive cumulative sum reaches tau * sum.  A radix select over the
+      // probabilities' bit patterns (positive doubles order like their bits)
+      // finds that entry's value 8 bits per pass; entries of equal value are
+      // then kept in ascending j.  Sums are taken in 2^-62 fixed point, so they
+      // are exact integers, independent of the order of the atomic adds.
+      constexpr int MAXE = SPARGE_MAX_TN / kThreads;
       const int per2 = (m + kThreads - 1) / kThreads;
-      const int lo2 = min(m, tid * per2), hi2 = min(m, lo2 + per2);
-      double part = 0.0;
-      for (int r = lo2; r < hi2; ++r) part += pv[r];
-      double total;
-      const double base = block_excl_scan_double(part, dred, total);
-      const double thresh = a.tau * total;
-      if (tid == 0) cut = m;
-      __syncthreads();
-      double run = base;
-      for (int r = lo2; r < hi2; ++r) {
-        if (run >= thresh) {
-          atomicMin(&cut, r);
-          break;
-        }
-        run += pv[r];
+      const int lo2 = min(m, tid * per2);
+      const int n2 = min(m, lo2 + per2) - lo2;
+      uint64_t key[MAXE], fx[MAXE];
+      uint64_t fsum = 0;
+#pragma unroll
+      for (int x = 0; x < MAXE; ++x) {
+        const double pr = x < n2 ? pv[lo2 + x] / se : 0.0;
+        key[x] = (uint64_t)__double_as_longlong(pr);
+        fx[x] = (uint64_t)(pr * 0x1p62);
+        fsum += fx[x];
       }
-      __syncthreads();
-      const int kept = cut;
-      for (int r = tid; r < kept; r += kThreads) flag[pj[r]] |= 2;
+      const uint64_t F = block_reduce_u64(fsum, ured);
+      // kept iff exclusive prefix < tau * F; at least the first entry
+      const uint64_t TF = max((uint64_t)1, (uint64_t)(a.tau * (double)F));
+      uint64_t prefix = 0, above = 0;
+      for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        hcnt[tid] = 0u;
+        hsum[tid] = 0ull;
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < MAXE; ++x)
+          if (x < n2 && ((key[x] >> shift) >> 8) == prefix) {     // in the selected range
+            const int d = (int)((key[x] >> shift) & 255u);
+            atomicAdd(&hcnt[d], 1u);
+            atomicAdd(&hsum[d], (unsigned long long)fx[x]);
+          }
+        __syncthreads();
+        if (tid < 64) {
+          // lane l scans bins 255-4l .. 252-4l: the crossing bin is the first,
+          // in descending digit order, where above + (sum before it) < TF <=
+          // above + (sum through it)
+          uint64_t sb[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sb[q] = hsum[255 - 4 * tid - q];
+          const uint64_t mine = sb[0] + sb[1] + sb[2] + sb[3];
+          uint64_t incl = mine;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const uint64_t t = __shfl_up(incl, off, 64);
+            if (tid >= off) incl += t;
+          }
+          uint64_t cum = above + (incl - mine);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (cum < TF && TF <= cum + sb[q]) {
+              s_digit = 255 - 4 * tid - q;
+              s_above = cum;
+            }
+            cum += sb[q];
+          }
+        }
+        __syncthreads();
+        prefix = (prefix << 8) | (uint64_t)s_digit;
+        above = s_above;
+      }
+      // prefix is now the value v of the boundary entry and above the sum of
+      // the entries greater than v; among the entries equal to v, the one of
+      // rank t (ascending j) is kept iff above + t * f(v) < TF
+      int my_ties = 0;
+#pragma unroll
+      for (int x = 0; x < MAXE; ++x) my_ties += (x < n2 && key[x] == prefix) ? 1 : 0;
+      int n_ties;
+      int rank = block_excl_scan_int(my_ties, ired, n_ties);
+      const uint64_t fv = (uint64_t)(__longlong_as_double((long long)prefix) * 0x1p62);
+      const uint64_t room = TF - above;             // >= 1
+      const long long tie_keep = fv == 0 ? n_ties : (long long)min((uint64_t)n_ties, (room + fv - 1) / fv);
+#pragma unroll
+      for (int x = 0; x < MAXE; ++x) {
+        if (x >= n2) continue;
+        bool keep = key[x] > prefix;
+        if (key[x] == prefix) keep = rank++ < tie_keep;
+        if (keep) flag[pj[lo2 + x]] |= 2;
+      }
       __syncthreads();
     }
   }
@@ -421,11 +468,9 @@ hipError_t launch_predict(const PredictArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(shat_gemm, g, dim3(kThreads), 0, st, a, 1.0 / sqrt((double)a.d));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int npad = 1;
-  while (npad < a.Tn) npad <<= 1;
-  const size_t lds = 12 * (size_t)npad + (size_t)a.Tn;
+  const size_t lds = 13 * (size_t)a.Tn;
   hipLaunchKernelGGL(mask_rows, dim3((unsigned)((long long)a.B * a.H * a.Tm)), dim3(kThreads), lds, st,
-                     a, npad);
+                     a, a.Tn);
   return hipGetLastError();
 }
 
