@@ -28,6 +28,16 @@ namespace {
 
 constexpr double kNegInfD = -__builtin_huge_val();
 
+// 1/sqrt(x) for x > 0 in float64: the hardware estimate refined by two
+// Newton steps y <- y (3 - x y^2) / 2, each of which squares the relative
+// error, so the result is within a few ulp of the rounded reciprocal root.
+__device__ __forceinline__ double rsqrt_f64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * fma(-0.5 * x, y * y, 1.5);
+  y = y * fma(-0.5 * x, y * y, 1.5);
+  return y;
+}
+
 __device__ __forceinline__ double bits_to_double(unsigned short u, bool bf16) {
   if (bf16) return (double)__uint_as_float((unsigned int)u << 16);
   return (double)(float)__builtin_bit_cast(_Float16, u);
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
     for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
 #pragma unroll
     for (int off = 1; off < DCH; off <<= 1) ss += __shfl_xor(ss, off, 64);
-    const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+    const double inv = ss > 0.0 ? rsqrt_f64(ss) : 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sx[e] += x[e];
@@ -226,8 +236,10 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
 constexpr int kGT = 64;     // tile rows / cols
 constexpr int kGK = 16;     // d chunk
 __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_sqrt_d) {
-  __shared__ double qt[kGK][kGT + 1];
-  __shared__ double kt[kGK][kGT + 1];
+  // rows padded by 2 doubles: 16-byte aligned for the operand reads, and the
+  // transposing stores of 16 consecutive k land in distinct banks
+  __shared__ __attribute__((aligned(16))) double qt[kGK][kGT + 2];
+  __shared__ __attribute__((aligned(16))) double kt[kGK][kGT + 2];
   const int it = blockIdx.x, jt = blockIdx.y;
   const int bh = blockIdx.z;
   const int b = bh / a.H, h = bh % a.H;
@@ -241,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
   const double* qb = a.ws.qbar + ((long long)b * a.H + h) * a.Tm * a.d;
   const double* kb = a.ws.kbar + ((long long)b * a.Hkv + hk) * a.Tn * a.d;
   const int tid = threadIdx.x;
-  const int ti = tid / 16, tj = tid % 16;      // 4 x 4 outputs each
+  const int ti = tid / 16, tj = tid % 16;      // rows 4 ti .. 4 ti + 3, columns 4 tj .. 4 tj + 3
   double acc[4][4];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
@@ -257,11 +269,13 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kGK; ++kk) {
-      double qv[4], kv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) qv[x] = qt[kk][ti + 16 * x];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) kv[y] = kt[kk][tj + 16 * y];
+      // four contiguous rows and four contiguous columns: two 16-byte reads each
+      const double2 q01 = *reinterpret_cast<const double2*>(&qt[kk][4 * ti]);
+      const double2 q23 = *reinterpret_cast<const double2*>(&qt[kk][4 * ti + 2]);
+      const double2 k01 = *reinterpret_cast<const double2*>(&kt[kk][4 * tj]);
+      const double2 k23 = *reinterpret_cast<const double2*>(&kt[kk][4 * tj + 2]);
+      const double qv[4] = {q01.x, q01.y, q23.x, q23.y};
+      const double kv[4] = {k01.x, k01.y, k23.x, k23.y};
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -272,11 +286,11 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
   double* out = a.ws.shat + ((long long)b * a.H + h) * a.Tm * a.Tn;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const int gi = i0 + ti + 16 * x;
+    const int gi = i0 + 4 * ti + x;
     if (gi >= a.Tm) continue;
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
-      const int gj = j0 + tj + 16 * y;
+      const int gj = j0 + 4 * tj + y;
       if (gj < a.Tn) out[(long long)gi * a.Tn + gj] = acc[x][y] * inv_sqrt_d;
     }
   }
