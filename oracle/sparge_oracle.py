@@ -439,6 +439,123 @@ def masked_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray
 
 
 # ---------------------------------------------------------------------------
+# fp8 P~V ([Review] Fig. 9, "SpargeAttn + Sage2": P~V on 8-bit floats)
+# ---------------------------------------------------------------------------
+# Readings (the pages name the variant only): OCP E4M3 (4 exponent bits, bias
+# 7, 3 mantissa bits, largest finite 448), round to nearest even; V scaled per
+# channel by the power of two delta_c = 2^e, e the least integer with
+# max_n |V[n, c]| <= 448 * 2^e (1 for an all-zero channel), so V / delta_c is
+# exact before its one rounding; P~ taken at the final row max (the two-pass
+# order) and scaled by 2^8 before its rounding; products summed exactly;
+# O = delta_c * sum / 2^8 / l with l the exact row sum.
+
+E4M3_MAX = 448.0
+PV8_P_SCALE = 256.0
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 value (ties to the even mantissa), saturating at +-448.
+    Normal numbers (|x| >= 2^-6) keep 3 fraction bits; below, the step is 2^-9."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    q = 2.0 ** (e - 3)                                # spacing of the binade (2^-9 when subnormal)
+    r = np.rint(a / q) * q                            # np.rint: ties to even
+    r = np.minimum(r, E4M3_MAX)
+    return np.sign(x) * r
+
+
+def v_channel_scales(Vh: np.ndarray) -> np.ndarray:
+    """delta_c = 2^e with e the least integer such that max|V[:, c]| <= 448 * 2^e."""
+    mx = np.abs(Vh).max(axis=0)
+    e = np.zeros_like(mx)
+    nz = mx > 0
+    e[nz] = np.ceil(np.log2(mx[nz] / E4M3_MAX))
+    # exact comparisons settle a log2 that lands next to an integer
+    e = np.where(nz & (mx > E4M3_MAX * 2.0 ** e), e + 1, e)
+    e = np.where(nz & (mx <= E4M3_MAX * 2.0 ** (e - 1)), e - 1, e)
+    return np.where(nz, 2.0 ** e, 1.0)
+
+
+def attend_row_block_fp8pv(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.ndarray, i: int,
+                           lam: float, causal: bool, decisions: np.ndarray, bq: int = BQ, bk: int = BK,
+                           R: int = ROWS_PER_GROUP, score_fn=None) -> np.ndarray:
+    """O_i of the fp8 P~V variant for one query block, given the (tile, group)
+    decisions of the lambda rule ([Tn, c_w], 1 = P~V runs): m_final and l are
+    eq. 1's final running max and row sum (exact); the voted groups add
+    e4m3(2^8 exp(S - m_final)) e4m3(V / delta) and O = delta sum / 2^8 / l."""
+    N, d = Qh.shape
+    Tn = num_blocks(N, bk)
+    rows = block_rows(N, bq, i)
+    n = len(rows)
+    q_idx = np.arange(rows.start, rows.stop)
+    Qi = Qh[rows.start:rows.stop]
+    live = tile_live(N, bq, bk, causal)[i]
+    todo = [j for j in range(Tn) if mg_row[j] and live[j]]
+    S_of = {}
+    m = np.full(n, NEG_INF)
+    for j in todo:
+        keys = block_rows(N, bk, j)
+        k_idx = np.arange(keys.start, keys.stop)
+        S = _scores_float(Qi, Kh[keys.start:keys.stop]) if score_fn is None else score_fn(rows, keys)
+        if causal:
+            S = np.where(k_idx[None, :] > q_idx[:, None], NEG_INF, S)
+        S_of[j] = S
+        m = np.maximum(m, S.max(axis=1))
+    m_sub = np.where(np.isfinite(m), m, 0.0)
+    l = np.zeros(n)
+    delta = v_channel_scales(Vh)
+    Vq = e4m3_round(Vh / delta[None, :])
+    acc = np.zeros((n, Vh.shape[1]))
+    for j in todo:
+        keys = block_rows(N, bk, j)
+        with np.errstate(invalid="ignore"):
+            P = np.exp(S_of[j] - m_sub[:, None])
+        l += P.sum(axis=1)
+        Pq = e4m3_round(PV8_P_SCALE * P)
+        for g in range(decisions.shape[1]):
+            if decisions[j, g] != 1:
+                continue
+            gi = np.arange(g * R, min(n, g * R + R))
+            acc[gi] += Pq[gi] @ Vq[keys.start:keys.stop]
+    out = np.zeros_like(acc)
+    nz = l > 0
+    out[nz] = acc[nz] * delta[None, :] / PV8_P_SCALE / l[nz, None]
+    return out
+
+
+def sparse_attention_fp8pv(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray, lam: float,
+                           causal: bool, blocks=None, skip_override: Optional[np.ndarray] = None,
+                           quant: Optional[dict] = None) -> np.ndarray:
+    """The fp8 P~V variant for Q [B, H, N, d], K/V [B, H_kv, N, d]: the lambda
+    decisions come from :func:`sparse_attention` (or ``skip_override``), the
+    output from :func:`attend_row_block_fp8pv`.  ``blocks`` restricts the work
+    to (b, h, i); other rows stay 0."""
+    B, H, N, d = Q.shape
+    H_kv = K.shape[1]
+    Tm = num_blocks(N, BQ)
+    _, _, dec = sparse_attention(Q, K, V, mg, lam, causal, blocks=blocks, skip_override=skip_override,
+                                 quant=quant)
+    O = np.zeros((B, H, N, V.shape[3]))
+    todo = blocks if blocks is not None else [(b, h, i) for b in range(B) for h in range(H) for i in range(Tm)]
+    for b, h, i in todo:
+        hk = kv_head(h, H, H_kv)
+        score_fn = None
+        if quant is not None:
+            qc, kc = quant["q_codes"][b, h], quant["k_codes"][b, hk]
+            dq, dk = quant["q_scale"][b, h], quant["k_scale"][b, hk]
+
+            def score_fn(rows, keys, qc=qc, kc=kc, dq=dq, dk=dk, i=i):
+                j = keys.start // BK
+                return (qc[rows.start:rows.stop] @ kc[keys.start:keys.stop].T) * (dq[i] * dk[j]) / math.sqrt(d)
+        r = block_rows(N, BQ, i)
+        O[b, h, r.start:r.stop] = attend_row_block_fp8pv(Q[b, h], K[b, hk], V[b, hk], mg[b, h, i], i, lam,
+                                                         causal, dec[b, h, i], score_fn=score_fn)
+    return O
+
+
+# ---------------------------------------------------------------------------
 # int8 per-block quantisation ([Review] Algorithm 1 step 2, components table)
 # ---------------------------------------------------------------------------
 

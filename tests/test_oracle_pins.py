@@ -498,3 +498,103 @@ def test_block_self_similarity_closed_forms():
     # a ragged last block of 3 identical tokens averages in as 1
     X = np.vstack([np.eye(d)[:b], np.ones((3, d))])
     assert abs(O.block_self_similarity(X, b) - 0.5 * (1.0 / b + 1.0)) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) rounding and the fp8 P~V variant
+# ---------------------------------------------------------------------------
+
+def _e4m3_from_bits(code):
+    """Value of an E4M3 code from its definition: sign, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN."""
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return None
+    return s * (m / 8.0 * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+
+
+def test_e4m3_round_fixes_every_finite_code_and_saturates():
+    vals = np.array([v for v in (_e4m3_from_bits(c) for c in range(256)) if v is not None])
+    assert vals.size == 254 and vals.max() == 448.0 and vals.min() == -448.0
+    assert np.array_equal(O.e4m3_round(vals), vals)
+    assert np.array_equal(O.e4m3_round(np.array([450.0, 463.9, 1e9, -1e9])), [448.0, 448.0, 448.0, -448.0])
+
+
+def test_e4m3_round_is_nearest_with_ties_to_even():
+    pos = np.unique(np.array([v for v in (_e4m3_from_bits(c) for c in range(128)) if v is not None]))
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = O.e4m3_round(mids)
+    # a midpoint goes to the neighbour whose mantissa is even
+    for lo, hi, g in zip(pos[:-1], pos[1:], got):
+        code_lo = [c for c in range(128) if _e4m3_from_bits(c) == lo][0]
+        assert g == (lo if code_lo % 2 == 0 else hi), (lo, hi, g)
+    rng = np.random.default_rng(3)
+    x = rng.uniform(-448, 448, 5000)
+    r = O.e4m3_round(x)
+    # nearest: no representable value is strictly closer
+    d = np.abs(x[:, None] - np.concatenate([pos, -pos])[None, :]).min(axis=1)
+    assert np.allclose(np.abs(x - r), d, rtol=0, atol=1e-12)
+    # closed form on [1, 2): steps of 1/8
+    y = rng.uniform(1, 2, 1000)
+    assert np.array_equal(O.e4m3_round(y), np.rint(8 * y) / 8)
+
+
+def test_v_channel_scales_are_the_least_power_of_two():
+    rng = np.random.default_rng(4)
+    V = rng.standard_normal((50, 8)) * (10.0 ** rng.uniform(-3, 4, 8))
+    V[:, 3] = 0.0
+    V[0, 5] = 448.0 * 4          # exactly at a power of two
+    V[:, 5] = np.clip(V[:, 5], -448.0 * 4, 448.0 * 4)
+    dl = O.v_channel_scales(V)
+    mx = np.abs(V).max(axis=0)
+    assert np.all(np.log2(dl) == np.round(np.log2(dl)))
+    assert dl[3] == 1.0 and dl[5] == 4.0
+    nz = mx > 0
+    assert np.all(mx[nz] <= 448.0 * dl[nz]) and np.all(mx[nz] > 224.0 * dl[nz])
+
+
+def test_fp8pv_equals_exact_attention_when_nothing_rounds():
+    """One-hot attention (each row sees one key far above the rest) and V on
+    the E4M3 grid: the fp8 variant's roundings change nothing."""
+    N, d = 128, 64
+    rng = np.random.default_rng(6)
+    Kh = rng.standard_normal((N, d)) * 0.01
+    Qh = np.zeros((N, d))
+    Qh[:, 0] = 1.0
+    Kh[:, 0] = -200.0
+    Kh[np.arange(0, N, 7), 0] = 200.0                # the keys every row attends to (S = +-25)
+    Vh = O.e4m3_round(rng.uniform(-300, 300, (N, d)))
+    Vh[0, :] = 448.0                                 # delta = 1 in every channel
+    mg = np.ones((1, 1, 1, 2), dtype=bool)
+    Q, K, V = Qh[None, None], Kh[None, None], Vh[None, None]
+    exact, _, dec = O.sparse_attention(Q, K, V, mg, -np.inf, False)
+    o8 = O.attend_row_block_fp8pv(Qh, Kh, Vh, mg[0, 0, 0], 0, -np.inf, False, dec[0, 0, 0])
+    # 19 attended keys per row with equal weight 1/19: P~ = 1 exactly, and the
+    # others underflow to 0 after scaling
+    assert np.max(np.abs(o8 - exact[0, 0])) < 1e-12
+
+
+def test_fp8pv_error_within_the_rounding_bound():
+    N, d = 256, 64
+    rng = np.random.default_rng(7)
+    Q, K, V = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    V[..., 5] *= 1000.0
+    mg = np.ones((1, 1, 2, 4), dtype=bool)
+    for causal in (False, True):
+        exact, _, dec = O.sparse_attention(Q, K, V, mg, -np.inf, causal)
+        o8 = O.sparse_attention_fp8pv(Q, K, V, mg, -np.inf, causal)
+        # per element: |p^ - p| <= 2^-4 p + 2^-18 (P~ scaled by 2^8, step 2^-9
+        # below 2^-6) and |v^ delta - v| <= 2^-4 |v| + 2^-10 delta
+        S = Q[0, 0] @ K[0, 0].T / math.sqrt(d)
+        if causal:
+            S = np.where(np.triu(np.ones((N, N), dtype=bool), 1), -np.inf, S)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        l = P.sum(axis=1, keepdims=True)
+        dl = O.v_channel_scales(V[0, 0])
+        av = np.abs(V[0, 0])
+        bound = ((2.0 ** -4 * P + 2.0 ** -18) @ (av * (1 + 2.0 ** -4) + 2.0 ** -10 * dl)
+                 + P @ (2.0 ** -4 * av + 2.0 ** -10 * dl)) / l
+        err = np.abs(o8[0, 0] - exact[0, 0])
+        assert np.all(err <= bound + 1e-12), float(np.max(err - bound))
+        assert O.rel_l1(exact, o8) < 0.05
