@@ -68,6 +68,9 @@ _SIGNATURES = {
     "sparge_attn": (ctypes.c_int, [_vp, _TP, _vp, _TP, _vp, _TP, _vp, _TP, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int,
                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "sparge_attn_fp8pv": (ctypes.c_int, [_vp, _TP, _vp, _TP, _vp, _TP, _vp, _TP, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int,
+                                         _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "sparge_grid_order": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "sparge_l1_workspace_size": (ctypes.c_size_t, []),
     "sparge_l1_sums": (ctypes.c_int, [_vp, _TP, ctypes.c_int, _vp, _TP, ctypes.c_int, _vp, _vp,
@@ -185,11 +188,12 @@ def predict_mask(q, k, tau: float, theta: float, causal: bool, ws=None) -> Mask:
 
 
 def attn(q, k, v, mask, lam: float, causal: bool, q_scale=None, k_scale=None, counts=None,
-         dbg: bool = False, out=None, ws=None, out_f32: bool = False):
-    """Stage 2 (sparge_attn).  ``mask`` is a :class:`Mask` (its row lists are
-    used) or a uint8 M_g tensor [B, H, Tm, Tn] (lists are built on the device).
-    ``out_f32`` stores O in float32 (before its rounding to V's type).
-    Returns (o, counts int64[8] on the device, pv_dbg or None)."""
+         dbg: bool = False, out=None, ws=None, out_f32: bool = False, fp8_pv: bool = False):
+    """Stage 2 (sparge_attn, or sparge_attn_fp8pv with ``fp8_pv``).  ``mask`` is
+    a :class:`Mask` (its row lists are used) or a uint8 M_g tensor [B, H, Tm, Tn]
+    (lists are built on the device).  ``out_f32`` stores O in float32 (before
+    its rounding to V's type).  Returns (o, counts int64[8] on the device,
+    pv_dbg or None)."""
     import torch
     B, H, N, d = q.shape
     dev = q.device
@@ -205,13 +209,14 @@ def attn(q, k, v, mask, lam: float, causal: bool, q_scale=None, k_scale=None, co
     counts = torch.empty(8, dtype=torch.int64, device=dev) if counts is None else counts
     pv_dbg = torch.zeros((B, H, Tm, Tn, BQ // 32), dtype=torch.uint8, device=dev) if dbg else None
     ws = workspace(q, k) if ws is None else ws
-    rc = lib().sparge_attn(_ptr(q), ctypes.byref(desc(q)), _ptr(k), ctypes.byref(desc(k)),
+    fn = lib().sparge_attn_fp8pv if fp8_pv else lib().sparge_attn
+    rc = fn(_ptr(q), ctypes.byref(desc(q)), _ptr(k), ctypes.byref(desc(k)),
                            _ptr(v), ctypes.byref(desc(v)), _ptr(o), ctypes.byref(desc(o)),
                            _dtype_code(q), _dtype_code(v), _dtype_code(o), _ptr(q_scale),
                            _ptr(k_scale), _ptr(mg),
                            _ptr(cnt), _ptr(idx), float(lam), int(bool(causal)), _ptr(counts),
                            _ptr(pv_dbg), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
-    _check("sparge_attn", rc)
+    _check("sparge_attn_fp8pv" if fp8_pv else "sparge_attn", rc)
     return o, counts, pv_dbg
 
 

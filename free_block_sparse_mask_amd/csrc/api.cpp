@@ -104,6 +104,7 @@ Workspace carve_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t
   w.row_l = reinterpret_cast<float*>(take(4 * (size_t)(B * H * N)));
   w.ulist = reinterpret_cast<uint32_t*>(take(4 * (size_t)(B * H * Tm * Tn)));
   w.ucnt = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * H * Tm)));
+  w.vscale = reinterpret_cast<float*>(take(4 * (size_t)(B * Hkv * d)));
   w.total = off;
   return w;
 }
@@ -323,12 +324,16 @@ int sparge_predict_mask(const void* q, const sparge_tensor* qs, const void* k,
   return ok();
 }
 
-int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
-                const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
-                int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
-                const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
-                double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int attn_impl(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+              const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+              int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+              const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+              double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
+              size_t workspace_bytes, void* stream, bool pv8) {
   int kind;
   if (qk_dtype == SPARGE_F16 && pv_dtype == SPARGE_F16) kind = 0;
   else if (qk_dtype == SPARGE_BF16 && pv_dtype == SPARGE_BF16) kind = 1;
@@ -408,6 +413,7 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
   a.Tn = (int)ceil_div(qs->N, kBk);
   a.d = (int)qs->d;
   a.kind = kind;
+  a.pv8 = pv8 ? 1 : 0;
   a.out_f32 = o_dtype == SPARGE_F32;
   a.causal = causal;
   a.q_scale = q_scale;
@@ -425,6 +431,8 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
   a.row_l = w.row_l;
   a.ulist = w.ulist;
   a.ucnt = w.ucnt;
+  a.vscale = w.vscale;
+  a.vpart = reinterpret_cast<float*>(w.ksum_part);   // free during an attention call
   hipError_t e = launch_zero_counts(a.counts, SPARGE_NUM_COUNTERS, st);
   if (e != hipSuccess) return hip_fail(e, "counter reset");
   if (need_lists) {
@@ -439,6 +447,30 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
   e = launch_attn(a, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+                const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+                int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+                const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+                double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return attn_impl(q, qs, k, ks, v, vs, o, os, qk_dtype, pv_dtype, o_dtype, q_scale, k_scale, mg, row_cnt,
+                   row_idx, lambda, causal, counts, pv_dbg, workspace, workspace_bytes, stream, false);
+}
+
+int sparge_attn_fp8pv(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+                      const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+                      int qk_dtype, int v_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+                      const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+                      double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return attn_impl(q, qs, k, ks, v, vs, o, os, qk_dtype, v_dtype, o_dtype, q_scale, k_scale, mg, row_cnt,
+                   row_idx, lambda, causal, counts, pv_dbg, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

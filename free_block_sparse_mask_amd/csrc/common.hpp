@@ -49,6 +49,8 @@ struct Workspace {
   float* row_l;        // [B,H,N] final row sum l
   uint32_t* ulist;     // [B,H,Tm,Tn] j | (wavefront mask << 16), ascending j
   int32_t* ucnt;       // [B,H,Tm]
+  // fp8 P~V: per-channel power-of-two V scales (the fp8 V^T shares vt)
+  float* vscale;       // [B,Hkv,d]
   size_t total;
 };
 
@@ -76,6 +78,9 @@ struct AttnArgs {
   int64_t o_sb, o_sh, o_sn;
   int B, H, Hkv, N, Tm, Tn, d;
   int kind;           // 0 f16, 1 bf16, 2 i8 QK + f16 PV, 3 i8 QK + bf16 PV
+  int pv8;            // P~V on fp8 E4M3 (V stored in the kind's P~V type)
+  float* vscale;      // workspace: per-channel V scales of the fp8 P~V
+  float* vpart;       // workspace: per-chunk channel maxima of |V|
   int out_f32;        // store float32 O instead of the P~V type
   int causal;
   const int32_t* row_cnt;

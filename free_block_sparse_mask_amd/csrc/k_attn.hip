@@ -74,6 +74,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -205,6 +206,11 @@ struct Geo {
   // pass 2: (K, V^T) slots
   static constexpr int E_BYTES = K_BYTES + V_BYTES;
   static constexpr int NS2 = (65536 / E_BYTES) >= 4 ? 4 : 2;
+  // pass 2 with fp8 P~V: V^T tiles of one byte per value (64 keys per row)
+  static constexpr int V8_BYTES = D * kBk;
+  static constexpr int V8CW = V8_BYTES / 1024 / kWavesPerBlock;
+  static constexpr int E8_BYTES = K_BYTES + V8_BYTES;
+  static constexpr int NS8 = (65536 / E8_BYTES) >= 4 ? 4 : 2;
   static_assert(VCW >= 1, "tile must span every wave");
   static_assert(EPM * 2 * QS == 32, "scores must split evenly over the MFMAs");
 };
@@ -215,10 +221,11 @@ size_t stats_lds_bytes(int Tn) {
   return (size_t)G::NSLOT * G::K_BYTES + (size_t)2 * ((Tn + 1) & ~1) +
          (size_t)4 * kWavesPerBlock * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
 }
-template <int D, int KIND>
+template <int D, int KIND, bool PV8>
 size_t pv_lds_bytes(int Tn) {
   using G = Geo<D, KIND>;
-  return (size_t)G::NS2 * G::E_BYTES + (size_t)4 * Tn + (G::I8 ? (size_t)4 * Tn : 0);
+  const size_t ring = PV8 ? (size_t)G::NS8 * G::E8_BYTES : (size_t)G::NS2 * G::E_BYTES;
+  return ring + (size_t)4 * Tn + (G::I8 ? (size_t)4 * Tn : 0);
 }
 
 // Per-lane pieces common to both passes: Q fragment, K DMA offsets, read bases.
@@ -611,12 +618,18 @@ void attn_stats(AttnArgs p) {
 // ---------------------------------------------------------------------------
 // Pass 2: P~V on the executed tiles, then O / l
 // ---------------------------------------------------------------------------
-template <int D, int KIND, bool CAUSAL>
+// PV8: P~V on fp8 E4M3 ([Review] Fig. 9, "SpargeAttn + Sage2"): P~ is scaled
+// by 2^8 and rounded to E4M3, V^T holds E4M3 codes of V / delta_c (delta_c a
+// per-channel power of two), and one v_mfma_scale_f32_32x32x64_f8f6f4 takes a
+// whole 64-key tile per 32 output rows; O = delta_c * O^T / 2^8 / l.
+template <int D, int KIND, bool CAUSAL, bool PV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_pv(AttnArgs p) {
   using G = Geo<D, KIND>;
   using Acc = typename std::conditional<G::I8, i32x16, f32x16>::type;
-  constexpr int NS = G::NS2;
+  constexpr int NS = PV8 ? G::NS8 : G::NS2;
+  constexpr int EB = PV8 ? G::E8_BYTES : G::E_BYTES;
+  constexpr int VCWX = PV8 ? G::V8CW : G::VCW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   int b, h, i;
@@ -628,7 +641,7 @@ void attn_pv(AttnArgs p) {
   const int U = p.ucnt[row_id];
   const uint32_t* gul = p.ulist + row_id * p.Tn;
   const float* kscale_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
-  uint32_t* ent = reinterpret_cast<uint32_t*>(smem + NS * G::E_BYTES);
+  uint32_t* ent = reinterpret_cast<uint32_t*>(smem + NS * EB);
   float* ksc = reinterpret_cast<float*>(ent + p.Tn);
   for (int e = tid; e < U; e += kThreads) {
     const uint32_t en = gul[e];
@@ -644,25 +657,42 @@ void attn_pv(AttnArgs p) {
   __syncthreads();
 
   const unsigned char* vtbase =
-      reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + L.hk) * D) * p.Np * 2;
+      reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + L.hk) * D) * p.Np * (PV8 ? 1 : 2);
+  // 16-bit V^T: rows of 128 bytes, granules XOR-swizzled by row / 2
   const int v_row0 = 16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP) + lane / 8;
   const uint32_t v_off = (uint32_t)(v_row0 * p.Np * 2) + (uint32_t)(((lane % 8) ^ ((v_row0 / 2) % 8)) * 16);
   const uint32_t v_wl = (uint32_t)((16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP)) * G::VROW);
   const int vsw = (l32 / 2) % 8;
   const uint32_t v_rd = (uint32_t)(l32 * G::VROW) + (uint32_t)((vsw & ~1) * 16) + (uint32_t)((hl ^ (vsw & 1)) * 16);
+  // fp8 V^T: rows of 64 bytes (4 granules), granule g of row m stored at
+  // position g ^ ((m >> 2) & 3); a 1 KB chunk holds 16 rows, lane -> (row
+  // lane / 4, position lane % 4)
+  const uint32_t v8_off = (uint32_t)((lane / 4) * p.Np) + (uint32_t)(((lane % 4) ^ ((lane / 16) & 3)) * 16);
+  const int f8 = (l32 >> 2) & 3;
+  const uint32_t v8_rd0 = (uint32_t)(l32 * 64 + (((2 * hl) ^ f8) * 16));
+  const uint32_t v8_rd1 = (uint32_t)(l32 * 64 + (((2 * hl + 1) ^ f8) * 16));
   const uint32_t ring_lds = lds_addr(smem);
 
-  // entry e -> slot: its K tile, then its V^T tile (KCW + VCW loads per wavefront)
+  // entry e -> slot: its K tile, then its V^T tile (KCW + VCWX loads per wavefront)
   auto issue = [&](int e, int slot) {
     const int j = __builtin_amdgcn_readfirstlane((int)(ent[e] & 0xffffu));
-    const uint32_t sl = ring_lds + (uint32_t)(slot * G::E_BYTES);
+    const uint32_t sl = ring_lds + (uint32_t)(slot * EB);
     L.issue_k(p, j, sl);
+    if constexpr (PV8) {
 #pragma unroll
-    for (int c = 0; c < G::VCW; ++c) {
-      const int row_c = 16 * c * (4 / G::VGRP);
-      const unsigned char* base = uniform_ptr(vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2);
-      dma16(base, v_off,
-            (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + row_c * G::VROW + v_wl)));
+      for (int c = 0; c < VCWX; ++c) {
+        const int q = c * kWavesPerBlock + wave;            // rows 16q .. 16q + 15
+        const unsigned char* base = uniform_ptr(vtbase + (long long)(16 * q) * p.Np + (long long)j * kBk);
+        dma16(base, v8_off, (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + q * 1024)));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < VCWX; ++c) {
+        const int row_c = 16 * c * (4 / G::VGRP);
+        const unsigned char* base = uniform_ptr(vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2);
+        dma16(base, v_off,
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + row_c * G::VROW + v_wl)));
+      }
     }
   };
 
@@ -677,12 +707,12 @@ void attn_pv(AttnArgs p) {
   for (int t = 0; t < pre; ++t) issue(t, t);
   for (int e = 0; e < U; ++e) {
     const int pend = min(U - 1, e + NS - 2) - e;    // entries issued after entry e
-    wait_pending<Lane<D, KIND, kWavesPerBlock>::KCW + G::VCW, NS - 2>(pend);
+    wait_pending<Lane<D, KIND, kWavesPerBlock>::KCW + VCWX, NS - 2>(pend);
     if (e + NS - 1 < U) issue(e + NS - 1, (e + NS - 1) % NS);
     const uint32_t en = (uint32_t)__builtin_amdgcn_readfirstlane((int)ent[e]);
     const int j = (int)(en & 0xffffu);
     if ((en >> (16 + wave)) & 1u) {       // this wavefront's group ran P~V on tile j
-      const unsigned char* kt = smem + (e % NS) * G::E_BYTES;
+      const unsigned char* kt = smem + (e % NS) * EB;
       const unsigned char* vt = kt + G::K_BYTES;
       u32x4 kf[2][G::QS];
       L.read_k(kt, kf);
@@ -701,33 +731,67 @@ void attn_pv(AttnArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
       mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, hl);
-      // P = exp(S - m_final), packed in the P~V input type as the B operand of 4 k-steps
-      u32x4 pb[4];
+      if constexpr (PV8) {
+        // P = exp(S - m_final) * 2^8 as E4M3: byte 16t + r of the lane's 32
+        // holds sv[t][r], the key order the fp8 V^T rows use
+        i32x8 pb;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int tt = s >> 1, r0 = 8 * (s & 1);
+        for (int v = 0; v < 8; ++v) {
+          const int t = v >> 2, r0 = 4 * (v & 3);
+          float y[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float x0 = fast_exp2(fmaf(sv[tt][r0 + 2 * q], c_scale, neg_m));
-          const float x1 = fast_exp2(fmaf(sv[tt][r0 + 2 * q + 1], c_scale, neg_m));
-          pb[s][q] = pack2<G::PVBF>(x0, x1);
+          for (int q = 0; q < 4; ++q) y[q] = fminf(fast_exp2(fmaf(sv[t][r0 + q], c_scale, neg_m)) * 256.0f, 448.0f);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+          pb[v] = w;
         }
-      }
-      // ---- O^T += V_j^T P^T ----
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t off = v_rd ^ (32u * s);
+        // ---- O^T += V_j^T P^T, one 64-key MFMA per 32 output rows ----
 #pragma unroll
         for (int t = 0; t < G::OT; ++t) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vt + t * 32 * G::VROW + off);
-          oacc[t] = mfma16<G::PVBF>(a, pb[s], oacc[t]);
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(vt + t * 32 * 64 + v8_rd0);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(vt + t * 32 * 64 + v8_rd1);
+          const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                            (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, oacc[t], 0, 0, 0, 127, 0, 127);
+        }
+      } else {
+        // P = exp(S - m_final), packed in the P~V input type as the B operand of 4 k-steps
+        u32x4 pb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int tt = s >> 1, r0 = 8 * (s & 1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x0 = fast_exp2(fmaf(sv[tt][r0 + 2 * q], c_scale, neg_m));
+            const float x1 = fast_exp2(fmaf(sv[tt][r0 + 2 * q + 1], c_scale, neg_m));
+            pb[s][q] = pack2<G::PVBF>(x0, x1);
+          }
+        }
+        // ---- O^T += V_j^T P^T ----
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t off = v_rd ^ (32u * s);
+#pragma unroll
+          for (int t = 0; t < G::OT; ++t) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(vt + t * 32 * G::VROW + off);
+            oacc[t] = mfma16<G::PVBF>(a, pb[s], oacc[t]);
+          }
         }
       }
     }
   }
 
-  // ---- epilogue: O / l ----
+  // ---- epilogue: O / l (fp8: times delta_c / 2^8) ----
   const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+  if constexpr (PV8) {
+    const float* vs = p.vscale + (long long)(b * p.Hkv + L.hk) * D;
+#pragma unroll
+    for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) oacc[t][4 * g + q] *= vs[32 * t + 8 * g + 4 * hl + q] * (1.0f / 256.0f);
+  }
   if (L.qvalid && p.out_f32) {
     float* ob = static_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)L.qrow * p.o_sn;
 #pragma unroll
@@ -794,31 +858,147 @@ __global__ __launch_bounds__(kThreads) void transpose_v(AttnArgs p) {
   }
 }
 
+// fp8 P~V, step 1: per chunk of kQuantChunkRows tokens, the channel maxima of
+// |V| (grid: chunks x B*Hkv; 8 channels per lane, rows strided over the
+// workgroup, then a reduction over the row slots in LDS).
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void v_absmax_partial(AttnArgs p) {
+  constexpr int CG = D / 8;                 // lanes per row
+  constexpr int SLOTS = kThreads / CG;
+  __shared__ float red[SLOTS][D + 1];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int tid = threadIdx.x, c = tid % CG, slot = tid / CG;
+  const unsigned short* vb = static_cast<const unsigned short*>(p.v) + b * p.v_sb + hk * p.v_sh;
+  const int r0 = chunk * kQuantChunkRows, r1 = min(p.N, r0 + kQuantChunkRows);
+  float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r0 + slot; r < r1; r += SLOTS) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(vb + (long long)r * p.v_sn + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned short u = (unsigned short)(w[e >> 1] >> (16 * (e & 1)));
+      const float x = BF16 ? __uint_as_float((unsigned int)u << 16) : (float)__builtin_bit_cast(_Float16, u);
+      mx[e] = fmaxf(mx[e], fabsf(x));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[slot][8 * c + e] = mx[e];
+  __syncthreads();
+  if (tid < D) {
+    float m = 0.0f;
+    for (int s = 0; s < SLOTS; ++s) m = fmaxf(m, red[s][tid]);
+    p.vpart[((long long)bh * gridDim.x + chunk) * D + tid] = m;
+  }
+}
+
+// fp8 P~V, step 2: delta_c = 2^e, e the least integer with max|V_c| <= 448 2^e
+// (clamped to 2^-100 for a channel that is all but zero; 1 for a zero one).
+__global__ void v_scale_final(AttnArgs p, int chunks) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  if (c >= p.d) return;
+  float m = 0.0f;
+  for (int k = 0; k < chunks; ++k) m = fmaxf(m, p.vpart[((long long)bh * chunks + k) * p.d + c]);
+  float delta = 1.0f;
+  if (m > 0.0f) {
+    int e = (int)ceilf(log2f(m / 448.0f));
+    e = max(-100, min(e, 127));
+    while (e < 127 && m > ldexpf(448.0f, e)) ++e;
+    while (e > -100 && m <= ldexpf(448.0f, e - 1)) --e;
+    delta = ldexpf(1.0f, e);
+  }
+  p.vscale[(long long)bh * p.d + c] = delta;
+}
+
+// fp8 P~V, step 3: V [B,Hkv,N,D] -> E4M3 codes of V / delta_c in V^T order
+// [B,Hkv,D,Np] (zero past N).  Inside each 64-key row, byte 32h + b holds key
+// 32 (b / 16) + 8 ((b % 16) / 4) + 4h + b % 4: the keys lane half h of the
+// P~V MFMA holds, in the order of its score registers.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void transpose_v8(AttnArgs p) {
+  __shared__ __attribute__((aligned(16))) unsigned short tile[64][72];
+  const int kt = blockIdx.x, dt = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int tid = threadIdx.x;
+  const unsigned short* vb = static_cast<const unsigned short*>(p.v) + b * p.v_sb + hk * p.v_sh;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int key = tid / 8 + 32 * r, ch = tid % 8;
+    const int gk = kt * 64 + key;
+    u32x4 val = {0, 0, 0, 0};
+    if (gk < p.N) val = *reinterpret_cast<const u32x4*>(vb + (long long)gk * p.v_sn + dt * 64 + 8 * ch);
+    *reinterpret_cast<u32x4*>(&tile[key][8 * ch]) = val;
+  }
+  __syncthreads();
+  const int dv = tid / 4, g = tid % 4;             // channel dt*64 + dv, bytes 16g .. 16g + 15
+  const float inv = 1.0f / p.vscale[(long long)bh * p.d + dt * 64 + dv];   // a power of two: exact
+  u32x4 w;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float y[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pos = 16 * g + 4 * v + q, hh = pos / 32, bb = pos % 32;
+      const int key = 32 * (bb / 16) + 8 * ((bb % 16) / 4) + 4 * hh + (bb % 4);
+      const unsigned short u = tile[key][dv];
+      const float x = BF16 ? __uint_as_float((unsigned int)u << 16) : (float)__builtin_bit_cast(_Float16, u);
+      y[q] = fminf(fmaxf(x * inv, -448.0f), 448.0f);
+    }
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w[v] = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
+  }
+  unsigned char* out = reinterpret_cast<unsigned char*>(p.vt) + ((long long)bh * p.d) * p.Np;
+  *reinterpret_cast<u32x4*>(out + (long long)(dt * 64 + dv) * p.Np + kt * 64 + 16 * g) = w;
+}
+
 __global__ void zero_u64(unsigned long long* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
 }
 
-template <int D, int KIND, bool CAUSAL>
+template <int D, int KIND, bool CAUSAL, bool PV8>
 hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
   const long long blocks = (long long)a.B * a.H * a.Tm;
   const size_t lds1 = stats_lds_bytes<D, KIND>(a.Tn);
-  const size_t lds2 = pv_lds_bytes<D, KIND>(a.Tn);
+  const size_t lds2 = pv_lds_bytes<D, KIND, PV8>(a.Tn);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pv<D, KIND, CAUSAL>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pv<D, KIND, CAUSAL, PV8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds1, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_pv<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds2, st, a);
+  hipLaunchKernelGGL((attn_pv<D, KIND, CAUSAL, PV8>), dim3((unsigned)blocks), dim3(kThreads), lds2, st, a);
   return hipGetLastError();
 }
 
 template <int D, int KIND>
 hipError_t launch_d_kind(const AttnArgs& a, hipStream_t st) {
-  return a.causal ? launch_passes<D, KIND, true>(a, st) : launch_passes<D, KIND, false>(a, st);
+  if (a.pv8) return a.causal ? launch_passes<D, KIND, true, true>(a, st) : launch_passes<D, KIND, false, true>(a, st);
+  return a.causal ? launch_passes<D, KIND, true, false>(a, st) : launch_passes<D, KIND, false, false>(a, st);
+}
+
+// the fp8 V^T: channel maxima, power-of-two scales, E4M3 codes
+template <int D>
+hipError_t launch_v8(const AttnArgs& a, hipStream_t st) {
+  const bool bf = (a.kind == 1 || a.kind == 3);
+  const int chunks = (int)ceil_div(a.N, kQuantChunkRows);
+  const dim3 g1((unsigned)chunks, (unsigned)(a.B * a.Hkv));
+  if (bf)
+    hipLaunchKernelGGL((v_absmax_partial<D, true>), g1, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((v_absmax_partial<D, false>), g1, dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(v_scale_final, dim3((unsigned)(a.B * a.Hkv)), dim3(128), 0, st, a, chunks);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g3((unsigned)(a.Np / 64), (unsigned)(a.d / 64), (unsigned)(a.B * a.Hkv));
+  if (bf)
+    hipLaunchKernelGGL(transpose_v8<true>, g3, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(transpose_v8<false>, g3, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -839,9 +1019,14 @@ hipError_t launch_zero_counts(unsigned long long* counts, int n, hipStream_t st)
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
-  dim3 g((unsigned)(a.Np / 64), (unsigned)(a.d / 64), (unsigned)(a.B * a.Hkv));
-  hipLaunchKernelGGL(transpose_v, g, dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (a.pv8) {
+    e = a.d == 64 ? launch_v8<64>(a, st) : launch_v8<128>(a, st);
+  } else {
+    dim3 g((unsigned)(a.Np / 64), (unsigned)(a.d / 64), (unsigned)(a.B * a.Hkv));
+    hipLaunchKernelGGL(transpose_v, g, dim3(kThreads), 0, st, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   return a.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
 }

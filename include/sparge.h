@@ -193,6 +193,31 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
                 size_t workspace_bytes, void* stream);
 
 /*
+ * The "SpargeAttn + Sage2" variant of stage 2 ([Review] Fig. 9): the same
+ * block-sparse attention and lambda rule as sparge_attn, with P~V on 8-bit
+ * floats (OCP E4M3: 4 exponent bits, bias 7, 3 mantissa bits, largest 448,
+ * round to nearest even).  The pages only name the variant; the formats
+ * taken here are:
+ *   V is scaled per channel by delta_c = 2^e, e the least integer with
+ *     max_n |V[n, c]| <= 448 * 2^e (clamped at 2^-100; 1 for a zero
+ *     channel), so V / delta_c is exact before its one rounding to E4M3;
+ *   P~ = exp(S - m_final) (m_final: the row's final running max) is scaled
+ *     by 2^8 and rounded to E4M3;
+ *   O = delta_c * sum(P8 V8) / 2^8 / l, with l the float32 row sum of the
+ *     unrounded P~ and the products summed in float32 on the matrix cores.
+ * Arguments as sparge_attn, except v_dtype (SPARGE_F16 or SPARGE_BF16): the
+ * element type v is stored in (qk_dtype equal to it, or SPARGE_I8); o_dtype
+ * is v_dtype or SPARGE_F32.  The workspace also holds the fp8 copy of V^T
+ * and the scales.  Same error behaviour as sparge_attn.
+ */
+int sparge_attn_fp8pv(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+                      const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+                      int qk_dtype, int v_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+                      const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+                      double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
  * Token orders of a T x H x W grid of visual tokens (host), the alternatives
  * the permutation comparison of [Review] (Table 4: random, row-major,
  * time-major, HilbertCurve) sets against each other.  Grid token (t, h, w)

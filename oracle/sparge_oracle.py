@@ -467,7 +467,8 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
 
 
 def v_channel_scales(Vh: np.ndarray) -> np.ndarray:
-    """delta_c = 2^e with e the least integer such that max|V[:, c]| <= 448 * 2^e."""
+    """delta_c = 2^e with e the least integer such that max|V[:, c]| <= 448 * 2^e,
+    at least 2^-100; 1 for an all-zero channel."""
     mx = np.abs(Vh).max(axis=0)
     e = np.zeros_like(mx)
     nz = mx > 0
@@ -475,16 +476,26 @@ def v_channel_scales(Vh: np.ndarray) -> np.ndarray:
     # exact comparisons settle a log2 that lands next to an integer
     e = np.where(nz & (mx > E4M3_MAX * 2.0 ** e), e + 1, e)
     e = np.where(nz & (mx <= E4M3_MAX * 2.0 ** (e - 1)), e - 1, e)
+    e = np.maximum(e, -100.0)                        # all but zero channels: 2^-100
     return np.where(nz, 2.0 ** e, 1.0)
 
 
 def attend_row_block_fp8pv(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.ndarray, i: int,
                            lam: float, causal: bool, decisions: np.ndarray, bq: int = BQ, bk: int = BK,
-                           R: int = ROWS_PER_GROUP, score_fn=None) -> np.ndarray:
+                           R: int = ROWS_PER_GROUP, score_fn=None, amb_window: Optional[float] = None,
+                           sum_rel: float = 0.0):
     """O_i of the fp8 P~V variant for one query block, given the (tile, group)
     decisions of the lambda rule ([Tn, c_w], 1 = P~V runs): m_final and l are
     eq. 1's final running max and row sum (exact); the voted groups add
-    e4m3(2^8 exp(S - m_final)) e4m3(V / delta) and O = delta sum / 2^8 / l."""
+    e4m3(2^8 exp(S - m_final)) e4m3(V / delta) and O = delta sum / 2^8 / l.
+
+    With ``amb_window`` w, also returns for every output element the most it
+    can move when a P~ within relative distance w of an E4M3 rounding
+    boundary rounds the other way (the width of that rounding step times the
+    element's V term, over 2^8 l), plus ``sum_rel`` times the sum of the
+    absolute products of every 64-key tile: the room another implementation
+    may take whose P~ differs from this one by less than w and whose tile
+    sums carry a relative error below sum_rel."""
     N, d = Qh.shape
     Tn = num_blocks(N, bk)
     rows = block_rows(N, bq, i)
@@ -508,36 +519,49 @@ def attend_row_block_fp8pv(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_ro
     delta = v_channel_scales(Vh)
     Vq = e4m3_round(Vh / delta[None, :])
     acc = np.zeros((n, Vh.shape[1]))
+    amb = np.zeros_like(acc)
     for j in todo:
         keys = block_rows(N, bk, j)
         with np.errstate(invalid="ignore"):
             P = np.exp(S_of[j] - m_sub[:, None])
         l += P.sum(axis=1)
         Pq = e4m3_round(PV8_P_SCALE * P)
+        if amb_window is not None:
+            step = np.abs(e4m3_round(PV8_P_SCALE * P * (1 + amb_window)) -
+                          e4m3_round(PV8_P_SCALE * P * (1 - amb_window)))
         for g in range(decisions.shape[1]):
             if decisions[j, g] != 1:
                 continue
             gi = np.arange(g * R, min(n, g * R + R))
             acc[gi] += Pq[gi] @ Vq[keys.start:keys.stop]
+            if amb_window is not None:
+                amb[gi] += (step[gi] + sum_rel * np.abs(Pq[gi])) @ np.abs(Vq[keys.start:keys.stop])
     out = np.zeros_like(acc)
     nz = l > 0
     out[nz] = acc[nz] * delta[None, :] / PV8_P_SCALE / l[nz, None]
-    return out
+    if amb_window is None:
+        return out
+    amb_out = np.zeros_like(amb)
+    amb_out[nz] = amb[nz] * delta[None, :] / PV8_P_SCALE / l[nz, None]
+    return out, amb_out
 
 
 def sparse_attention_fp8pv(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray, lam: float,
                            causal: bool, blocks=None, skip_override: Optional[np.ndarray] = None,
-                           quant: Optional[dict] = None) -> np.ndarray:
+                           quant: Optional[dict] = None, amb_window: Optional[float] = None,
+                           sum_rel: float = 0.0):
     """The fp8 P~V variant for Q [B, H, N, d], K/V [B, H_kv, N, d]: the lambda
     decisions come from :func:`sparse_attention` (or ``skip_override``), the
     output from :func:`attend_row_block_fp8pv`.  ``blocks`` restricts the work
-    to (b, h, i); other rows stay 0."""
+    to (b, h, i); other rows stay 0.  With ``amb_window``, returns (O, room)
+    with room as in :func:`attend_row_block_fp8pv`."""
     B, H, N, d = Q.shape
     H_kv = K.shape[1]
     Tm = num_blocks(N, BQ)
     _, _, dec = sparse_attention(Q, K, V, mg, lam, causal, blocks=blocks, skip_override=skip_override,
                                  quant=quant)
     O = np.zeros((B, H, N, V.shape[3]))
+    room = np.zeros_like(O)
     todo = blocks if blocks is not None else [(b, h, i) for b in range(B) for h in range(H) for i in range(Tm)]
     for b, h, i in todo:
         hk = kv_head(h, H, H_kv)
@@ -550,9 +574,13 @@ def sparse_attention_fp8pv(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.n
                 j = keys.start // BK
                 return (qc[rows.start:rows.stop] @ kc[keys.start:keys.stop].T) * (dq[i] * dk[j]) / math.sqrt(d)
         r = block_rows(N, BQ, i)
-        O[b, h, r.start:r.stop] = attend_row_block_fp8pv(Q[b, h], K[b, hk], V[b, hk], mg[b, h, i], i, lam,
-                                                         causal, dec[b, h, i], score_fn=score_fn)
-    return O
+        res = attend_row_block_fp8pv(Q[b, h], K[b, hk], V[b, hk], mg[b, h, i], i, lam, causal, dec[b, h, i],
+                                     score_fn=score_fn, amb_window=amb_window, sum_rel=sum_rel)
+        if amb_window is None:
+            O[b, h, r.start:r.stop] = res
+        else:
+            O[b, h, r.start:r.stop], room[b, h, r.start:r.stop] = res
+    return O if amb_window is None else (O, room)
 
 
 # ---------------------------------------------------------------------------
