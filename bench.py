@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 variant")
+    ap.add_argument("--no-fp8pv", action="store_true", help="skip the fp8 P~V variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=150,
                     help="query blocks of head 0 the CPU oracle attends (sample size)")
@@ -247,6 +248,39 @@ def main():
             "counts": c8,
         }
         log(f"[bench] int8 step: wall {wall8:.3f} ms, quant {quant_ms:.3f}, predict {pred8:.3f}, attn {attn8:.3f}")
+
+    if not args.no_fp8pv:
+        # the fp8 P~V variant (sparge_attn_fp8pv) on the same bf16 inputs
+        torch.cuda.synchronize()
+
+        def step_f8(ev=None):
+            if ev is not None:
+                ev[0].record()
+            mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
+            if ev is not None:
+                ev[1].record()
+            o, counts, _ = fb.attn(qd, kd, vd, mask, w.lam, w.causal, ws=ws, fp8_pv=True)
+            if ev is not None:
+                ev[2].record()
+            return counts
+
+        for _ in range(args.warmup):
+            step_f8()
+        torch.cuda.synchronize()
+        evsf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        tf = time.perf_counter()
+        for s in range(args.steps):
+            countsf = step_f8(evsf[s])
+        torch.cuda.synchronize()
+        wallf = (time.perf_counter() - tf) * 1e3 / args.steps
+        predf = float(np.mean([e[0].elapsed_time(e[1]) for e in evsf]))
+        attnf = float(np.mean([e[1].elapsed_time(e[2]) for e in evsf]))
+        cf = fb.counts_dict(countsf)
+        result["fp8pv"] = {
+            "ms_per_step": wallf, "predict_ms": predf, "attn_ms": attnf,
+            "dense_equiv_tflops": dense / (wallf * 1e-3) / 1e12, "counts": cf,
+        }
+        log(f"[bench] fp8 P~V step: wall {wallf:.3f} ms, predict {predf:.3f}, attn {attnf:.3f}")
 
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4

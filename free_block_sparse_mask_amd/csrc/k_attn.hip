@@ -210,7 +210,9 @@ struct Geo {
   static constexpr int V8_BYTES = D * kBk;
   static constexpr int V8CW = V8_BYTES / 1024 / kWavesPerBlock;
   static constexpr int E8_BYTES = K_BYTES + V8_BYTES;
-  static constexpr int NS8 = (65536 / E8_BYTES) >= 4 ? 4 : 2;
+  // as many slots (up to 4) as keep the ring at 72 KB, so two workgroups
+  // still share a CU
+  static constexpr int NS8 = 4 * E8_BYTES <= 65536 ? 4 : (3 * E8_BYTES <= 73728 ? 3 : 2);
   static_assert(VCW >= 1, "tile must span every wave");
   static_assert(EPM * 2 * QS == 32, "scores must split evenly over the MFMAs");
 };

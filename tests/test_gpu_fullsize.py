@@ -133,3 +133,42 @@ def test_full_size_gqa_int8():
     c = _check_whole(w, mask, counts, o16, o32)
     log(f"   counts {c}")
     _check_heads(w, q, k, v, mask, dbg, o32, [0, 31], int8=True, v_dtype="f16")
+
+
+def test_full_size_gqa_fp8pv():
+    """The fp8 P~V variant at 128K GQA, in the bench's configuration: sampled
+    blocks of two heads against the oracle's fp8 restatement (same rules as
+    the small fp8 parity tests), whole-output properties on everything."""
+    from test_gpu_fp8pv import FP8_ABS_SLACK, FP8_AMB_WINDOW, FP8_REL_L1, FP8_SUM_REL
+    w = I.workload(4)
+    log(f"[full] {w.name} fp8 P~V")
+    q, k, v = I.make_qkv(w, workers=16)
+    qd, kd, vd = _up(q, w.dtype), _up(k, w.dtype), _up(v, w.dtype)
+    ws = fb.workspace(qd, kd)
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
+    o16, counts, dbg = fb.attn(qd, kd, vd, mask, w.lam, w.causal, ws=ws, dbg=True, fp8_pv=True)
+    o32, counts32, _ = fb.attn(qd, kd, vd, mask, w.lam, w.causal, ws=ws, out_f32=True, fp8_pv=True)
+    torch.cuda.synchronize()
+    assert torch.equal(counts, counts32)
+    c = _check_whole(w, mask, counts, o16, o32)
+    log(f"   counts {c}")
+    group = w.H // w.H_kv
+    Tm = O.num_blocks(w.N, O.BQ)
+    for h in (0, 31):
+        hk = h // group
+        Qh = O.widen(q[:, h:h + 1], w.dtype)
+        Kh = O.widen(k[:, hk:hk + 1], w.dtype)
+        Vh = O.widen(v[:, hk:hk + 1], w.dtype)
+        blocks = [(0, 0, i) for i in _sample_blocks(Tm)]
+        mg_h = mask.mg[:, h:h + 1].cpu().numpy().astype(bool)
+        gdec = dbg[:, h:h + 1].cpu().numpy().astype(np.int8)
+        ref, room = O.sparse_attention_fp8pv(Qh, Kh, Vh, mg_h, w.lam, w.causal, blocks=blocks, skip_override=gdec,
+                                             amb_window=FP8_AMB_WINDOW, sum_rel=FP8_SUM_REL)
+        og = o32[:, h:h + 1].cpu().double().numpy()
+        sel = np.concatenate([np.arange(O.block_rows(w.N, O.BQ, i).start, O.block_rows(w.N, O.BQ, i).stop)
+                              for _, _, i in blocks])
+        r, g, rm = ref[0, 0, sel], og[0, 0, sel], room[0, 0, sel]
+        e_rel = O.rel_l1(r, g)
+        over = float(np.max(np.abs(r - g) - rm))
+        log(f"   head {h}: blocks {[bl[2] for bl in blocks]}: rel_l1={e_rel:.2e} max over room={over:.2e}")
+        assert e_rel <= FP8_REL_L1 and over <= FP8_ABS_SLACK
