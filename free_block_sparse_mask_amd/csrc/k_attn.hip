@@ -254,9 +254,8 @@ struct Lane {
   uint32_t k_wl;             // this wavefront's LDS offset inside a tile (uniform)
   uint32_t k_rd;
 
-  // wq: wavefront index inside its query block (0..3); has_rows: false for
-  // a workgroup slot past the last query block
-  __device__ __forceinline__ void init(const AttnArgs& p, int b_, int h_, int i_, int wq, bool has_rows) {
+  // wq: wavefront index inside its query block (0..3)
+  __device__ __forceinline__ void init(const AttnArgs& p, int b_, int h_, int i_, int wq) {
     b = b_;
     h = h_;
     i = i_;
@@ -268,7 +267,7 @@ struct Lane {
     hl = lane >> 5;
     q0 = i * kBq + wq * kRowsPerWave;
     qrow = q0 + l32;
-    qvalid = has_rows && qrow < p.N;
+    qvalid = qrow < p.N;
     row_id = (long long)(b * p.H + h) * p.Tm + i;
     if constexpr (G::I8) {
       const int8_t* qb = static_cast<const int8_t*>(p.q) + ((long long)(b * p.H + h) * p.N) * D;
@@ -276,7 +275,7 @@ struct Lane {
       for (int s = 0; s < G::QS; ++s)
         qf[s] = qvalid ? *reinterpret_cast<const u32x4*>(qb + (long long)qrow * D + 32 * s + 16 * hl)
                        : u32x4{0, 0, 0, 0};
-      qscale = has_rows ? p.q_scale[row_id] : 1.0f;
+      qscale = p.q_scale[row_id];
       kbase = static_cast<const unsigned char*>(p.k) + ((long long)(b * p.Hkv + hk) * p.N) * D;
       k_sn_bytes = D;
     } else {
@@ -390,7 +389,7 @@ void attn_stats(AttnArgs p) {
   if (!map_block(p, p.Tm, b, h, i)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   LN L;
-  L.init(p, b, h, i, wave, true);
+  L.init(p, b, h, i, wave);
   const long long row_id = L.row_id;
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
   const int n_live = CAUSAL ? min(p.Tn, last_q / kBk + 1) : p.Tn;
@@ -637,7 +636,7 @@ void attn_pv(AttnArgs p) {
   int b, h, i;
   if (!map_block(p, p.Tm, b, h, i)) return;
   Lane<D, KIND, kWavesPerBlock> L;
-  L.init(p, b, h, i, (int)(threadIdx.x >> 6), true);
+  L.init(p, b, h, i, (int)(threadIdx.x >> 6));
   const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
   const long long row_id = L.row_id;
   const int U = p.ucnt[row_id];
