@@ -59,6 +59,9 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // log2-units distance below the running max past which a whole tile's
 // exponentials cannot change a float32 row sum (see attn_stats)
 constexpr float kFarLog2 = 40.0f;
+// attention pass 1: K ring slots and tiles loaded ahead
+constexpr int kStatsSlots = 2;
+constexpr int kStatsAhead = 1;
 
 // v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
 // in the other, so combining the two gives every lane the pair (l, l ^ 32).
@@ -202,7 +205,7 @@ struct Geo {
   static constexpr int OT = D / 32;                    // 32-column tiles of O^T
   static constexpr int EPM = 32 / (2 * QS);            // scores per lane per QK^T MFMA
   // pass 1: K ring slots
-  static constexpr int NSLOT = 2;
+  static constexpr int NSLOT = kStatsSlots;
   // pass 2: (K, V^T) slots
   static constexpr int E_BYTES = K_BYTES + V_BYTES;
   static constexpr int NS2 = (65536 / E_BYTES) >= 4 ? 4 : 2;
@@ -519,32 +522,47 @@ void attn_stats(AttnArgs p) {
     }
   };
 
-  // One barrier per entry: at entry e's barrier its tile (the only load in
-  // flight) has landed and every wavefront is done with entry e-1, whose
-  // slot then takes entry e+1.
+  // A ring of NSLOT K slots, PD tiles loaded ahead, one barrier per entry:
+  // at entry e's barrier its tile has landed (the younger loads may still be
+  // in flight) and every wavefront is done with entry e-1, whose slot then
+  // takes entry e+PD.
+  constexpr int NSLOT = G::NSLOT;
+  constexpr int PD = kStatsAhead;
+  static_assert(PD >= 1 && PD < NSLOT, "the refilled slot must be free");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   int jd_v = 0;               // tile of the next refill (read one entry early)
-  if (UC > 0) {
-    L.issue_k(p, __builtin_amdgcn_readfirstlane((int)lst[0]), ring_lds);
-    jd_v = lst[min(1, UC - 1)];
-  }
-  // step(e): the barrier, then tile e, which refills the other slot with e+1
+  for (int t = 0; t < min(PD, UC); ++t)
+    L.issue_k(p, __builtin_amdgcn_readfirstlane((int)lst[t]), ring_lds + (uint32_t)((t % NSLOT) * G::K_BYTES));
+  if (UC > 0) jd_v = lst[min(PD, UC - 1)];
+  // step(e): the barrier, then tile e, which refills entry e-1's slot with e+PD
   auto step = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    wait_barrier<0>();
+    wait_pending<LN::KCW, PD - 1>(min(UC - 1, e + PD - 1) - e);
     tile(e, slot_c, [&]() {
-      const int j1 = __builtin_amdgcn_readfirstlane(jd_v);
-      if (e + 1 < UC) L.issue_k(p, j1, ring_lds + (uint32_t)((1 - SL) * G::K_BYTES));
-      jd_v = lst[min(e + 2, UC - 1)];
+      const int jn = __builtin_amdgcn_readfirstlane(jd_v);
+      if (e + PD < UC) L.issue_k(p, jn, ring_lds + (uint32_t)(((SL + PD) % NSLOT) * G::K_BYTES));
+      jd_v = lst[min(e + PD + 1, UC - 1)];
     });
   };
   int e = 0;
-  for (; e + 2 <= UC; e += 2) {
-    step(e, I0{});
-    step(e + 1, I1{});
+  if constexpr (NSLOT == 2) {
+    for (; e + 2 <= UC; e += 2) {
+      step(e, I0{});
+      step(e + 1, I1{});
+    }
+    if (e < UC) step(e, I0{});
+  } else {
+    static_assert(NSLOT == 3, "two or three slots");
+    for (; e + 3 <= UC; e += 3) {
+      step(e, I0{});
+      step(e + 1, I1{});
+      step(e + 2, I2{});
+    }
+    if (e < UC) step(e, I0{});
+    if (e + 1 < UC) step(e + 1, I1{});
   }
-  if (e < UC) step(e, I0{});
   wait_barrier<0>();                       // every vote word is written
 
   // ---- the block's executed-tile list (listed tiles with a voting wavefront) ----
