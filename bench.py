@@ -203,7 +203,8 @@ def main():
         "counts": c,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "transpose_v + attn_stats + attn_pv <128, bf16, causal> (one sparge_attn call)",
+                     "kernel": "transpose_v + build_packs + attn_stats (packed, then single) + sum_counts + attn_pv "
+                               "<128, bf16, causal> (one sparge_attn call)",
                      "flops_per_launch": exe},
     }
 

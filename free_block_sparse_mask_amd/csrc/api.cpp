@@ -105,6 +105,10 @@ Workspace carve_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t
   w.ulist = reinterpret_cast<uint32_t*>(take(4 * (size_t)(B * H * Tm * Tn)));
   w.ucnt = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * H * Tm)));
   w.vscale = reinterpret_cast<float*>(take(4 * (size_t)(B * Hkv * d)));
+  w.packs = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv) * (size_t)pack_slots((int)H, (int)Hkv, (int)Tm)));
+  w.npack = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
+  w.pack_next = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
+  w.cnt_part = reinterpret_cast<unsigned long long*>(take(8 * (size_t)kCountSlots * SPARGE_NUM_COUNTERS));
   w.total = off;
   return w;
 }
@@ -432,9 +436,12 @@ int attn_impl(const void* q, const sparge_tensor* qs, const void* k, const sparg
   a.ulist = w.ulist;
   a.ucnt = w.ucnt;
   a.vscale = w.vscale;
+  a.packs = w.packs;
+  a.npack = w.npack;
+  a.pack_next = w.pack_next;
+  a.cnt_part = w.cnt_part;
   a.vpart = reinterpret_cast<float*>(w.ksum_part);   // free during an attention call
-  hipError_t e = launch_zero_counts(a.counts, SPARGE_NUM_COUNTERS, st);
-  if (e != hipSuccess) return hip_fail(e, "counter reset");
+  hipError_t e = hipSuccess;   // the attention kernels overwrite every counter
   if (need_lists) {
     e = launch_compact(mg, (int64_t)a.B * a.H * a.Tm, a.Tm, a.Tn, a.N, causal, w.list_cnt, w.list_idx, st);
     if (e != hipSuccess) return hip_fail(e, "mask compaction launch");

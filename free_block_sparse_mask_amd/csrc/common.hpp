@@ -15,6 +15,20 @@ constexpr int kBk = SPARGE_BK;              // key/value block rows
 constexpr int kRowsPerWave = 32;            // rows voting together (one wavefront)
 constexpr int kWavesPerBlock = kBq / kRowsPerWave;
 constexpr int kThreads = 256;
+// attention pass 1: query blocks that list every live tile share one
+// workgroup (and one K stream) in packs of this many blocks of one kv head
+constexpr int kPackBlocks = 2;
+
+// attention pass 1: slots of partial counters (workgroup id % kCountSlots),
+// so that short workgroups do not all add to the same eight addresses
+constexpr int kCountSlots = 64;
+
+// slots per (b, kv head) of the dense-block packs: G * Tm rounded up to a
+// whole number of packs
+inline __host__ __device__ int pack_slots(int H, int Hkv, int Tm) {
+  const int n = (H / Hkv) * Tm;
+  return (n + kPackBlocks - 1) / kPackBlocks * kPackBlocks;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -51,6 +65,11 @@ struct Workspace {
   int32_t* ucnt;       // [B,H,Tm]
   // fp8 P~V: per-channel power-of-two V scales (the fp8 V^T shares vt)
   float* vscale;       // [B,Hkv,d]
+  // attention pass 1: dense query blocks in packs, and packs per kv head
+  int32_t* packs;      // [B,Hkv,pack_slots] row ids (b H + h) Tm + i, -1 pads
+  int32_t* npack;      // [B,Hkv]
+  int32_t* pack_next;  // [B,Hkv] next unclaimed pack of each kv head
+  unsigned long long* cnt_part;   // [kCountSlots][SPARGE_NUM_COUNTERS]
   size_t total;
 };
 
@@ -72,6 +91,10 @@ struct AttnArgs {
   float* row_l;        // workspace: pass 1 row sum per row
   uint32_t* ulist;     // workspace: executed-tile lists (j | mask << 16)
   int32_t* ucnt;       // workspace: their lengths
+  int32_t* packs;      // workspace: dense query blocks in packs (see Workspace)
+  int32_t* npack;      // workspace: packs per (b, kv head)
+  int32_t* pack_next;  // workspace: next unclaimed pack per (b, kv head)
+  unsigned long long* cnt_part;   // workspace: partial counters
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;

@@ -27,10 +27,17 @@
 // a small fraction of the tiles, and pass 1 holds only K: a two-slot ring
 // small enough that four workgroups share a CU.
 //
+// Most of pass 1's tiles belong to query blocks whose row of M_g is all
+// ones on the live tiles (the fix blocks of eq. (9) force it), so their
+// lists are 0, 1, ..., live - 1 and prefixes of one another.  build_packs
+// pairs such blocks of one kv head, heaviest first, and one workgroup of 8
+// wavefronts runs a pair on one K stream (half the tile loads); the other
+// blocks keep a workgroup of their own.
+//
 // Layout (CDNA4 first, not the pages' CUDA warp layout):
-// * One workgroup of 4 wavefronts per query block i of 128 rows; wavefront w
-//   owns rows [32w, 32w + 32) of the block, so the lambda vote is one ballot
-//   over a 64-lane wavefront (both lane halves hold the same 32 rows).
+// * 4 wavefronts per query block i of 128 rows; wavefront w owns rows
+//   [32w, 32w + 32) of the block, so the lambda vote is one ballot over a
+//   64-lane wavefront (both lane halves hold the same 32 rows).
 // * S^T = K_j Q_i^T on v_mfma_f32_32x32x16 (bf16/f16) or v_mfma_i32_32x32x32_i8:
 //   the accumulator layout of S^T puts one query row per lane (lane % 32) and
 //   16 of its 32 keys per 32x32 tile in registers, so the row max is an
@@ -46,7 +53,8 @@
 //   followed by a barrier).  The 16-byte granules of each LDS row are
 //   XOR-swizzled by row so the MFMA operand reads hit distinct banks.
 // * Grid order: heaviest query blocks (largest i) first, in phases of a few
-//   kv heads with one kv head per XCD (see map_block).
+//   kv heads with one kv head per XCD (see map_block); the pairs of pass 1
+//   come from per-kv-head queues, each XCD starting on its own kv heads.
 #include <type_traits>
 
 #include "common.hpp"
@@ -59,9 +67,12 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // log2-units distance below the running max past which a whole tile's
 // exponentials cannot change a float32 row sum (see attn_stats)
 constexpr float kFarLog2 = 40.0f;
-// attention pass 1: K ring slots and tiles loaded ahead
+// attention pass 1: K ring slots and tiles loaded ahead, for one query block
+// per workgroup and for packs of dense blocks
 constexpr int kStatsSlots = 2;
 constexpr int kStatsAhead = 1;
+constexpr int kPackSlots = 2;
+constexpr int kPackAhead = 1;
 
 // v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
 // in the other, so combining the two gives every lane the pair (l, l ^ 32).
@@ -204,8 +215,6 @@ struct Geo {
   static constexpr int QS = I8 ? D / 32 : D / 16;      // k-steps of the QK^T MFMA
   static constexpr int OT = D / 32;                    // 32-column tiles of O^T
   static constexpr int EPM = 32 / (2 * QS);            // scores per lane per QK^T MFMA
-  // pass 1: K ring slots
-  static constexpr int NSLOT = kStatsSlots;
   // pass 2: (K, V^T) slots
   static constexpr int E_BYTES = K_BYTES + V_BYTES;
   static constexpr int NS2 = (65536 / E_BYTES) >= 4 ? 4 : 2;
@@ -220,11 +229,11 @@ struct Geo {
   static_assert(EPM * 2 * QS == 32, "scores must split evenly over the MFMAs");
 };
 
-template <int D, int KIND>
+template <int D, int KIND, int NP>
 size_t stats_lds_bytes(int Tn) {
   using G = Geo<D, KIND>;
-  return (size_t)G::NSLOT * G::K_BYTES + (size_t)2 * ((Tn + 1) & ~1) +
-         (size_t)4 * kWavesPerBlock * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
+  return (size_t)(NP == 1 ? kStatsSlots : kPackSlots) * G::K_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
+         (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
 }
 template <int D, int KIND, bool PV8>
 size_t pv_lds_bytes(int Tn) {
@@ -373,49 +382,183 @@ __device__ __forceinline__ void mask_scores(const AttnArgs& p, f32x16 (&sv)[2], 
 // ---------------------------------------------------------------------------
 // Pass 1: running max, row sums, lambda votes; K only
 // ---------------------------------------------------------------------------
-// One workgroup of 4 wavefronts per query block.  The block's listed K tiles
-// stream through a two-slot LDS ring, one barrier per tile.  A wavefront
-// keeps only the scores of the current tile (128 VGPRs), and the LDS of a
+// Live K tiles of query block i (the causal ones end at the diagonal)
+template <bool CAUSAL>
+__device__ __forceinline__ int live_tiles(const AttnArgs& p, int i) {
+  const int last_q = min(p.N, (i + 1) * kBq) - 1;
+  return CAUSAL ? min(p.Tn, last_q / kBk + 1) : p.Tn;
+}
+
+// Dense query blocks (those whose list holds every live tile, so the list
+// is 0, 1, ..., live - 1) of one (b, kv head), heaviest first (block index
+// descending, then query head), in packs of kPackBlocks; the last pack is
+// padded with -1.  One workgroup of 1024 threads per (b, kv head).  It also
+// resets the kv head's pack queue, and workgroup 0 the partial counters.
+template <bool CAUSAL>
+__global__ __launch_bounds__(1024) void build_packs(AttnArgs p) {
+  __shared__ int wsum[16];
+  const int g = blockIdx.x, b = g / p.Hkv, hk = g % p.Hkv;
+  const int G = p.H / p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (g == 0)
+    for (int x = tid; x < kCountSlots * SPARGE_NUM_COUNTERS; x += 1024) p.cnt_part[x] = 0ull;
+  const int n_cand = G * p.Tm;
+  int32_t* out = p.packs + (long long)g * pack_slots(p.H, p.Hkv, p.Tm);
+  int base = 0;
+  for (int c0 = 0; c0 < n_cand; c0 += 1024) {
+    const int c = c0 + tid;
+    bool dense = false;
+    int row = 0;
+    if (c < n_cand) {
+      const int i = p.Tm - 1 - c / G;
+      row = (b * p.H + hk * G + c % G) * p.Tm + i;
+      dense = p.row_cnt[row] == live_tiles<CAUSAL>(p, i);
+    }
+    const unsigned long long bal = __ballot(dense);
+    if (lane == 0) wsum[wave] = (int)__popcll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int x = wsum[w];
+      off += w < wave ? x : 0;
+      tot += x;
+    }
+    if (dense) out[base + off + (int)__popcll(bal & ((1ull << lane) - 1ull))] = row;
+    base += tot;
+    __syncthreads();
+  }
+  const int np = (base + kPackBlocks - 1) / kPackBlocks;
+  for (int x = base + tid; x < np * kPackBlocks; x += 1024) out[x] = -1;
+  if (tid == 0) {
+    p.npack[g] = np;
+    p.pack_next[g] = 0;
+  }
+}
+
+// counters = the sums of the partial counters
+__global__ void sum_counts(AttnArgs p) {
+  const int c = threadIdx.x;
+  if (c >= SPARGE_NUM_COUNTERS) return;
+  unsigned long long t = 0;
+  for (int s = 0; s < kCountSlots; ++s) t += p.cnt_part[s * SPARGE_NUM_COUNTERS + c];
+  p.counts[c] = t;
+}
+
+// NP = 1: one workgroup of 4 wavefronts per query block that lists some but
+// not all of its live tiles (all blocks when p.packs is null).  The block's
+// listed K tiles stream through a two-slot LDS ring, one barrier per tile.
+// A wavefront keeps only the scores of the current tile, and the LDS of a
 // workgroup (two 16 KB slots, the list, the votes) stays under a quarter of
 // the CU's 160 KB, so four workgroups share a CU: four wavefronts per SIMD
 // hide each other's MFMA, exponential and LDS latencies.
-template <int D, int KIND, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+// NP = kPackBlocks: one workgroup of 4 NP wavefronts per pack of dense query
+// blocks of one kv head (build_packs).  Their lists are prefixes of one
+// another, so one K stream serves all of them: the workgroup walks the
+// longest list, and a block whose list has ended only takes its share of the
+// tile loads and the barriers.  With pairs (NP = 2), two workgroups share a
+// CU, four wavefronts per SIMD, and drift against each other as the single
+// workgroups do; one workgroup of four blocks per CU measured slower.
+template <int D, int KIND, bool CAUSAL, int NP>
+__global__ __launch_bounds__(NP * kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void attn_stats(AttnArgs p) {
   using G = Geo<D, KIND>;
   using Acc = typename std::conditional<G::I8, i32x16, f32x16>::type;
-  using LN = Lane<D, KIND, kWavesPerBlock>;
+  constexpr bool PACK = NP > 1;
+  constexpr int NW = NP * kWavesPerBlock;
+  constexpr int NT = NP * kThreads;
+  using LN = Lane<D, KIND, NW>;
+  constexpr int NSLOT = PACK ? kPackSlots : kStatsSlots;
+  constexpr int PD = PACK ? kPackAhead : kStatsAhead;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ unsigned long long red[kWavesPerBlock][4];
+  __shared__ unsigned long long red[NW][4];
+  __shared__ int pick[2];
 
-  int b, h, i;
-  if (!map_block(p, p.Tm, b, h, i)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int member = wave / kWavesPerBlock, wq = wave % kWavesPerBlock;
+  int b, h, i;
+  int UC;                     // this block's list length
+  int UCU;                    // entries the workgroup walks (the longest list)
+  bool active = true;         // the wavefront's pack slot holds a block
+  if constexpr (!PACK) {
+    if (!map_block(p, p.Tm, b, h, i)) return;
+    UC = p.row_cnt[(long long)(b * p.H + h) * p.Tm + i];
+    if (p.packs != nullptr && UC == live_tiles<CAUSAL>(p, i)) return;   // a packed dense block
+    UCU = UC;
+  } else {
+    // Each (b, kv head) hands out its packs in order, heaviest first, from
+    // a counter.  Workgroups go to the 8 XCDs round robin (id % 8), and the
+    // workgroups of XCD x start at kv head x ng / 8 of the ng, moving on to
+    // the next kv heads once those are handed out.  So the workgroups
+    // resident on one XCD hold neighbouring packs (one kv head, close block
+    // indices) that start together and walk the same K tiles through its L2,
+    // different XCDs read different K, and an XCD whose kv heads run out
+    // takes over the rest of the others'.  The grid has a workgroup for
+    // every pack slot; those that find every queue empty return.
+    const int per = pack_slots(p.H, p.Hkv, p.Tm);
+    const int ng = p.B * p.Hkv;
+    if (tid == 0) {
+      const int g0 = (int)((long long)(blockIdx.x % 8u) * ng / 8);
+      int pg = -1, pk = 0;
+      for (int s = 0; s < ng && pg < 0; ++s) {
+        const int gg = (g0 + s) % ng;
+        // the queue head only grows, so an old value never hides packs left
+        if (__hip_atomic_load(p.pack_next + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= p.npack[gg])
+          continue;
+        const int kk = atomicAdd(p.pack_next + gg, 1);
+        if (kk < p.npack[gg]) {
+          pg = gg;
+          pk = kk;
+        }
+      }
+      pick[0] = pg;
+      pick[1] = pk;
+    }
+    __syncthreads();
+    const int g = pick[0], k = pick[1];
+    if (g < 0) return;
+    const int32_t* pr = p.packs + (long long)g * per + (long long)k * NP;
+    // the pack's first block is the heaviest; the slots are wavefront-uniform
+    const int r0 = __builtin_amdgcn_readfirstlane(pr[0]);
+    int r = __builtin_amdgcn_readfirstlane(pr[__builtin_amdgcn_readfirstlane(member)]);
+    active = r >= 0;
+    r = active ? r : r0;
+    i = r % p.Tm;
+    h = (r / p.Tm) % p.H;
+    b = r / p.Tm / p.H;
+    UC = active ? live_tiles<CAUSAL>(p, i) : 0;
+    UCU = live_tiles<CAUSAL>(p, r0 % p.Tm);
+  }
   LN L;
-  L.init(p, b, h, i, wave);
+  L.init(p, b, h, i, wq);
   const long long row_id = L.row_id;
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
-  const int n_live = CAUSAL ? min(p.Tn, last_q / kBk + 1) : p.Tn;
-  const int UC = p.row_cnt[row_id];
+  const int n_live = live_tiles<CAUSAL>(p, i);
 
-  // LDS: K ring | the block's list | votes (2 bits per wavefront and entry) |
-  // int8 K scales of the listed tiles
+  // LDS: K ring | the block's list (NP = 1) | votes (2 bits per wavefront and
+  // entry) | int8 K scales of the walked entries
   const int nwords = (p.Tn + 15) / 16;
   unsigned char* ring = smem;
-  uint16_t* lst = reinterpret_cast<uint16_t*>(smem + G::NSLOT * G::K_BYTES);
-  uint32_t* votes = reinterpret_cast<uint32_t*>(lst + ((p.Tn + 1) & ~1));
-  float* ksc = reinterpret_cast<float*>(votes + kWavesPerBlock * nwords);
+  uint16_t* lst = reinterpret_cast<uint16_t*>(smem + NSLOT * G::K_BYTES);
+  uint32_t* votes = reinterpret_cast<uint32_t*>(smem + NSLOT * G::K_BYTES + (PACK ? 0 : 2 * ((p.Tn + 1) & ~1)));
+  float* ksc = reinterpret_cast<float*>(votes + NW * nwords);
   {
-    const uint16_t* gl = p.row_idx + row_id * p.Tn;
     const float* kscale_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
-    for (int e = tid; e < UC; e += kThreads) {
-      const int j = gl[e];
-      lst[e] = (uint16_t)j;
-      if constexpr (G::I8) ksc[e] = kscale_row[j];
+    if constexpr (PACK) {
+      if constexpr (G::I8)
+        for (int e = tid; e < UCU; e += NT) ksc[e] = kscale_row[e];
+    } else {
+      const uint16_t* gl = p.row_idx + row_id * p.Tn;
+      for (int e = tid; e < UC; e += NT) {
+        const int j = gl[e];
+        lst[e] = (uint16_t)j;
+        if constexpr (G::I8) ksc[e] = kscale_row[j];
+      }
     }
   }
   __syncthreads();
   const uint32_t ring_lds = lds_addr(ring);
+  // tile of entry e (a packed list is 0, 1, 2, ...)
+  auto entry_tile = [&](int e) -> int { return PACK ? e : (int)lst[e]; };
 
   float m_run = kNegInf;      // running max, log2 units
   float l_half = 0.0f;        // this lane half's share of the row sum
@@ -430,7 +573,7 @@ void attn_stats(AttnArgs p) {
   constexpr int KLA = 2;      // k-steps the operand reads run ahead of the MFMAs
   auto tile = [&](int e, auto slot_c, auto&& refill) {
     constexpr int SL = decltype(slot_c)::value;
-    const int j = __builtin_amdgcn_readfirstlane((int)lst[e]);
+    const int j = __builtin_amdgcn_readfirstlane(entry_tile(e));
     float c_scale = p.scale_log2;
     if constexpr (G::I8) c_scale = L.qscale * ksc[e] * p.scale_log2;
     // K operands in k-step order, both 32-key halves per step, so the two
@@ -526,57 +669,72 @@ void attn_stats(AttnArgs p) {
   // at entry e's barrier its tile has landed (the younger loads may still be
   // in flight) and every wavefront is done with entry e-1, whose slot then
   // takes entry e+PD.
-  constexpr int NSLOT = G::NSLOT;
-  constexpr int PD = kStatsAhead;
   static_assert(PD >= 1 && PD < NSLOT, "the refilled slot must be free");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   int jd_v = 0;               // tile of the next refill (read one entry early)
-  for (int t = 0; t < min(PD, UC); ++t)
-    L.issue_k(p, __builtin_amdgcn_readfirstlane((int)lst[t]), ring_lds + (uint32_t)((t % NSLOT) * G::K_BYTES));
-  if (UC > 0) jd_v = lst[min(PD, UC - 1)];
-  // step(e): the barrier, then tile e, which refills entry e-1's slot with e+PD
+  for (int t = 0; t < min(PD, UCU); ++t)
+    L.issue_k(p, __builtin_amdgcn_readfirstlane(entry_tile(t)), ring_lds + (uint32_t)((t % NSLOT) * G::K_BYTES));
+  if (UCU > 0) jd_v = entry_tile(min(PD, UCU - 1));
+  // step(e): the barrier, then tile e, which refills entry e-1's slot with
+  // e+PD; a packed block whose list has ended only refills
   auto step = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    wait_pending<LN::KCW, PD - 1>(min(UC - 1, e + PD - 1) - e);
-    tile(e, slot_c, [&]() {
+    wait_pending<LN::KCW, PD - 1>(min(UCU - 1, e + PD - 1) - e);
+    auto refill = [&]() {
       const int jn = __builtin_amdgcn_readfirstlane(jd_v);
-      if (e + PD < UC) L.issue_k(p, jn, ring_lds + (uint32_t)(((SL + PD) % NSLOT) * G::K_BYTES));
-      jd_v = lst[min(e + PD + 1, UC - 1)];
-    });
+      if (e + PD < UCU) L.issue_k(p, jn, ring_lds + (uint32_t)(((SL + PD) % NSLOT) * G::K_BYTES));
+      jd_v = entry_tile(min(e + PD + 1, UCU - 1));
+    };
+    if (!PACK || e < UC)
+      tile(e, slot_c, refill);
+    else
+      refill();
   };
   int e = 0;
   if constexpr (NSLOT == 2) {
-    for (; e + 2 <= UC; e += 2) {
+    for (; e + 2 <= UCU; e += 2) {
       step(e, I0{});
       step(e + 1, I1{});
     }
-    if (e < UC) step(e, I0{});
-  } else {
-    static_assert(NSLOT == 3, "two or three slots");
-    for (; e + 3 <= UC; e += 3) {
+    if (e < UCU) step(e, I0{});
+  } else if constexpr (NSLOT == 3) {
+    for (; e + 3 <= UCU; e += 3) {
       step(e, I0{});
       step(e + 1, I1{});
       step(e + 2, I2{});
     }
-    if (e < UC) step(e, I0{});
-    if (e + 1 < UC) step(e + 1, I1{});
+    if (e < UCU) step(e, I0{});
+    if (e + 1 < UCU) step(e + 1, I1{});
+  } else {
+    static_assert(NSLOT == 4, "two to four slots");
+    for (; e + 4 <= UCU; e += 4) {
+      step(e, I0{});
+      step(e + 1, I1{});
+      step(e + 2, I2{});
+      step(e + 3, I3{});
+    }
+    if (e < UCU) step(e, I0{});
+    if (e + 1 < UCU) step(e + 1, I1{});
+    if (e + 2 < UCU) step(e + 2, I2{});
   }
   wait_barrier<0>();                       // every vote word is written
 
   // ---- the block's executed-tile list (listed tiles with a voting wavefront) ----
-  if (wave == 0) {
+  const int wv0 = member * kWavesPerBlock;   // the block's first wavefront
+  if (active && wq == 0) {
     uint32_t* ul = p.ulist + row_id * p.Tn;
     int n = 0;
     for (int base = 0; base < UC; base += 64) {
       const int x = base + lane;
       uint32_t m = 0, j = 0;
       if (x < UC) {
-        j = lst[x];
+        j = (uint32_t)entry_tile(x);
 #pragma unroll
         for (int w = 0; w < kWavesPerBlock; ++w) {
-          const uint32_t c = (votes[w * nwords + (x >> 4)] >> (2 * (x & 15))) & 3u;
+          const uint32_t c = (votes[(wv0 + w) * nwords + (x >> 4)] >> (2 * (x & 15))) & 3u;
           m |= (c == 1u ? 1u : 0u) << w;
         }
       }
@@ -588,18 +746,19 @@ void attn_stats(AttnArgs p) {
     if (lane == 0) p.ucnt[row_id] = n;
   }
   const float l_tot = sum_halves(l_half);
-  if (L.qvalid && L.hl == 0) {
+  if (active && L.qvalid && L.hl == 0) {
     const long long r = (long long)(b * p.H + h) * p.N + L.qrow;
     p.row_m[r] = m_run;
     p.row_l[r] = l_tot;
   }
-  if (p.dbg != nullptr) {
+  const int btid = tid % kThreads;          // thread index inside the block's wavefronts
+  if (active && p.dbg != nullptr) {
     uint8_t* drow = p.dbg + row_id * p.Tn * kWavesPerBlock;
-    for (int x = tid; x < UC * kWavesPerBlock; x += kThreads) {
+    for (int x = btid; x < UC * kWavesPerBlock; x += kThreads) {
       const int e2 = x / kWavesPerBlock, w = x % kWavesPerBlock;
       if (i * kBq + w * kRowsPerWave < p.N)
-        drow[(int)lst[e2] * kWavesPerBlock + w] =
-            (uint8_t)((votes[w * nwords + (e2 >> 4)] >> (2 * (e2 & 15))) & 3u);
+        drow[entry_tile(e2) * kWavesPerBlock + w] =
+            (uint8_t)((votes[(wv0 + w) * nwords + (e2 >> 4)] >> (2 * (e2 & 15))) & 3u);
     }
   }
 
@@ -613,24 +772,25 @@ void attn_stats(AttnArgs p) {
     red[wave][3] = n_empty;
   }
   __syncthreads();
-  if (tid == 0 && p.counts != nullptr) {
+  if (active && btid == 0) {
     unsigned long long ex = 0, sk = 0, vo = 0, em = 0;
+    unsigned long long* cp = p.cnt_part + (blockIdx.x % kCountSlots) * SPARGE_NUM_COUNTERS;
     for (int w = 0; w < kWavesPerBlock; ++w) {
       // waves whose 32 rows all lie beyond N hold no group
       if (i * kBq + w * kRowsPerWave >= p.N) continue;
-      ex += red[w][0];
-      sk += red[w][1];
-      vo += red[w][2];
-      em += red[w][3];
+      ex += red[wv0 + w][0];
+      sk += red[wv0 + w][1];
+      vo += red[wv0 + w][2];
+      em += red[wv0 + w][3];
     }
-    atomicAdd(p.counts + SPARGE_CNT_LIVE, (unsigned long long)n_live);
-    atomicAdd(p.counts + SPARGE_CNT_QK_EXEC, (unsigned long long)UC);
-    atomicAdd(p.counts + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - UC));
-    atomicAdd(p.counts + SPARGE_CNT_PV_EXEC, ex);
-    atomicAdd(p.counts + SPARGE_CNT_PV_SKIP, sk);
-    atomicAdd(p.counts + SPARGE_CNT_PV_VOID, vo);
-    atomicAdd(p.counts + SPARGE_CNT_EMPTY_ROWS, em);
-    atomicAdd(p.counts + SPARGE_CNT_ROWS, (unsigned long long)(last_q - i * kBq + 1));
+    atomicAdd(cp + SPARGE_CNT_LIVE, (unsigned long long)n_live);
+    atomicAdd(cp + SPARGE_CNT_QK_EXEC, (unsigned long long)UC);
+    atomicAdd(cp + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - UC));
+    atomicAdd(cp + SPARGE_CNT_PV_EXEC, ex);
+    atomicAdd(cp + SPARGE_CNT_PV_SKIP, sk);
+    atomicAdd(cp + SPARGE_CNT_PV_VOID, vo);
+    atomicAdd(cp + SPARGE_CNT_EMPTY_ROWS, em);
+    atomicAdd(cp + SPARGE_CNT_ROWS, (unsigned long long)(last_q - i * kBq + 1));
   }
 }
 
@@ -976,15 +1136,31 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 template <int D, int KIND, bool CAUSAL, bool PV8>
 hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
   const long long blocks = (long long)a.B * a.H * a.Tm;
-  const size_t lds1 = stats_lds_bytes<D, KIND>(a.Tn);
+  const long long packs = (long long)a.B * a.Hkv * (pack_slots(a.H, a.Hkv, a.Tm) / kPackBlocks);
+  const size_t lds1 = stats_lds_bytes<D, KIND, 1>(a.Tn);
+  const size_t lds1p = stats_lds_bytes<D, KIND, kPackBlocks>(a.Tn);
   const size_t lds2 = pv_lds_bytes<D, KIND, PV8>(a.Tn);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL, 1>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL, kPackBlocks>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1p);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pv<D, KIND, CAUSAL, PV8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), lds1, st, a);
+  // pass 1: the dense query blocks in packs, then the others
+  hipLaunchKernelGGL(build_packs<CAUSAL>, dim3((unsigned)(a.B * a.Hkv)), dim3(1024), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL, kPackBlocks>), dim3((unsigned)packs),
+                     dim3(kPackBlocks * kThreads), lds1p, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL, 1>), dim3((unsigned)blocks), dim3(kThreads), lds1, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sum_counts, dim3(1), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_pv<D, KIND, CAUSAL, PV8>), dim3((unsigned)blocks), dim3(kThreads), lds2, st, a);

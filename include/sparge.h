@@ -173,11 +173,16 @@ int sparge_predict_mask(const void* q, const sparge_tensor* qs, const void* k,
  *   nearest even).
  * mg [B,H,Tm,Tn] uint8 is required.  row_cnt/row_idx (as written by
  *   sparge_predict_mask) are optional: if both are NULL the row lists are
- *   built from mg in the workspace.  Only live tiles are visited.
+ *   built from mg in the workspace.  Only live tiles are visited.  A given
+ *   list must be ascending and hold live tiles only; a row whose count
+ *   equals its number of live tiles is run as the list 0, 1, ..., live - 1.
  * workspace (sparge_workspace_size bytes) is required: it holds a
  *   transposed copy of V, the per-row softmax statistics and executed-tile
- *   lists passed from the first to the second attention kernel, and the row
- *   lists built from mg.
+ *   lists passed from the first to the second attention kernel, the row
+ *   lists built from mg, the grouping of the query blocks that list every
+ *   live tile, and partial counters.  Everything in it is rewritten by each
+ *   call: calls on one stream may share a workspace, calls that can overlap
+ *   may not.
  * lambda < 0 (-inf disables the rule).
  * counts: int64[SPARGE_NUM_COUNTERS], overwritten (see SPARGE_CNT_*).
  * pv_dbg: optional uint8 [B,H,Tm,Tn,SPARGE_BQ/sparge_rows_per_wave()] with

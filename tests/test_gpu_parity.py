@@ -91,6 +91,50 @@ def test_attention_random_mask_edge_rows(dtype, d, causal):
             assert rep["counts"]["pv_skip"] > 0
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_dense_rows_in_packs(causal):
+    """Query blocks that list every live tile share a pass-1 workgroup with up
+    to three other blocks of their kv head.  Two batches, two kv heads of two
+    query heads each, and a ragged N.  The dense blocks per kv head number 7,
+    6, 5 and 9, so packs end padded.  Their i differ, so lists of different
+    lengths share one K stream.  The remaining blocks are random and include
+    an empty one."""
+    B, H, Hkv, N, d = 2, 4, 2, 1100, 64
+    rng = np.random.default_rng(17)
+    Qf = rng.standard_normal((B, H, N, d)) * 1.5
+    Kf = rng.standard_normal((B, Hkv, N, d)) * 1.5
+    Vf = rng.standard_normal((B, Hkv, N, d))
+    q, k, v = (I.to_bits(x, "bf16") for x in (Qf, Kf, Vf))
+    Q, K, V = (O.widen(x, "bf16") for x in (q, k, v))
+    Tm, Tn = O.num_blocks(N, 128), O.num_blocks(N, 64)
+    live = O.tile_live(N, 128, 64, causal)
+    mg_np = (rng.random((B, H, Tm, Tn)) < 0.5) & live
+    n_dense = {(0, 0): 7, (0, 1): 6, (1, 0): 5, (1, 1): 9}
+    empty = (1, 3, 1)
+    chosen = set()
+    for (b, hk), n in n_dense.items():
+        cand = [(b, h, i) for h in (2 * hk, 2 * hk + 1) for i in range(Tm) if (b, h, i) != empty]
+        chosen.update(cand[x] for x in rng.choice(len(cand), size=n, replace=False))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Tm):
+                if (b, h, i) in chosen:
+                    mg_np[b, h, i] = live[i]
+                elif mg_np[b, h, i].sum() == live[i].sum():
+                    mg_np[b, h, i, 0] = False           # only the chosen blocks are dense
+    mg_np[empty] = False
+    dense_rows = sum(int(mg_np[b, h, i].sum() == live[i].sum()) for b in range(B) for h in range(H)
+                     for i in range(Tm))
+    assert dense_rows == sum(n_dense.values())
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    mg = torch.from_numpy(mg_np.astype(np.uint8)).to(DEV)
+    for lam in (-3.0, -math.inf):
+        log(f"[attn-packs] causal={causal} lam={lam} dense blocks={dense_rows}")
+        o, o32, counts, dbg = run_attn(qd, kd, vd, mg, lam, causal)
+        rep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32")
+        log(f"   max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} counts={rep['counts']}")
+
+
 def test_attention_with_predicted_lists_equals_mask_path():
     """The row lists written by predict_mask and the lists built from M_g give
     bit-identical outputs."""
