@@ -71,8 +71,9 @@ constexpr float kFarLog2 = 40.0f;
 // per workgroup and for packs of dense blocks
 constexpr int kStatsSlots = 2;
 constexpr int kStatsAhead = 1;
-constexpr int kPackSlots = 2;
-constexpr int kPackAhead = 1;
+constexpr int kPackSlots = 4;
+constexpr int kPackAhead = 2;
+constexpr int kPackPerBarrier = 2;   // pair kernel: entries per workgroup barrier
 
 // v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
 // in the other, so combining the two gives every lane the pair (l, l ^ 32).
@@ -665,10 +666,13 @@ void attn_stats(AttnArgs p) {
     }
   };
 
-  // A ring of NSLOT K slots, PD tiles loaded ahead, one barrier per entry:
-  // at entry e's barrier its tile has landed (the younger loads may still be
-  // in flight) and every wavefront is done with entry e-1, whose slot then
-  // takes entry e+PD.
+  // A ring of NSLOT K slots, PD tiles loaded ahead, one barrier per TPB
+  // entries.  Single blocks (TPB = 1): at entry e's barrier its tile has
+  // landed (the younger loads may still be in flight) and every wavefront is
+  // done with entry e-1, whose slot then takes entry e+PD.  Pairs (TPB = PD =
+  // 2, four slots): the barrier before entries e, e+1 follows the landing of
+  // both, and every wavefront is done with e-2 and e-1, whose slots then take
+  // e+2 and e+3; between barriers the wavefronts drift by up to a tile.
   static_assert(PD >= 1 && PD < NSLOT, "the refilled slot must be free");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -680,9 +684,12 @@ void attn_stats(AttnArgs p) {
   if (UCU > 0) jd_v = entry_tile(min(PD, UCU - 1));
   // step(e): the barrier, then tile e, which refills entry e-1's slot with
   // e+PD; a packed block whose list has ended only refills
+  constexpr int TPB = PACK ? kPackPerBarrier : 1;
+  static_assert(TPB + PD <= NSLOT && NSLOT % TPB == 0 && PD >= TPB, "a period's slots must be free");
   auto step = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    wait_pending<LN::KCW, PD - 1>(min(UCU - 1, e + PD - 1) - e);
+    if constexpr (SL % TPB == 0)
+      wait_pending<LN::KCW, PD - TPB>(min(UCU - 1, e + PD - 1) - min(UCU - 1, e + TPB - 1));
     auto refill = [&]() {
       const int jn = __builtin_amdgcn_readfirstlane(jd_v);
       if (e + PD < UCU) L.issue_k(p, jn, ring_lds + (uint32_t)(((SL + PD) % NSLOT) * G::K_BYTES));
