@@ -175,11 +175,24 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
   const int c = tid % DCH, slot = tid / DCH;
   const bool bf = a.bf16 != 0;
 
+  // every row this thread reads is requested before any arithmetic, so the
+  // block's 16-32 KB are in flight at once (one load per row at a time left
+  // the kernel at a third of the HBM bandwidth)
+  constexpr int RPT = kBq / SLOTS;           // rows per thread (Q blocks; K blocks use half)
+  u32x4 wr[RPT];
+#pragma unroll
+  for (int it = 0; it < RPT; ++it) {
+    const int r = slot + it * SLOTS;
+    wr[it] = r < nrows ? *reinterpret_cast<const u32x4*>(base + (long long)(r0 + r) * sn + 8 * c)
+                       : u32x4{0, 0, 0, 0};
+  }
   double sx[8], sh[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sx[e] = sh[e] = 0.0;
-  for (int r = slot; r < nrows; r += SLOTS) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(base + (long long)(r0 + r) * sn + 8 * c);
+#pragma unroll
+  for (int it = 0; it < RPT; ++it) {
+    if (slot + it * SLOTS >= nrows) break;
+    const u32x4 w = wr[it];
     double x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = bits_to_double((unsigned short)(w[e >> 1] >> ((e & 1) * 16)), bf);

@@ -38,10 +38,21 @@ __global__ __launch_bounds__(kThreads) void kmean_partial(QuantArgs a, int nchun
   double s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.0;
-  for (int r = r0 + slot; r < r1; r += SLOTS) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(base + (long long)r * a.k_sn + 8 * c);
+  // four rows requested before their sums (the same order of additions)
+  constexpr int U = 4;
+  for (int rb = r0 + slot; rb < r1; rb += U * SLOTS) {
+    u32x4 w[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += widen16((unsigned short)(w[e >> 1] >> ((e & 1) * 16)), bf);
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + u * SLOTS;
+      w[u] = r < r1 ? *reinterpret_cast<const u32x4*>(base + (long long)r * a.k_sn + 8 * c) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (rb + u * SLOTS >= r1) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += widen16((unsigned short)(w[u][e >> 1] >> ((e & 1) * 16)), bf);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[slot][8 * c + e] = s[e];
@@ -102,12 +113,23 @@ __global__ __launch_bounds__(kThreads) void quant_blocks(QuantArgs a) {
   const int nrows = min(a.N, r0 + brows) - r0;
   const bool bf = a.bf16 != 0;
 
+  // the thread's rows, all requested at once and read from HBM once for
+  // both the maximum and the codes
+  constexpr int RPT = kBq / SLOTS;           // rows per thread (Q blocks; K blocks use half)
+  u32x4 wr[RPT];
+#pragma unroll
+  for (int it = 0; it < RPT; ++it) {
+    const int r = slot + it * SLOTS;
+    wr[it] = r < nrows ? *reinterpret_cast<const u32x4*>(base + (long long)(r0 + r) * sn + 8 * c)
+                       : u32x4{0, 0, 0, 0};
+  }
   double amax = 0.0;
-  for (int r = slot; r < nrows; r += SLOTS) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(base + (long long)(r0 + r) * sn + 8 * c);
+#pragma unroll
+  for (int it = 0; it < RPT; ++it) {
+    if (slot + it * SLOTS >= nrows) break;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double x = widen16((unsigned short)(w[e >> 1] >> ((e & 1) * 16)), bf) - mu[8 * c + e];
+      const double x = widen16((unsigned short)(wr[it][e >> 1] >> ((e & 1) * 16)), bf) - mu[8 * c + e];
       amax = fmax(amax, fabs(x));
     }
   }
@@ -119,12 +141,14 @@ __global__ __launch_bounds__(kThreads) void quant_blocks(QuantArgs a) {
   }
   const double m = red[0];
   const double delta = m > 0.0 ? m / 127.0 : 1.0;
-  for (int r = slot; r < nrows; r += SLOTS) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(base + (long long)(r0 + r) * sn + 8 * c);
+#pragma unroll
+  for (int it = 0; it < RPT; ++it) {
+    const int r = slot + it * SLOTS;
+    if (r >= nrows) break;
     unsigned int packed[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double x = widen16((unsigned short)(w[e >> 1] >> ((e & 1) * 16)), bf) - mu[8 * c + e];
+      const double x = widen16((unsigned short)(wr[it][e >> 1] >> ((e & 1) * 16)), bf) - mu[8 * c + e];
       double qv = rint(x / delta);
       qv = fmin(127.0, fmax(-127.0, qv));
       const unsigned int byte = (unsigned int)(unsigned char)(signed char)(int)qv;
