@@ -172,3 +172,23 @@ def test_full_size_gqa_fp8pv():
         over = float(np.max(np.abs(r - g) - rm))
         log(f"   head {h}: blocks {[bl[2] for bl in blocks]}: rel_l1={e_rel:.2e} max over room={over:.2e}")
         assert e_rel <= FP8_REL_L1 and over <= FP8_ABS_SLACK
+
+
+MAX_TN = 4096   # SPARGE_MAX_TN of include/sparge.h
+
+
+@pytest.mark.parametrize("H,H_kv,causal", [(2, 1, True), (1, 1, False)], ids=["causal_gqa", "noncausal"])
+def test_largest_supported_sequence(H, H_kv, causal):
+    """N = 64 * SPARGE_MAX_TN = 262144, the longest sequence the library takes:
+    Tn = 4096 key blocks, so the widest M_g rows and row lists, the largest
+    LDS lists and vote arrays of both attention passes, and (causal) rows
+    whose dense lists walk 4096 tiles.  The llm_32k recipe at that length;
+    mask rows of every head and sampled query blocks against the oracle."""
+    w = I.workload(2, N=64 * MAX_TN, H=H, H_kv=H_kv, causal=causal)
+    assert O.num_blocks(w.N, O.BK) == MAX_TN
+    log(f"[full] largest N: H={w.H} Hkv={w.H_kv} N={w.N} causal={w.causal}")
+    q, k, v = I.make_qkv(w, workers=16)
+    mask, counts, dbg, o16, o32 = _run(w, q, k, v)
+    c = _check_whole(w, mask, counts, o16, o32)
+    log(f"   counts {c}")
+    _check_heads(w, q, k, v, mask, dbg, o32, list(range(w.H)))
