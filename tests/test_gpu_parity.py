@@ -135,6 +135,40 @@ def test_attention_dense_rows_in_packs(causal):
         log(f"   max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} counts={rep['counts']}")
 
 
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 127, 129])
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_short_sequences_whole_path(N, d, causal):
+    """Sequences of one token up to just past one query block: a single
+    ragged key tile, wavefronts whose 32 rows all lie beyond N, one-entry
+    softmax rows in stage 1, and dense blocks paired with padding.  Three
+    query heads on one kv head; stage 1 and stage 2 against the oracle on
+    every block."""
+    H, Hkv = 3, 1
+    rng = np.random.default_rng(1000 + N + d)
+    Qf = rng.standard_normal((1, H, N, d))
+    Kf = rng.standard_normal((1, Hkv, N, d))
+    Vf = rng.standard_normal((1, Hkv, N, d))
+    # one self-similar query head (selective blocks) and self-similar keys (no
+    # forced columns); the other heads' blocks are fix, so dense
+    Qf[0, 1] = Qf[0, 1, :1] + 0.05 * Qf[0, 1]
+    Kf[0, 0] = Kf[0, 0, :1] + 0.05 * Kf[0, 0]
+    q, k, v = (I.to_bits(x, "bf16") for x in (Qf, Kf, Vf))
+    Q, K, V = (O.widen(x, "bf16") for x in (q, k, v))
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    tau, theta, lam = 0.1, 0.9, -1.0
+    log(f"[short] N={N} d={d} causal={causal}")
+    mask = fb.predict_mask(qd, kd, tau, theta, causal)
+    torch.cuda.synchronize()
+    rep = check_mask(mask, Q, K, tau, theta, causal)
+    mg_np = mask.mg.cpu().numpy().astype(bool)
+    o, o32, counts, dbg = run_attn(qd, kd, vd, mask.mg, lam, causal)
+    arep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32")
+    log(f"   mask ambiguous={rep['ambiguous']}; max_abs={arep['max_abs']:.2e} counts={arep['counts']}")
+    assert arep["counts"]["rows"] == H * N
+    if O.num_blocks(N, 64) >= 2:
+        assert arep["counts"]["qk_skip"] > 0            # the selective head keeps only its top tile
+
+
 def test_attention_with_predicted_lists_equals_mask_path():
     """The row lists written by predict_mask and the lists built from M_g give
     bit-identical outputs."""
