@@ -81,6 +81,10 @@ __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ int max_halves_i(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -359,13 +363,19 @@ __device__ __forceinline__ auto mfma_qk(u32x4 a, u32x4 b,
     return mfma16<KIND == 1>(a, b, c);
 }
 
+// whether tile j has dead scores for the wavefront whose rows start at q0:
+// keys beyond N, rows beyond N, or (causal) keys after some row
+template <bool CAUSAL>
+__device__ __forceinline__ bool tile_needs_mask(const AttnArgs& p, int j, int q0) {
+  return (j * kBk + kBk > p.N) || (q0 + kRowsPerWave > p.N) || (CAUSAL && j * kBk + kBk - 1 > q0);
+}
+
 // Dead scores of one tile set to -inf in place: keys beyond N, causal future,
 // rows beyond N (only diagonal and ragged tiles need it).
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_scores(const AttnArgs& p, f32x16 (&sv)[2], int j, int q0, int qrow, bool qvalid,
                                             int hl) {
-  const bool need_mask = (j * kBk + kBk > p.N) || (q0 + kRowsPerWave > p.N) || (CAUSAL && j * kBk + kBk - 1 > q0);
-  if (need_mask) {
+  if (tile_needs_mask<CAUSAL>(p, j, q0)) {
     // key = j*64 + 4*hl + off(t, r) is dead iff key > last, the last visible
     // key of this row (-1 for a row beyond N): off > last - j*64 - 4*hl
     const int last = !qvalid ? -1 : (CAUSAL ? min(qrow, p.N - 1) : p.N - 1);
@@ -602,31 +612,55 @@ void attn_stats(AttnArgs p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * KLA, 0);
-    // the scores as floats, masked in place (the raw accumulator is dead after)
-    f32x16 sv[2];
-    if constexpr (G::I8) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
-    } else {
-      sv[0] = acc[0];
-      sv[1] = acc[1];
-    }
-    mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
     // ---- online softmax (eq. 1) in log2 units; the scale is folded into an FMA ----
-    // row max: 4 independent chains of 8 values starting from -inf, then 4 -> 1
-    float mq[4];
+    // The scores as floats, masked in place, and the row max: 4 independent
+    // chains of 8 values, then 4 -> 1.  An int8 tile without dead scores
+    // takes the max on the int32 sums instead (exact in float: at most
+    // 127 * 127 * 128 < 2^24 in magnitude) and converts the scores only when
+    // its exponentials run.
+    f32x16 sv[2];
+    float mx;
+    bool have_sv = true;
+    if constexpr (G::I8) {
+      if (!tile_needs_mask<CAUSAL>(p, j, L.q0)) {
+        int mi[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int o = 8 * (q & 1);
-      float m = kNegInf;
+        for (int q = 0; q < 4; ++q) {
+          const int o = 8 * (q & 1);
+          int m = max(acc[q >> 1][o], acc[q >> 1][o + 1]);
 #pragma unroll
-      for (int x = 0; x < 8; x += 2) m = fmaxf(fmaxf(m, sv[q >> 1][o + x]), sv[q >> 1][o + x + 1]);
-      mq[q] = m;
+          for (int x = 2; x < 8; x += 2) m = max(max(m, acc[q >> 1][o + x]), acc[q >> 1][o + x + 1]);
+          mi[q] = m;
+        }
+        mx = (float)max_halves_i(max(max(mi[0], mi[1]), max(mi[2], mi[3])));
+        have_sv = false;
+      }
     }
-    float mx = fmaxf(fmaxf(fmaxf(mq[0], mq[1]), mq[2]), mq[3]);
-    mx = max_halves(mx);
+    auto to_float = [&]() {
+      if constexpr (G::I8) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
+      } else {
+        sv[0] = acc[0];
+        sv[1] = acc[1];
+      }
+    };
+    if (have_sv) {
+      to_float();
+      mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
+      float mq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = 8 * (q & 1);
+        float m = kNegInf;
+#pragma unroll
+        for (int x = 0; x < 8; x += 2) m = fmaxf(fmaxf(m, sv[q >> 1][o + x]), sv[q >> 1][o + x + 1]);
+        mq[q] = m;
+      }
+      mx = max_halves(fmaxf(fmaxf(fmaxf(mq[0], mq[1]), mq[2]), mq[3]));
+    }
     const float mloc = mx * c_scale;               // c_scale > 0: max commutes with the scale
     const float m_new = fmaxf(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
@@ -641,6 +675,7 @@ void attn_stats(AttnArgs p) {
     // its exponentials are not evaluated.
     const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
     if (!far) {
+      if (!have_sv) to_float();
       const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
       const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
       float ps[8];
