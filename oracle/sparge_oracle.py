@@ -18,7 +18,7 @@ Pages cited (by title and section):
              Accelerating Any Model Inference", OpenReview author rebuttal:
              replies "Weaknesses1", "Weaknesses3.1" and "Weaknesses3.2".
 
-Readings taken where the pages are open (each is listed in the design doc):
+Readings taken where the pages are open:
 
 * CosSim (eq. 6) is the mean of the b x b cosine-similarity matrix of the
   block's tokens, diagonal included; a zero row has cosine 0 with everything
