@@ -169,6 +169,43 @@ def test_short_sequences_whole_path(N, d, causal):
         assert arep["counts"]["qk_skip"] > 0            # the selective head keeps only its top tile
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_strided_layouts_and_batches(causal):
+    """Q, K, V and O in the [B, N, H, d] layout (token stride H*d, head stride
+    d), two batches, GQA and a ragged N: both stages give the same bits as on
+    contiguous [B, H, N, d] copies, and match the oracle."""
+    w = I.workload(2, N=700, H=4, H_kv=2, B=2, causal=causal)
+    q, k, v = I.make_qkv(w)
+    Q, K, V = (O.widen(x, w.dtype) for x in (q, k, v))
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+
+    def bshd(x):       # the same values with the strides of a [B, N, H, d] tensor
+        return x.transpose(1, 2).contiguous().transpose(1, 2)
+
+    qs, ks, vs = bshd(qd), bshd(kd), bshd(vd)
+    assert qs.stride(2) == w.H * w.d and ks.stride(1) == w.d
+    log(f"[strided] B={w.B} H={w.H} Hkv={w.H_kv} N={w.N} causal={causal}")
+    m1 = fb.predict_mask(qd, kd, w.tau, w.theta, causal)
+    m2 = fb.predict_mask(qs, ks, w.tau, w.theta, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(m1.mg, m2.mg) and torch.equal(m1.row_cnt, m2.row_cnt)
+    assert torch.equal(m1.s_q, m2.s_q) and torch.equal(m1.s_k, m2.s_k)
+    cnt = m1.row_cnt.cpu().numpy()
+    valid = np.arange(m1.row_idx.shape[-1]) < cnt[..., None]
+    assert np.array_equal(m1.row_idx.cpu().numpy()[valid], m2.row_idx.cpu().numpy()[valid])
+    o1, c1, _ = fb.attn(qd, kd, vd, m1, w.lam, causal)
+    out = torch.empty(w.B, w.N, w.H, w.d, dtype=vd.dtype, device=DEV).transpose(1, 2)
+    o2, c2, _ = fb.attn(qs, ks, vs, m2, w.lam, causal, out=out)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == out.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(c1, c2)
+    rep = check_mask(m2, Q, K, w.tau, w.theta, causal)
+    o, o32, counts, dbg = run_attn(qs, ks, vs, m2, w.lam, causal)
+    arep = check_attention(o32, counts, dbg, Q, K, V, m2.mg.cpu().numpy().astype(bool), w.lam, causal, "f32")
+    log(f"   mask ambiguous={rep['ambiguous']}; max_abs={arep['max_abs']:.2e} rel_l1={arep['rel_l1']:.2e} "
+        f"counts={arep['counts']}")
+
+
 def test_attention_with_predicted_lists_equals_mask_path():
     """The row lists written by predict_mask and the lists built from M_g give
     bit-identical outputs."""
