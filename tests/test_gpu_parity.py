@@ -255,13 +255,18 @@ def test_quant_codes_match_oracle():
         log(f"   near-tie codes: q={int(near_q.sum())} k={int(near_k.sum())}")
 
 
-def test_int8_attention_matches_oracle():
-    w, q, k, _ = _case(4, N=1100, H=4, H_kv=2)
-    v = I.make_tensor(w, I.TENSOR_V, dtype="f16")
+@pytest.mark.parametrize("v_dtype,d,causal", [("f16", 128, True), ("bf16", 128, True), ("f16", 64, False),
+                                               ("bf16", 64, True)])
+def test_int8_attention_matches_oracle(v_dtype, d, causal):
+    """int8 Q/K with fp16 or bf16 P~V (both pairs the ABI takes), d 64 and 128,
+    causal and not."""
+    w, q, k, _ = _case(4, N=1100, H=4, H_kv=2, d=d, causal=causal)
+    v = I.make_tensor(w, I.TENSOR_V, dtype=v_dtype)
+    log(f"[int8] V {v_dtype} d={d} causal={causal}")
     Q, K = O.widen(q, w.dtype), O.widen(k, w.dtype)
-    V = O.widen(v, "f16")
+    V = O.widen(v, v_dtype)
     qd, kd = to_dev(q, w.dtype), to_dev(k, w.dtype)
-    vd = to_dev(v, "f16")
+    vd = to_dev(v, v_dtype)
     mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
     q8, k8, qs, ks = fb.quant_qk_int8(qd, kd)
     o, o32, counts, dbg = run_attn(q8, k8, vd, mask, w.lam, w.causal, q_scale=qs, k_scale=ks)
@@ -274,7 +279,7 @@ def test_int8_attention_matches_oracle():
         f"flips={rep['lambda_flips']}")
     # against the unquantised oracle the error is the quantisation error
     o_float, _, _ = O.sparse_attention(Q, K, V, ref_mask, w.lam, w.causal)
-    og = O.widen(to_bits(o), "f16")
+    og = O.widen(to_bits(o), v_dtype)
     log(f"   vs float path: rel_l1={O.rel_l1(o_float, og):.2e}")
 
 
