@@ -199,6 +199,11 @@ def test_strided_layouts_and_batches(causal):
     torch.cuda.synchronize()
     assert o2.data_ptr() == out.data_ptr()
     assert torch.equal(o1, o2) and torch.equal(c1, c2)
+    # int8 quantisation reads the same strides
+    a8 = fb.quant_qk_int8(qd, kd)
+    b8 = fb.quant_qk_int8(qs, ks)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a8, b8))
     rep = check_mask(m2, Q, K, w.tau, w.theta, causal)
     o, o32, counts, dbg = run_attn(qs, ks, vs, m2, w.lam, causal)
     arep = check_attention(o32, counts, dbg, Q, K, V, m2.mg.cpu().numpy().astype(bool), w.lam, causal, "f32")
