@@ -7,7 +7,7 @@ the library is not built, every call raises.
 
 Entry points (names follow the C ABI in include/sparge.h):
   predict_mask(q, k, tau, theta, causal)        -> Mask (mg, row_cnt, row_idx, s_q, s_k)
-  attn(q, k, v, mask_or_mg, lam, causal, ...)   -> (o, counts)
+  attn(q, k, v, mask_or_mg, lam, causal, ...)   -> (o, counts, pv_dbg or None)
   quant_qk_int8(q, k)                           -> (q8, k8, q_scale, k_scale)
   hilbert_index(T, H, W)                        -> (perm, inv) as numpy int32 (host)
   hilbert_permute(x, perm, inverse)             -> y
@@ -142,7 +142,9 @@ _workspaces = {}
 
 
 def workspace(q, k):
-    """A cached device workspace large enough for (q, k) on q's device."""
+    """A cached device workspace large enough for (q, k) on q's device.  Every
+    call rewrites it, so calls on one stream may share it; calls that can run
+    at the same time (other streams) need workspaces of their own (``ws=``)."""
     import torch
     need = lib().sparge_workspace_size(ctypes.byref(desc(q)), ctypes.byref(desc(k)))
     dev = q.device
