@@ -6,7 +6,7 @@
 // formulas" eqs. (1)-(3), the sparse warp online softmax paragraph and
 // "Algorithm 1" (steps 6-17).
 //
-// Two kernels, one pass over the listed tiles each:
+// Two passes over the listed tiles:
 //
 // attn_stats (pass 1) runs the online softmax of eq. (1) over the listed key
 //   blocks of one query block in ascending order: S = Q K^T, the running max
@@ -24,15 +24,17 @@
 //
 // At the workloads this path is built for, about one listed tile in eight
 // has a voting wavefront, so V (half of the bytes of a K/V pass) is read for
-// a small fraction of the tiles, and pass 1 holds only K: a two-slot ring
-// small enough that four workgroups share a CU.
+// a small fraction of the tiles, and pass 1 holds only K in LDS: a two-slot
+// ring for a single block, small enough that four workgroups share a CU, and
+// a four-slot ring for a pair of blocks, two workgroups per CU.
 //
 // Most of pass 1's tiles belong to query blocks whose row of M_g is all
 // ones on the live tiles (the fix blocks of eq. (9) force it), so their
 // lists are 0, 1, ..., live - 1 and prefixes of one another.  build_packs
 // pairs such blocks of one kv head, heaviest first, and one workgroup of 8
 // wavefronts runs a pair on one K stream (half the tile loads); the other
-// blocks keep a workgroup of their own.
+// blocks keep a workgroup of their own in a second launch, and sum_counts
+// adds up the partial counters of both.
 //
 // Layout (CDNA4 first, not the pages' CUDA warp layout):
 // * 4 wavefronts per query block i of 128 rows; wavefront w owns rows
