@@ -211,6 +211,27 @@ def test_strided_layouts_and_batches(causal):
         f"counts={arep['counts']}")
 
 
+def test_repeat_calls_bit_identical():
+    """Pass 1 hands its pairs of dense blocks out from atomic per-kv-head
+    queues, so which workgroup runs which pair changes from call to call;
+    every block's result must not.  The llm_32k recipe at N = 16384 with
+    GQA, where pairs carry most tiles: three calls, each with a workspace of
+    its own, give the same O, counters and decision map bit for bit."""
+    w, q, k, v = _case(2, N=16384, H=8, H_kv=2)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    runs = []
+    for r in range(3):
+        ws = torch.empty_like(fb.workspace(qd, kd))
+        runs.append(fb.attn(qd, kd, vd, mask, w.lam, w.causal, dbg=True, ws=ws))
+    torch.cuda.synchronize()
+    o0, c0, d0 = runs[0]
+    log(f"[repeat] counts {fb.counts_dict(c0)}")
+    assert fb.counts_dict(c0)["qk_exec"] > 0
+    for o, c, d in runs[1:]:
+        assert torch.equal(o, o0) and torch.equal(c, c0) and torch.equal(d, d0)
+
+
 def test_attention_with_predicted_lists_equals_mask_path():
     """The row lists written by predict_mask and the lists built from M_g give
     bit-identical outputs."""
