@@ -198,7 +198,9 @@ def main():
         },
         "mask_pred_share": float(np.mean(pred_ms)) / step_ms,
         "predict_ms": float(np.mean(pred_ms)),
+        "predict_ms_median_min": [float(np.median(pred_ms)), float(np.min(pred_ms))],
         "attn_ms": attn_avg,
+        "attn_ms_median_min": [float(np.median(attn_ms)), float(np.min(attn_ms))],
         "event_step_ms": step_ms,
         "counts": c,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
