@@ -324,6 +324,7 @@ __global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int cap) {
   __shared__ unsigned long long hsum[256];
   __shared__ int s_digit;
   __shared__ uint64_t s_above;
+  __shared__ uint64_t s_key;
   static_assert(kThreads == 256, "one histogram bin per thread");
 
   const long long row = blockIdx.x;               // (b*H + h)*Tm + i
@@ -431,6 +432,17 @@ __global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int cap) {
         __syncthreads();
         prefix = (prefix << 8) | (uint64_t)s_digit;
         above = s_above;
+        // a crossing bin with one entry: that entry is the boundary value
+        // (the entries above it are exactly those summed in `above`), so the
+        // remaining passes would only spell out its key
+        if (pass < 7 && hcnt[s_digit] == 1u) {
+#pragma unroll
+          for (int x = 0; x < MAXE; ++x)
+            if (x < n2 && (key[x] >> shift) == prefix) s_key = key[x];
+          __syncthreads();
+          prefix = s_key;
+          break;
+        }
       }
       // prefix is now the value v of the boundary entry and above the sum of
       // the entries greater than v; among the entries equal to v, the one of
