@@ -141,9 +141,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
   constexpr int DCH = D / 8;                 // lanes per token row
   constexpr int SLOTS = kThreads / DCH;      // token rows in flight
-  __shared__ double red_x[SLOTS][D + 1];
-  __shared__ double red_h[SLOTS][D + 1];
-  __shared__ double red_s[kThreads];
+  constexpr int NWV = kThreads / 64;         // wavefronts
+  __shared__ double red_x[NWV][D];
+  __shared__ double red_h[NWV][D];
+  __shared__ double red_s[NWV];
 
   const long long nq = (long long)a.B * a.H * a.Tm;
   long long blk = blockIdx.x;
@@ -208,18 +209,31 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
       sh[e] += x[e] * inv;
     }
   }
+  // column sums: first over the row slots of a wavefront (lanes that differ
+  // in the bits above the DCH lanes of a row), then over the wavefronts
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    red_x[slot][8 * c + e] = sx[e];
-    red_h[slot][8 * c + e] = sh[e];
+  for (int off = DCH; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sx[e] += __shfl_xor(sx[e], off, 64);
+      sh[e] += __shfl_xor(sh[e], off, 64);
+    }
+  const int wv = tid >> 6, lane = tid & 63;
+  if (lane < DCH) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      red_x[wv][8 * lane + e] = sx[e];
+      red_h[wv][8 * lane + e] = sh[e];
+    }
   }
   __syncthreads();
   double contrib = 0.0;
   if (tid < D) {
     double tx = 0.0, th = 0.0;
-    for (int s = 0; s < SLOTS; ++s) {
-      tx += red_x[s][tid];
-      th += red_h[s][tid];
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      tx += red_x[w][tid];
+      th += red_h[w][tid];
     }
     const double mean = tx / nrows;
     const double mh = th / nrows;
@@ -229,7 +243,14 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
     else
       a.ws.kbar[(((long long)b * a.Hkv + h) * a.Tn + t) * D + tid] = mean;
   }
-  const double s = block_reduce_sum(contrib, red_s);
+  // s = the sum of the D values of contrib (threads >= D hold 0)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) contrib += __shfl_xor(contrib, off, 64);
+  if (lane == 0) red_s[wv] = contrib;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) s += red_s[w];
   if (tid == 0) {
     if (is_q) {
       const long long o = ((long long)b * a.H + h) * a.Tm + t;
