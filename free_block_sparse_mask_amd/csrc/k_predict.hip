@@ -293,14 +293,29 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-  for (int k0 = 0; k0 < a.d; k0 += kGK) {
-    for (int e = tid; e < kGT * kGK; e += kThreads) {
+  // the next d chunk is loaded into registers while this one is used
+  constexpr int PER = kGT * kGK / kThreads;    // elements per thread and operand
+  double pq[PER], pk[PER];
+  auto load_chunk = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * kThreads;
       const int r = e / kGK, kk = e % kGK;
       const int gi = i0 + r, gj = j0 + r;
-      qt[kk][r] = gi < a.Tm ? qb[(long long)gi * a.d + k0 + kk] : 0.0;
-      kt[kk][r] = gj < a.Tn ? kb[(long long)gj * a.d + k0 + kk] : 0.0;
+      pq[u] = gi < a.Tm ? qb[(long long)gi * a.d + k0 + kk] : 0.0;
+      pk[u] = gj < a.Tn ? kb[(long long)gj * a.d + k0 + kk] : 0.0;
+    }
+  };
+  load_chunk(0);
+  for (int k0 = 0; k0 < a.d; k0 += kGK) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * kThreads;
+      qt[e % kGK][e / kGK] = pq[u];
+      kt[e % kGK][e / kGK] = pk[u];
     }
     __syncthreads();
+    if (k0 + kGK < a.d) load_chunk(k0 + kGK);
 #pragma unroll
     for (int kk = 0; kk < kGK; ++kk) {
       // four contiguous rows and four contiguous columns: two 16-byte reads each
