@@ -14,8 +14,9 @@
 //                 per-token norms by a 16-lane shuffle reduction, column sums
 //                 of x and x/|x| combined through LDS; s = |mean x/|x||^2.
 //   shat_gemm     Shat = qbar kbar^T / sqrt(d) per (batch, head) on 64 x 64
-//                 tiles staged through LDS (tiles wholly in the causal future
-//                 are skipped).
+//                 tiles staged through LDS and multiplied on the float64
+//                 matrix cores (tiles wholly in the causal future are
+//                 skipped).
 //   mask_rows     one workgroup per query block row: softmax over the live
 //                 selective columns, the TopCdf cut by a radix select over
 //                 the probabilities with fixed-point sums (no sort), eq. 9
@@ -269,11 +270,18 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kGT = 64;     // tile rows / cols
 constexpr int kGK = 16;     // d chunk
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+// Each wavefront owns a 32 x 32 quarter of the tile as 2 x 2 blocks of the
+// float64 matrix core's 16 x 16 x 4 product.  Operand lane l holds row (or
+// column) l % 16 at k = l / 16; accumulator element r of lane l is row
+// l / 16 + 4 r, column l % 16.  Two 8-byte LDS reads per lane feed 1024
+// FMAs per wavefront, where the 4 x 4 per-thread FMA tile needed 64 bytes of
+// LDS reads per 16 FMAs and waited on LDS bandwidth.
 __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_sqrt_d) {
-  // rows padded by 2 doubles: 16-byte aligned for the operand reads, and the
-  // transposing stores of 16 consecutive k land in distinct banks
-  __shared__ __attribute__((aligned(16))) double qt[kGK][kGT + 2];
-  __shared__ __attribute__((aligned(16))) double kt[kGK][kGT + 2];
+  // k-major tiles: rows padded by 2 doubles so that the transposing stores of
+  // 16 consecutive k land in distinct banks
+  __shared__ double qt[kGK][kGT + 2];
+  __shared__ double kt[kGK][kGT + 2];
   const int it = blockIdx.x, jt = blockIdx.y;
   const int bh = blockIdx.z;
   const int b = bh / a.H, h = bh % a.H;
@@ -287,12 +295,14 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
   const double* qb = a.ws.qbar + ((long long)b * a.H + h) * a.Tm * a.d;
   const double* kb = a.ws.kbar + ((long long)b * a.Hkv + hk) * a.Tn * a.d;
   const int tid = threadIdx.x;
-  const int ti = tid / 16, tj = tid % 16;      // rows 4 ti .. 4 ti + 3, columns 4 tj .. 4 tj + 3
-  double acc[4][4];
+  const int lane = tid & 63, wv = tid >> 6;
+  const int wr = 32 * (wv >> 1), wc = 32 * (wv & 1);    // the wavefront's quarter
+  const int l16 = lane & 15, l4 = lane >> 4;
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
   // the next d chunk is loaded into registers while this one is used
   constexpr int PER = kGT * kGK / kThreads;    // elements per thread and operand
   double pq[PER], pk[PER];
@@ -317,32 +327,29 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
     __syncthreads();
     if (k0 + kGK < a.d) load_chunk(k0 + kGK);
 #pragma unroll
-    for (int kk = 0; kk < kGK; ++kk) {
-      // four contiguous rows and four contiguous columns: two 16-byte reads each
-      const double2 q01 = *reinterpret_cast<const double2*>(&qt[kk][4 * ti]);
-      const double2 q23 = *reinterpret_cast<const double2*>(&qt[kk][4 * ti + 2]);
-      const double2 k01 = *reinterpret_cast<const double2*>(&kt[kk][4 * tj]);
-      const double2 k23 = *reinterpret_cast<const double2*>(&kt[kk][4 * tj + 2]);
-      const double qv[4] = {q01.x, q01.y, q23.x, q23.y};
-      const double kv[4] = {k01.x, k01.y, k23.x, k23.y};
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fma(qv[x], kv[y], acc[x][y]);
+    for (int ks = 0; ks < kGK; ks += 4) {
+      const double qa0 = qt[ks + l4][wr + l16], qa1 = qt[ks + l4][wr + 16 + l16];
+      const double kb0 = kt[ks + l4][wc + l16], kb1 = kt[ks + l4][wc + 16 + l16];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa0, kb0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa0, kb1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa1, kb0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa1, kb1, acc[1][1], 0, 0, 0);
     }
     __syncthreads();
   }
   double* out = a.ws.shat + ((long long)b * a.H + h) * a.Tm * a.Tn;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int gi = i0 + 4 * ti + x;
-    if (gi >= a.Tm) continue;
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int gj = j0 + 4 * tj + y;
-      if (gj < a.Tn) out[(long long)gi * a.Tn + gj] = acc[x][y] * inv_sqrt_d;
+    for (int r = 0; r < 4; ++r) {
+      const int gi = i0 + wr + 16 * x + l4 + 4 * r;
+      if (gi >= a.Tm) continue;
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const int gj = j0 + wc + 16 * y + l16;
+        if (gj < a.Tn) out[(long long)gi * a.Tn + gj] = acc[x][y][r] * inv_sqrt_d;
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
