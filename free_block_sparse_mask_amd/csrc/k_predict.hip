@@ -44,6 +44,43 @@ __device__ __forceinline__ double bits_to_double(unsigned short u, bool bf16) {
   return (double)(float)__builtin_bit_cast(_Float16, u);
 }
 
+// Lane exchanges of a double as two 32-bit halves.  dpp_f64<CTRL> reads the
+// lane that the DPP control names (0xB1: quad lanes 1,0,3,2; 0x4E: quad lanes
+// 2,3,0,1; 0x141: the mirror within each 8 lanes; 0x140: the mirror within
+// each 16 lanes).  These run on the vector ALU instead of the LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Sum over aligned groups of W lanes (W = 2, 4, 8 or 16), every lane of a
+// group left with the same total.  Each step adds the value of a lane in the
+// other half of the current group; after the first two steps all lanes of a
+// quad agree, so a mirror pairs the same halves as an xor would and the sums
+// equal those of an xor butterfly (x ^ 1, x ^ 2, x ^ 4, x ^ 8) bit for bit.
+template <int W>
+__device__ __forceinline__ double group_sum(double v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "group of 2 to 16 lanes");
+  v += dpp_f64<0xB1>(v);
+  if constexpr (W >= 4) v += dpp_f64<0x4E>(v);
+  if constexpr (W >= 8) v += dpp_f64<0x141>(v);
+  if constexpr (W >= 16) v += dpp_f64<0x140>(v);
+  return v;
+}
+
+// x[l] + x[l ^ 32] in every lane (v_permlane32_swap of both halves)
+__device__ __forceinline__ double sum_halves_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+  const double a = __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0]));
+  const double b = __longlong_as_double((long long)(((unsigned long long)hi[1] << 32) | lo[1]));
+  return a + b;
+}
+
 // Workgroup-wide exclusive scan of one int per thread (256 threads).
 __device__ int block_excl_scan_int(int v, int* lds, int& total) {
   const int tid = threadIdx.x;
@@ -201,8 +238,7 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-#pragma unroll
-    for (int off = 1; off < DCH; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    ss = group_sum<DCH>(ss);
     const double inv = ss > 0.0 ? rsqrt_f64(ss) : 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -213,12 +249,17 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
   // column sums: first over the row slots of a wavefront (lanes that differ
   // in the bits above the DCH lanes of a row), then over the wavefronts
 #pragma unroll
-  for (int off = DCH; off < 64; off <<= 1)
+  for (int off = DCH; off < 32; off <<= 1)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sx[e] += __shfl_xor(sx[e], off, 64);
       sh[e] += __shfl_xor(sh[e], off, 64);
     }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sx[e] = sum_halves_f64(sx[e]);
+    sh[e] = sum_halves_f64(sh[e]);
+  }
   const int wv = tid >> 6, lane = tid & 63;
   if (lane < DCH) {
 #pragma unroll
