@@ -81,76 +81,66 @@ __device__ __forceinline__ double sum_halves_f64(double x) {
   return a + b;
 }
 
-// Workgroup-wide exclusive scan of one int per thread (256 threads).
+constexpr int kWaves = kThreads / 64;
+
+// Workgroup-wide exclusive scan of one int per thread (256 threads): a scan
+// within each wavefront, then the wavefront totals through LDS (lds holds at
+// least kWaves ints).
 __device__ int block_excl_scan_int(int v, int* lds, int& total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int t = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += t;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
   }
-  total = lds[kThreads - 1];
-  const int incl = lds[tid];
+  if (lane == 63) lds[w] = incl;
   __syncthreads();
-  return incl - v;
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int x = 0; x < kWaves; ++x) {
+    const int t = lds[x];
+    before += x < w ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + incl - v;
 }
 
-__device__ double block_excl_scan_double(double v, double* lds, double& total) {
+// Workgroup reductions of one value per thread (256 threads), all taken as
+// the tree x[t] op x[t + off] for off = 128, 64, ..., 1: the two steps across
+// wavefronts through LDS, the six within wavefront 0 as an xor butterfly
+// (lane t < off meets lane t + off, the same operands in the same order), so
+// a floating-point sum is the same number whichever way the tree is walked.
+template <typename T, typename Op>
+__device__ __forceinline__ T block_reduce(T v, T* lds, Op op) {
   const int tid = threadIdx.x;
   lds[tid] = v;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const double t = tid >= off ? lds[tid - off] : 0.0;
-    __syncthreads();
-    lds[tid] += t;
-    __syncthreads();
+  if (tid < 64) {
+    T x = op(op(lds[tid], lds[tid + 128]), op(lds[tid + 64], lds[tid + 192]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = op(x, __shfl_xor(x, off, 64));
+    if (tid == 0) lds[0] = x;
   }
-  total = lds[kThreads - 1];
-  const double incl = lds[tid];
   __syncthreads();
-  return incl - v;
+  const T r = lds[0];
+  __syncthreads();
+  return r;
 }
 
 __device__ double block_reduce_max(double v, double* lds) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) lds[tid] = fmax(lds[tid], lds[tid + off]);
-    __syncthreads();
-  }
-  const double r = lds[0];
-  __syncthreads();
-  return r;
+  return block_reduce(v, lds, [](double x, double y) { return fmax(x, y); });
 }
 
 __device__ double block_reduce_sum(double v, double* lds) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) lds[tid] += lds[tid + off];
-    __syncthreads();
-  }
-  const double r = lds[0];
-  __syncthreads();
-  return r;
+  return block_reduce(v, lds, [](double x, double y) { return x + y; });
 }
 
 __device__ uint64_t block_reduce_u64(uint64_t v, unsigned long long* lds) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) lds[tid] += lds[tid + off];
-    __syncthreads();
-  }
-  const uint64_t r = lds[0];
-  __syncthreads();
-  return r;
+  return block_reduce((unsigned long long)v, lds,
+                      [](unsigned long long x, unsigned long long y) { return x + y; });
 }
 
 // Writes the M_g row (Tn bytes) and the ascending list of its ones.
