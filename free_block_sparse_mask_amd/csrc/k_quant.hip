@@ -8,7 +8,9 @@
 //
 // All arithmetic that decides a code is float64: the K mean, K - mean, the
 // block maximum, x / delta and the rounding (ties to even), so every code is
-// decided exactly as the float64 definition decides it.  HBM-bound kernels:
+// decided exactly as the float64 definition decides it (a product with
+// 1 / delta stands in for the division wherever it provably rounds alike).
+// HBM-bound kernels:
 //   kmean_partial  column sums of K over chunks of 1024 tokens
 //   kmean_final    mean over the chunks, in chunk order (deterministic)
 //   quant_blocks   one workgroup per Q or K block: max |x|, then the codes
@@ -77,7 +79,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void quant_blocks(QuantArgs a) {
   constexpr int DCH = D / 8;
   constexpr int SLOTS = kThreads / DCH;
-  __shared__ double red[kThreads];
+  __shared__ double red[kThreads / 64];
   __shared__ double mu[D];
   const long long nq = (long long)a.B * a.H * a.Tm;
   long long blk = blockIdx.x;
@@ -133,14 +135,22 @@ __global__ __launch_bounds__(kThreads) void quant_blocks(QuantArgs a) {
       amax = fmax(amax, fabs(x));
     }
   }
-  red[tid] = amax;
+  // the maximum is the same in any order: within each wavefront, then over
+  // the four
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmax(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmax(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const double m = red[0];
+  double m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = fmax(m, red[w]);
   const double delta = m > 0.0 ? m / 127.0 : 1.0;
+  // The code is rint of the rounded quotient x / delta, and |x / delta| <= 127.
+  // y = x * (1 / delta) lies within 2^-44 of that quotient (two roundings of
+  // relative size 2^-53 on a value below 2^7, plus the quotient's own), so
+  // both round to the same integer unless y is within that distance of a
+  // half-integer; inside a guard band of 2^-40 the division itself decides.
+  const double rdelta = 1.0 / delta;
 #pragma unroll
   for (int it = 0; it < RPT; ++it) {
     const int r = slot + it * SLOTS;
@@ -149,7 +159,9 @@ __global__ __launch_bounds__(kThreads) void quant_blocks(QuantArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const double x = widen16((unsigned short)(wr[it][e >> 1] >> ((e & 1) * 16)), bf) - mu[8 * c + e];
-      double qv = rint(x / delta);
+      const double y = x * rdelta;
+      double qv = rint(y);
+      if (fabs(fabs(y - trunc(y)) - 0.5) < 0x1p-40) qv = rint(x / delta);
       qv = fmin(127.0, fmax(-127.0, qv));
       const unsigned int byte = (unsigned int)(unsigned char)(signed char)(int)qv;
       packed[e >> 2] |= byte << ((e & 3) * 8);

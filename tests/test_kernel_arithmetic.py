@@ -1,0 +1,74 @@
+"""CPU replays of float64 shortcuts the HIP kernels take, each checked against
+the plain definition it stands in for.  numpy's float64 operations are IEEE
+correctly rounded, as are the kernel's v_mul_f64 and its double division, so
+the replay takes the same decisions as the kernel."""
+import numpy as np
+
+
+def codes_by_division(x, delta):
+    """The definition: rint of the rounded quotient, clamped to [-127, 127]."""
+    return np.clip(np.rint(x / delta), -127.0, 127.0)
+
+
+def codes_by_product(x, delta):
+    """The quantisation kernel's route: x * (1 / delta), with the division
+    itself inside a 2^-40 band around half-integers."""
+    y = x * (1.0 / delta)
+    q = np.rint(y)
+    near = np.abs(np.abs(y - np.trunc(y)) - 0.5) < 2.0 ** -40
+    q[near] = np.rint(x[near] / delta)
+    return np.clip(q, -127.0, 127.0), int(near.sum())
+
+
+def to_bf16(a):
+    """Round float32 values to bfloat16 (ties to even) and widen back."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def test_product_codes_equal_division_codes_on_blocks():
+    rng = np.random.default_rng(20261203)
+    for trial in range(200):
+        scale = 10.0 ** rng.uniform(-6, 4)
+        x = to_bf16(rng.standard_normal(128 * 128) * scale)
+        if trial % 2:                       # K blocks: minus a float64 channel mean
+            x = x - to_bf16(rng.standard_normal(128) * scale).repeat(128)
+        m = np.max(np.abs(x))
+        delta = m / 127.0 if m > 0 else 1.0
+        q, _ = codes_by_product(x, delta)
+        assert np.array_equal(q, codes_by_division(x, delta))
+
+
+def test_product_codes_equal_division_codes_at_near_ties():
+    """x placed on and a few ulps around (k + 1/2) delta for every k, where
+    the product and the quotient can fall on different sides of the tie."""
+    rng = np.random.default_rng(7)
+    fallbacks = 0
+    for _ in range(50):
+        m = 10.0 ** rng.uniform(-5, 5) * rng.uniform(1, 2)
+        delta = m / 127.0
+        ties = (np.arange(-127, 127) + 0.5) * delta
+        xs = [ties]
+        for steps in range(1, 6):
+            up, dn = ties.copy(), ties.copy()
+            for _ in range(steps):
+                up = np.nextafter(up, np.inf)
+                dn = np.nextafter(dn, -np.inf)
+            xs += [up, dn]
+        x = np.clip(np.concatenate(xs), -m, m)
+        q, n = codes_by_product(x, delta)
+        fallbacks += n
+        assert np.array_equal(q, codes_by_division(x, delta))
+    # the band is where the division is needed, and it was exercised
+    assert fallbacks > 0
+
+
+def test_guard_band_is_wide_enough():
+    """|x * (1/delta) - fl(x / delta)| stays far inside the 2^-40 band for
+    |x / delta| <= 127."""
+    rng = np.random.default_rng(11)
+    delta = 10.0 ** rng.uniform(-8, 8, 20000)
+    x = rng.uniform(-127, 127, 20000) * delta
+    gap = np.abs(x * (1.0 / delta) - x / delta)
+    assert gap.max() < 2.0 ** -44
