@@ -115,6 +115,7 @@ __device__ int block_excl_scan_int(int v, int* lds, int& total) {
 // a floating-point sum is the same number whichever way the tree is walked.
 template <typename T, typename Op>
 __device__ __forceinline__ T block_reduce(T v, T* lds, Op op) {
+  static_assert(kThreads == 256, "the two cross-wavefront steps assume four wavefronts");
   const int tid = threadIdx.x;
   lds[tid] = v;
   __syncthreads();
@@ -410,11 +411,11 @@ __global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int cap) {
   const int last_q = min(a.N, (i + 1) * kBq) - 1;
   const int n_live = a.causal ? min(a.Tn, last_q / kBk + 1) : a.Tn;
   const bool fix_q = a.ws.sq[row] < a.theta;
-  const double* skr = a.ws.sk + ((long long)b * a.Hkv + hk) * a.Tn;
-  for (int j = tid; j < a.Tn; j += kThreads) flag[j] = (skr[j] < a.theta) ? 1 : 0;
-  __syncthreads();
-
+  // a fix row keeps every live tile (eq. 9) and needs no column flags
   if (!fix_q) {
+    const double* skr = a.ws.sk + ((long long)b * a.Hkv + hk) * a.Tn;
+    for (int j = tid; j < a.Tn; j += kThreads) flag[j] = (skr[j] < a.theta) ? 1 : 0;
+    __syncthreads();
     // gather the live selective columns in ascending j
     const int per = (n_live + kThreads - 1) / kThreads;
     const int lo = min(n_live, tid * per), hi = min(n_live, lo + per);
