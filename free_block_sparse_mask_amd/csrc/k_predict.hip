@@ -11,8 +11,9 @@
 // compressed map, its softmax and the TopCdf prefix sums) is computed in
 // float64.  Three kernels:
 //   pool_cossim   one workgroup per Q or K block: coalesced 16-byte loads,
-//                 per-token norms by a 16-lane shuffle reduction, column sums
-//                 of x and x/|x| combined through LDS; s = |mean x/|x||^2.
+//                 per-token norms summed over their 16 lanes with DPP moves,
+//                 column sums of x and x/|x| combined across lanes and then
+//                 the four wavefronts through LDS; s = |mean x/|x||^2.
 //   shat_gemm     Shat = qbar kbar^T / sqrt(d) per (batch, head) on 64 x 64
 //                 tiles staged through LDS and multiplied on the float64
 //                 matrix cores (tiles wholly in the causal future are
@@ -20,7 +21,8 @@
 //   mask_rows     one workgroup per query block row: softmax over the live
 //                 selective columns, the TopCdf cut by a radix select over
 //                 the probabilities with fixed-point sums (no sort), eq. 9
-//                 forcing, then the M_g row and its compacted ascending list.
+//                 forcing, then the M_g row and its compacted ascending list
+//                 (a fix row skips straight to its list of live tiles).
 #include "common.hpp"
 
 namespace sparge {
