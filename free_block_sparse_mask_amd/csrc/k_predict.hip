@@ -302,25 +302,30 @@ __global__ __launch_bounds__(kThreads) void pool_cossim(PredictArgs a) {
 // ---------------------------------------------------------------------------
 // shat_gemm: Shat = qbar kbar^T / sqrt(d) (eq. 7 before the -inf columns)
 // ---------------------------------------------------------------------------
-constexpr int kGT = 64;     // tile rows / cols
+constexpr int kGT = 64;     // tile rows (query blocks)
+constexpr int kGTJ = 128;   // tile columns (key blocks)
 constexpr int kGK = 16;     // d chunk
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-// Each wavefront owns a 32 x 32 quarter of the tile as 2 x 2 blocks of the
-// float64 matrix core's 16 x 16 x 4 product.  Operand lane l holds row (or
-// column) l % 16 at k = l / 16; accumulator element r of lane l is row
-// l / 16 + 4 r, column l % 16.  Two 8-byte LDS reads per lane feed 1024
-// FMAs per wavefront, where the 4 x 4 per-thread FMA tile needed 64 bytes of
-// LDS reads per 16 FMAs and waited on LDS bandwidth.
-__global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_sqrt_d) {
+// Each wavefront owns 32 rows x kGTJ/2 columns of the tile as 2 x NJ blocks of
+// the float64 matrix core's 16 x 16 x 4 product.  Operand lane l holds row
+// (or column) l % 16 at k = l / 16; accumulator element r of lane l is row
+// l / 16 + 4 r, column l % 16.  Two 8-byte LDS reads per lane feed 1024 FMAs
+// per wavefront, where a 4 x 4 per-thread FMA tile needed 64 bytes of LDS
+// reads per 16 FMAs and waited on LDS bandwidth; the wide tile gives each
+// chunk's loads and barriers twice the MFMA work to hide behind.
+// three wavefronts per SIMD (144 VGPRs, no spills) against two by default
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void shat_gemm(PredictArgs a, double inv_sqrt_d) {
+  constexpr int NJ = kGTJ / 32;                // 16-column blocks per wavefront
   // k-major tiles: rows padded by 2 doubles so that the transposing stores of
   // 16 consecutive k land in distinct banks
   __shared__ double qt[kGK][kGT + 2];
-  __shared__ double kt[kGK][kGT + 2];
+  __shared__ double kt[kGK][kGTJ + 2];
   const int it = blockIdx.x, jt = blockIdx.y;
   const int bh = blockIdx.z;
   const int b = bh / a.H, h = bh % a.H;
   const int hk = h / (a.H / a.Hkv);
-  const int i0 = it * kGT, j0 = jt * kGT;
+  const int i0 = it * kGT, j0 = jt * kGTJ;
   if (a.causal) {
     const int i_last = min(a.Tm - 1, i0 + kGT - 1);
     const int last_q = min(a.N, (i_last + 1) * kBq) - 1;
@@ -330,32 +335,40 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
   const double* kb = a.ws.kbar + ((long long)b * a.Hkv + hk) * a.Tn * a.d;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int wr = 32 * (wv >> 1), wc = 32 * (wv & 1);    // the wavefront's quarter
+  const int wr = 32 * (wv >> 1), wc = (kGTJ / 2) * (wv & 1);    // the wavefront's quarter
   const int l16 = lane & 15, l4 = lane >> 4;
-  f64x4 acc[2][2];
+  f64x4 acc[2][NJ];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int y = 0; y < NJ; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
   // the next d chunk is loaded into registers while this one is used
-  constexpr int PER = kGT * kGK / kThreads;    // elements per thread and operand
-  double pq[PER], pk[PER];
+  constexpr int PQ = kGT * kGK / kThreads, PK = kGTJ * kGK / kThreads;
+  double pq[PQ], pk[PK];
   auto load_chunk = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
+    for (int u = 0; u < PQ; ++u) {
       const int e = tid + u * kThreads;
-      const int r = e / kGK, kk = e % kGK;
-      const int gi = i0 + r, gj = j0 + r;
-      pq[u] = gi < a.Tm ? qb[(long long)gi * a.d + k0 + kk] : 0.0;
-      pk[u] = gj < a.Tn ? kb[(long long)gj * a.d + k0 + kk] : 0.0;
+      const int gi = i0 + e / kGK;
+      pq[u] = gi < a.Tm ? qb[(long long)gi * a.d + k0 + e % kGK] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int e = tid + u * kThreads;
+      const int gj = j0 + e / kGK;
+      pk[u] = gj < a.Tn ? kb[(long long)gj * a.d + k0 + e % kGK] : 0.0;
     }
   };
   load_chunk(0);
   for (int k0 = 0; k0 < a.d; k0 += kGK) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
+    for (int u = 0; u < PQ; ++u) {
       const int e = tid + u * kThreads;
       qt[e % kGK][e / kGK] = pq[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int e = tid + u * kThreads;
       kt[e % kGK][e / kGK] = pk[u];
     }
     __syncthreads();
@@ -363,11 +376,12 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
 #pragma unroll
     for (int ks = 0; ks < kGK; ks += 4) {
       const double qa0 = qt[ks + l4][wr + l16], qa1 = qt[ks + l4][wr + 16 + l16];
-      const double kb0 = kt[ks + l4][wc + l16], kb1 = kt[ks + l4][wc + 16 + l16];
-      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa0, kb0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa0, kb1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa1, kb0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa1, kb1, acc[1][1], 0, 0, 0);
+#pragma unroll
+      for (int y = 0; y < NJ; ++y) {
+        const double kby = kt[ks + l4][wc + 16 * y + l16];
+        acc[0][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa0, kby, acc[0][y], 0, 0, 0);
+        acc[1][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa1, kby, acc[1][y], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void shat_gemm(PredictArgs a, double inv_
       const int gi = i0 + wr + 16 * x + l4 + 4 * r;
       if (gi >= a.Tm) continue;
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
+      for (int y = 0; y < NJ; ++y) {
         const int gj = j0 + wc + 16 * y + l16;
         if (gj < a.Tn) out[(long long)gi * a.Tn + gj] = acc[x][y][r] * inv_sqrt_d;
       }
@@ -580,7 +594,7 @@ hipError_t launch_predict(const PredictArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(pool_cossim<128>, dim3((unsigned)pool_blocks), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g((unsigned)ceil_div(a.Tm, kGT), (unsigned)ceil_div(a.Tn, kGT), (unsigned)(a.B * a.H));
+  dim3 g((unsigned)ceil_div(a.Tm, kGT), (unsigned)ceil_div(a.Tn, kGTJ), (unsigned)(a.B * a.H));
   hipLaunchKernelGGL(shat_gemm, g, dim3(kThreads), 0, st, a, 1.0 / sqrt((double)a.d));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
