@@ -216,10 +216,21 @@ def test_repeat_calls_bit_identical():
     queues, so which workgroup runs which pair changes from call to call;
     every block's result must not.  The llm_32k recipe at N = 16384 with
     GQA, where pairs carry most tiles: three calls, each with a workspace of
-    its own, give the same O, counters and decision map bit for bit."""
+    its own, give the same O, counters and decision map bit for bit.  Stage
+    1 likewise: its only atomics are integer histogram counts and
+    fixed-point sums, so three predictions agree in every output."""
     w, q, k, v = _case(2, N=16384, H=8, H_kv=2)
     qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
-    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    masks = [fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=torch.empty_like(fb.workspace(qd, kd)))
+             for _ in range(3)]
+    torch.cuda.synchronize()
+    mask = masks[0]
+    # a row list holds row_cnt entries; the rest of its storage is unwritten
+    listed = torch.arange(mask.row_idx.shape[-1], device=qd.device) < mask.row_cnt[..., None].long()
+    for m in masks[1:]:
+        for f in ("mg", "row_cnt", "s_q", "s_k"):
+            assert torch.equal(getattr(m, f), getattr(mask, f)), f
+        assert torch.equal(m.row_idx[listed], mask.row_idx[listed])
     runs = []
     for r in range(3):
         ws = torch.empty_like(fb.workspace(qd, kd))
