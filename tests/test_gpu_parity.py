@@ -292,6 +292,32 @@ def test_quant_codes_match_oracle():
         log(f"   near-tie codes: q={int(near_q.sum())} k={int(near_k.sum())}")
 
 
+def test_quant_codes_at_rounding_ties():
+    """An fp16 query block whose maximum is 60000 (delta = 60000 / 127) and
+    whose other entries are the fp16 values nearest (k + 1/2) delta, k = -127
+    .. 126: x / delta falls on or next to half-integers, and for some entries
+    x * (1 / delta) rounds to a different integer than the quotient does.
+    The codes must be those of the rounded quotient, entry for entry; no
+    entry is excluded here."""
+    d, N, m = 64, 128, 60000.0
+    delta = m / 127.0
+    near = ((np.arange(-127, 127) + 0.5) * delta).astype(np.float16).astype(np.float64)
+    vals = np.resize(near, N * d)
+    vals[0] = m
+    Qf = vals.reshape(1, 1, N, d)
+    qbits = Qf.astype(np.float16).view(np.uint16)
+    assert np.array_equal(qbits.view(np.float16).astype(np.float64), Qf)   # exact in fp16
+    # the case separates the two routes: a product alone would get some codes wrong
+    assert np.any(np.rint(near * (1.0 / delta)) != np.rint(near / delta))
+    kbits = np.random.default_rng(5).standard_normal((1, 1, N, d)).astype(np.float16).view(np.uint16)
+    q8, k8, qs, ks = fb.quant_qk_int8(to_dev(qbits, "f16"), to_dev(kbits, "f16"))
+    torch.cuda.synchronize()
+    ref = O.quantize_qk(Qf, O.widen(kbits, "f16"))
+    assert np.array_equal(q8.cpu().numpy().astype(np.float64), ref["q_codes"])
+    assert np.array_equal(qs.cpu().numpy(), ref["q_scale"].astype(np.float32))
+    log(f"[quant ties] {int(np.sum(ref['q_tie_dist'] < 1e-9))} entries within 1e-9 of a tie, codes equal")
+
+
 @pytest.mark.parametrize("v_dtype,d,causal", [("f16", 128, True), ("bf16", 128, True), ("f16", 64, False),
                                                ("bf16", 64, True)])
 def test_int8_attention_matches_oracle(v_dtype, d, causal):
