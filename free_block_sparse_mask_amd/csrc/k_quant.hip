@@ -71,6 +71,9 @@ __global__ void kmean_final(QuantArgs a, int nchunks) {
   const int c = threadIdx.x;
   if (c >= a.d) return;
   double t = 0.0;
+  // the partial sums are added in chunk order; unrolling only lets their
+  // loads be in flight together
+#pragma unroll 16
   for (int k = 0; k < nchunks; ++k) t += a.ws.ksum_part[((long long)bh * nchunks + k) * a.d + c];
   a.ws.kmean[(long long)bh * a.d + c] = t / (double)a.N;
 }
