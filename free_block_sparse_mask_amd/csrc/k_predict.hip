@@ -430,6 +430,7 @@ __global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int cap) {
   // a fix row keeps every live tile (eq. 9) and needs no column flags
   if (!fix_q) {
     const double* skr = a.ws.sk + ((long long)b * a.Hkv + hk) * a.Tn;
+#pragma unroll 8
     for (int j = tid; j < a.Tn; j += kThreads) flag[j] = (skr[j] < a.theta) ? 1 : 0;
     __syncthreads();
     // gather the live selective columns in ascending j
@@ -440,12 +441,17 @@ __global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int cap) {
     int m;
     int pos = block_excl_scan_int(mine, ired, m);
     const double* srow = a.ws.shat + row * a.Tn;
-    for (int j = lo; j < hi; ++j)
+    // every j < hi is a column of the row, so its value is loaded before the
+    // test and the unrolled loads overlap
+#pragma unroll 8
+    for (int j = lo; j < hi; ++j) {
+      const double sv = srow[j];
       if (!(flag[j] & 1)) {
-        pv[pos] = srow[j];
+        pv[pos] = sv;
         pj[pos] = j;
         ++pos;
       }
+    }
     __syncthreads();
     if (m > 0) {
       // softmax over the m finite entries (eq. 8's P^[i])
