@@ -72,3 +72,54 @@ def test_guard_band_is_wide_enough():
     x = rng.uniform(-127, 127, 20000) * delta
     gap = np.abs(x * (1.0 / delta) - x / delta)
     assert gap.max() < 2.0 ** -44
+
+
+def dpp_source(ctrl):
+    """Source lane of each of 64 lanes for the DPP controls the pooling
+    kernel uses (the moves stay inside 16-lane rows)."""
+    lanes = np.arange(64)
+    base, i = lanes & ~15, lanes & 15
+    if ctrl == "quad_1032":
+        return base + (i & ~3) + np.array([1, 0, 3, 2])[i & 3]
+    if ctrl == "quad_2301":
+        return base + (i & ~3) + np.array([2, 3, 0, 1])[i & 3]
+    if ctrl == "half_mirror":
+        return base + (i & ~7) + (7 - (i & 7))
+    if ctrl == "mirror":
+        return base + (15 - i)
+    raise ValueError(ctrl)
+
+
+def test_dpp_group_sums_equal_xor_butterfly():
+    """The pooling kernel sums each token's squares over groups of 8 or 16
+    lanes with DPP moves (quad permutations, then mirrors) where an xor
+    butterfly used to run; both add the same operands in the same order, so
+    the float64 sums are identical bit for bit."""
+    rng = np.random.default_rng(3)
+    steps = {8: ["quad_1032", "quad_2301", "half_mirror"], 16: ["quad_1032", "quad_2301", "half_mirror", "mirror"]}
+    for width, ctrls in steps.items():
+        for _ in range(200):
+            x = rng.standard_normal(64) * 10.0 ** rng.uniform(-8, 8, 64)
+            dpp = x.copy()
+            for c in ctrls:
+                dpp = dpp + dpp[dpp_source(c)]
+            xor = x.copy()
+            off = 1
+            while off < width:
+                xor = xor + xor[np.arange(64) ^ off]
+                off <<= 1
+            assert np.array_equal(dpp, xor)
+            # every lane of a group holds that group's total
+            groups = dpp.reshape(-1, width)
+            assert np.all(groups == groups[:, :1])
+
+
+def test_half_wave_swap_sum_equals_xor_32():
+    """x[l % 32] + x[32 + l % 32] (the two results of v_permlane32_swap) is
+    x[l] + x[l ^ 32] in every lane."""
+    rng = np.random.default_rng(4)
+    for _ in range(100):
+        x = rng.standard_normal(64) * 10.0 ** rng.uniform(-8, 8, 64)
+        lanes = np.arange(64)
+        swap = x[lanes % 32] + x[32 + lanes % 32]
+        assert np.array_equal(swap, x + x[lanes ^ 32])
