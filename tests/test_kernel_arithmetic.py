@@ -123,3 +123,24 @@ def test_half_wave_swap_sum_equals_xor_32():
         lanes = np.arange(64)
         swap = x[lanes % 32] + x[32 + lanes % 32]
         assert np.array_equal(swap, x + x[lanes ^ 32])
+
+
+def test_block_sum_tree_equals_halving_loop():
+    """mask_rows sums 256 doubles as (v[t] + v[t+128]) + (v[t+64] + v[t+192])
+    for t < 64, then an xor butterfly over those 64 lanes, and takes lane 0.
+    That is the tree of the LDS loop x[t] += x[t + off], off = 128 .. 1, so
+    the softmax denominator is the same number bit for bit."""
+    rng = np.random.default_rng(6)
+    for _ in range(300):
+        v = rng.standard_normal(256) * 10.0 ** rng.uniform(-10, 10, 256)
+        x = v.copy()
+        off = 128
+        while off:
+            x[:off] = x[:off] + x[off:2 * off]
+            off >>= 1
+        y = (v[:64] + v[128:192]) + (v[64:128] + v[192:256])
+        off = 32
+        while off:
+            y = y + y[np.arange(64) ^ off]
+            off >>= 1
+        assert y[0] == x[0]
