@@ -77,6 +77,19 @@ int check_qk_shapes(const sparge_tensor* q, const sparge_tensor* k) {
 
 bool empty_problem(const sparge_tensor* q) { return q->B == 0 || q->H == 0 || q->N == 0; }
 
+// Byte range [lo, hi) a non-empty tensor's elements span (strides are >= 0).
+void byte_span(const void* base, const sparge_tensor* t, int esize, uintptr_t& lo, uintptr_t& hi) {
+  lo = (uintptr_t)base;
+  hi = lo + (uintptr_t)(((t->B - 1) * t->sb + (t->H - 1) * t->sh + (t->N - 1) * t->sn + t->d) * esize);
+}
+
+bool spans_overlap(const void* x, const sparge_tensor* xs, const void* y, const sparge_tensor* ys, int esize) {
+  uintptr_t xl, xh, yl, yh;
+  byte_span(x, xs, esize, xl, xh);
+  byte_span(y, ys, esize, yl, yh);
+  return xl < yh && yl < xh;
+}
+
 }  // namespace
 
 Workspace carve_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d) {
@@ -207,9 +220,10 @@ int sparge_hilbert_permute(const void* x, const sparge_tensor* xs, void* y, cons
   if (xs->N >= (1LL << 31)) return fail(SPARGE_EUNSUPPORTED, "N too large");
   if (inverse != 0 && inverse != 1) return fail(SPARGE_EINVAL, "inverse must be 0 or 1");
   if (empty_problem(xs)) return ok();
-  if (x == nullptr || y == nullptr || perm == nullptr) return fail(SPARGE_EINVAL, "null pointer");
+  if (x == nullptr || y == nullptr) return fail(SPARGE_EINVAL, "null pointer");
   if (!aligned16(x) || !aligned16(y)) return fail(SPARGE_EINVAL, "x and y must be 16-byte aligned");
-  if (x == y) return fail(SPARGE_EINVAL, "x and y must not overlap");
+  if (spans_overlap(x, xs, y, ys, es)) return fail(SPARGE_EINVAL, "x and y must not overlap");
+  if (perm == nullptr) return fail(SPARGE_EINVAL, "null perm");
   PermuteArgs a{};
   a.x = x;
   a.y = y;

@@ -10,7 +10,8 @@
 //
 // A pure HBM copy: each lane moves 16 bytes; the lanes of one token row are
 // consecutive, so every row read and write is one contiguous segment.  The
-// permutation index is read once per row.
+// permutation index is read once per row; an index outside [0, N) (a stale
+// or malformed order) moves nothing, so it cannot reach outside x or y.
 #include "common.hpp"
 
 namespace sparge {
@@ -26,8 +27,10 @@ __global__ __launch_bounds__(kThreads) void permute_rows(PermuteArgs a, int lane
   const int p = (int)(row % a.N);
   const long long bh = row / a.N;
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-  const int src = a.inverse ? p : a.perm[p];
-  const int dst = a.inverse ? a.perm[p] : p;
+  const int q = a.perm[p];
+  if ((unsigned)q >= (unsigned)a.N) return;
+  const int src = a.inverse ? p : q;
+  const int dst = a.inverse ? q : p;
   const unsigned char* xs = static_cast<const unsigned char*>(a.x) + b * a.x_sb + h * a.x_sh + src * a.x_sn;
   unsigned char* yd = static_cast<unsigned char*>(a.y) + b * a.y_sb + h * a.y_sh + dst * a.y_sn;
   *reinterpret_cast<u32x4*>(yd + 16 * part) = *reinterpret_cast<const u32x4*>(xs + 16 * part);

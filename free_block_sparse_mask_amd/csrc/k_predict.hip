@@ -146,6 +146,25 @@ __device__ uint64_t block_reduce_u64(uint64_t v, unsigned long long* lds) {
                       [](unsigned long long x, unsigned long long y) { return x + y; });
 }
 
+// ceil(tau * F) exactly, for 0 < tau <= 1 and a 64-bit integer F: tau is
+// m * 2^-s with an integer mantissa m < 2^53 (s >= 52 since tau <= 1), so
+// the 117-bit product m * F shifted right by s, rounded up, is the value.
+// An integer prefix c satisfies c < tau * F exactly when c < ceil(tau * F).
+__device__ __forceinline__ uint64_t ceil_tau_times(double tau, uint64_t F) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(tau);
+  const int ex = (int)((bits >> 52) & 0x7ff);
+  uint64_t m = bits & ((1ull << 52) - 1);
+  int s = 1074;                                   // subnormal tau: m * 2^-1074
+  if (ex != 0) {
+    m |= 1ull << 52;
+    s = 1075 - ex;
+  }
+  if (m == 0 || F == 0) return 0;
+  if (s >= 117) return 1;                         // 0 < tau * F < 1
+  const unsigned __int128 prod = (unsigned __int128)m * F;
+  return (uint64_t)((prod + (((unsigned __int128)1 << s) - 1)) >> s);
+}
+
 // Writes the M_g row (Tn bytes) and the ascending list of its ones.
 // keep(j) must be readable by every thread.
 template <typename Keep>
@@ -486,8 +505,17 @@ __global__ __launch_bounds__(kThreads) void mask_rows(PredictArgs a, int cap) {
         fsum += fx[x];
       }
       const uint64_t F = block_reduce_u64(fsum, ured);
-      // kept iff exclusive prefix < tau * F; at least the first entry
-      const uint64_t TF = max((uint64_t)1, (uint64_t)(a.tau * (double)F));
+      // kept iff exclusive prefix < tau * F, i.e. < TF = ceil(tau * F), taken
+      // exactly: 1 <= TF <= F, so the running sums always cross TF inside
+      // some bin, the first entry is always kept, and tau = 1 keeps every
+      // entry whose fixed-point value is non-zero.  (A float64 product
+      // tau * (double)F would not do: (double)F is F rounded to a multiple of
+      // 2^9 near 2^62, on either side of F.)
+      const uint64_t TF = ceil_tau_times(a.tau, F);
+      if (tid == 0) {
+        s_digit = 0;
+        s_above = 0;
+      }
       uint64_t prefix = 0, above = 0;
       for (int pass = 0; pass < 8; ++pass) {
         const int shift = 56 - 8 * pass;

@@ -103,8 +103,10 @@ int sparge_hilbert_index(int T, int H, int W, int32_t* perm, int32_t* inv);
  * size; a row of d elements must be a multiple of 16 bytes).
  * inverse = 0: y[b,h,p,:] = x[b,h,perm[p],:] (Q, K, V into curve order).
  * inverse = 1: y[b,h,perm[p],:] = x[b,h,p,:] (the output back to raster order).
- * perm is a device int32 array of N entries forming a permutation of 0..N-1
- * (not checked on the device).  x and y must not overlap.
+ * perm is a device int32 array of N entries forming a permutation of 0..N-1.
+ * It is not validated: an entry outside [0, N) moves nothing (that row of y
+ * is left as it was), so a malformed order cannot read or write outside x
+ * and y.  The byte ranges x and y span must not overlap (SPARGE_EINVAL).
  */
 int sparge_hilbert_permute(const void* x, const sparge_tensor* xs, void* y, const sparge_tensor* ys,
                            int dtype, const int32_t* perm, int inverse, void* stream);

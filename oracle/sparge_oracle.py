@@ -161,6 +161,24 @@ def topcdf(p: np.ndarray, tau: float) -> Tuple[np.ndarray, Dict[str, np.ndarray]
     return keep, {"excl": excl_by_idx, "order": order, "thresh": tau * total, "p": p}
 
 
+def topcdf_ambiguous(p: np.ndarray, keep: np.ndarray, info: Dict[str, np.ndarray],
+                     near_cdf: float = 1e-4, near_tie: float = 1e-6) -> np.ndarray:
+    """Entries of one TopCdf row (eq. 8) whose selection another correct
+    implementation may take the other way through rounding alone: the
+    exclusive prefix lies within ``near_cdf`` of tau * sum, or the
+    probability is tied (relatively within ``near_tie``) with the last kept
+    entry while at least one other entry shares that tie (a tie that may
+    straddle the cut).  Acceptance bookkeeping for comparisons, not part of
+    the method.  ``keep`` and ``info`` are :func:`topcdf`'s results."""
+    amb = np.abs(info["excl"] - info["thresh"]) <= near_cdf
+    if keep.any():
+        last_kept = info["order"][int(keep.sum()) - 1]
+        tied = np.abs(p - p[last_kept]) <= near_tie * p[last_kept]
+        if tied.sum() > 1:
+            amb |= tied
+    return amb
+
+
 def predict_mask_head(Qh: np.ndarray, Kh: np.ndarray, tau: float, theta: float, causal: bool,
                       bq: int = BQ, bk: int = BK, fix_q: Optional[np.ndarray] = None,
                       fix_k: Optional[np.ndarray] = None, scale_in_map: bool = True,
@@ -203,12 +221,7 @@ def predict_mask_head(Qh: np.ndarray, Kh: np.ndarray, tau: float, theta: float, 
         p = e / e.sum()                              # P^[i] = softmax(S^[i])
         keep, info = topcdf(p, tau)
         mg[i, cols[keep]] = True
-        amb = np.abs(info["excl"] - info["thresh"]) <= near_cdf
-        last_kept = info["order"][int(keep.sum()) - 1]
-        tied = np.abs(p - p[last_kept]) <= near_tie * p[last_kept]
-        if tied.sum() > 1:                           # a near-tie straddles the cut
-            amb |= tied
-        ambiguous[i, cols[amb]] = True
+        ambiguous[i, cols[topcdf_ambiguous(p, keep, info, near_cdf, near_tie)]] = True
     mg[fq, :] = True                                 # eq. 9, rows
     mg[:, fk] = True                                 # eq. 9, columns
     mg &= live
@@ -272,14 +285,21 @@ def attend_row_block(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.
                      lam: float, causal: bool, bq: int = BQ, bk: int = BK,
                      R: int = ROWS_PER_GROUP, skip_override: Optional[np.ndarray] = None,
                      score_fn=None, vote_info: Optional[list] = None,
-                     margins: Optional[np.ndarray] = None):
+                     margins: Optional[np.ndarray] = None,
+                     pv8: Optional[Tuple[np.ndarray, np.ndarray]] = None):
     """O_i for one query block i of one head, visiting key blocks j with
     M_g[i, j] = 1 in ascending j (eq. 1 with eqs. 2-3 and the lambda rule).
 
     ``skip_override`` [Tn, c_w] (int8: 1 execute, 2 skip, anything else = use
     the rule) replays another implementation's PV decisions.
     ``score_fn(rows, keys)`` replaces Q_i K_j^T / sqrt(d) (used by the int8
-    path).  ``margins`` [Tn, c_w], if given, receives max(m_loc - m_new) - lambda
+    path).  ``pv8`` = (V8, delta) switches the P~V product to 8-bit floats
+    ([Review] Fig. 9, "SpargeAttn + Sage2"): V8 [N, d_v] holds the E4M3
+    values of V / delta (delta [d_v] per channel, :func:`v_channel_scales`),
+    and each tile adds e4m3(P8_SCALE P~) V8 delta / P8_SCALE, with P~ =
+    exp(S - m_new) taken at the running max of that step, in Algorithm 1's
+    order; the rescaling by exp(m - m_new) and l are exact.
+    ``margins`` [Tn, c_w], if given, receives max(m_loc - m_new) - lambda
     of every voting group (the rule skips iff it is negative).  Returns
     (O_i [n, d_v], counts dict, decisions [Tn, c_w] int8 with 1 = PV executed,
     2 = skipped by the lambda vote, 3 = void group (no visible key in the
@@ -339,7 +359,12 @@ def attend_row_block(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.
             else:
                 cnt["pv_exec"] += 1
                 decisions[j, g] = 1
-                O[gi] = alpha[gi, None] * O[gi] + Pt[gi] @ Vh[keys.start:keys.stop]
+                if pv8 is None:
+                    O[gi] = alpha[gi, None] * O[gi] + Pt[gi] @ Vh[keys.start:keys.stop]
+                else:
+                    V8, delta = pv8
+                    P8 = e4m3_round(P8_SCALE * Pt[gi])
+                    O[gi] = alpha[gi, None] * O[gi] + (P8 @ V8[keys.start:keys.stop]) * (delta / P8_SCALE)
         m = m_new
     out = np.zeros_like(O)
     nz = l > 0
@@ -354,13 +379,15 @@ def sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray
                      causal: bool, bq: int = BQ, bk: int = BK, R: int = ROWS_PER_GROUP,
                      blocks: Optional[Sequence[Tuple[int, int, int]]] = None,
                      skip_override: Optional[np.ndarray] = None, quant: Optional[dict] = None,
-                     margins: Optional[np.ndarray] = None):
+                     margins: Optional[np.ndarray] = None, pv8: bool = False):
     """Stage 2 for Q [B, H, N, d], K/V [B, H_kv, N, d] and M_g [B, H, Tm, Tn].
 
     ``blocks`` restricts the work to (b, h, i) query blocks; the other rows of
     the returned O stay 0.  ``skip_override`` [B, H, Tm, Tn, c_w] replays PV
     decisions.  ``quant`` (from :func:`quantize_qk`) switches S to the int8
-    form.  ``margins`` [B, H, Tm, Tn, c_w] (NaN-filled by the caller) receives
+    form.  ``pv8`` runs the P~V products on 8-bit floats (see
+    :func:`attend_row_block`), with V scaled per channel of each kv head.
+    ``margins`` [B, H, Tm, Tn, c_w] (NaN-filled by the caller) receives
     every vote's margin, as in :func:`attend_row_block`.  Returns (O [B, H, N, d_v], counts dict summed over the blocks,
     decisions [B, H, Tm, Tn, c_w]).
     """
@@ -373,8 +400,12 @@ def sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray
     tot = dict.fromkeys(COUNT_NAMES, 0)
     todo = blocks if blocks is not None else [(b, h, i) for b in range(B) for h in range(H)
                                               for i in range(Tm)]
+    v8 = {}
     for b, h, i in todo:
         hk = kv_head(h, H, H_kv)
+        if pv8 and (b, hk) not in v8:
+            delta = v_channel_scales(V[b, hk])
+            v8[b, hk] = (e4m3_round(V[b, hk] / delta[None, :]), delta)
         score_fn = None
         if quant is not None:
             qc, kc = quant["q_codes"][b, h], quant["k_codes"][b, hk]
@@ -387,7 +418,8 @@ def sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray
         ov = None if skip_override is None else skip_override[b, h, i]
         o, c, decision = attend_row_block(Q[b, h], K[b, hk], V[b, hk], mg[b, h, i], i, lam, causal,
                                           bq, bk, R, ov, score_fn,
-                                          margins=None if margins is None else margins[b, h, i])
+                                          margins=None if margins is None else margins[b, h, i],
+                                          pv8=v8.get((b, hk)))
         rows = block_rows(N, bq, i)
         O[b, h, rows.start:rows.stop] = o
         dec[b, h, i] = decision
@@ -441,16 +473,23 @@ def masked_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray
 # ---------------------------------------------------------------------------
 # fp8 P~V ([Review] Fig. 9, "SpargeAttn + Sage2": P~V on 8-bit floats)
 # ---------------------------------------------------------------------------
-# Readings (the pages name the variant only): OCP E4M3 (4 exponent bits, bias
-# 7, 3 mantissa bits, largest finite 448), round to nearest even; V scaled per
-# channel by the power of two delta_c = 2^e, e the least integer with
-# max_n |V[n, c]| <= 448 * 2^e (1 for an all-zero channel), so V / delta_c is
-# exact before its one rounding; P~ taken at the final row max (the two-pass
-# order) and scaled by 2^8 before its rounding; products summed exactly;
-# O = delta_c * sum / 2^8 / l with l the exact row sum.
+# The pages name the variant and nothing more.  Format readings (the plainest
+# ones the variant's name supports):
+# * OCP E4M3: 4 exponent bits (bias 7), 3 mantissa bits, largest finite 448,
+#   subnormal step 2^-9; round to nearest, ties to the even mantissa.
+# * V per channel c of a kv head: delta_c = 2^e, e the least integer with
+#   max_n |V[n, c]| <= 448 * 2^e (1 for an all-zero channel), so V / delta_c
+#   is exact and fits the format before its one rounding.
+# * P~ = exp(S - m_ij) lies in [0, 1] under the running max of Algorithm 1;
+#   it is scaled by P8_SCALE = 2^8, the largest power of two that keeps 1
+#   inside the format's range (2^8 <= 448 < 2^9), so the scaling is exact
+#   and P~ keeps the format's full exponent range.
+# * The products are summed, and l and the rescaling of eq. 1 are taken, as
+#   in the unquantised recurrence (exactly, here).
+# The recurrence itself is attend_row_block's, with its ``pv8`` argument.
 
 E4M3_MAX = 448.0
-PV8_P_SCALE = 256.0
+P8_SCALE = 256.0
 
 
 def e4m3_round(x: np.ndarray) -> np.ndarray:
@@ -467,8 +506,8 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
 
 
 def v_channel_scales(Vh: np.ndarray) -> np.ndarray:
-    """delta_c = 2^e with e the least integer such that max|V[:, c]| <= 448 * 2^e,
-    at least 2^-100; 1 for an all-zero channel."""
+    """delta_c = 2^e with e the least integer such that max|V[:, c]| <= 448 * 2^e;
+    1 for an all-zero channel.  Vh [N, d_v]."""
     mx = np.abs(Vh).max(axis=0)
     e = np.zeros_like(mx)
     nz = mx > 0
@@ -476,111 +515,7 @@ def v_channel_scales(Vh: np.ndarray) -> np.ndarray:
     # exact comparisons settle a log2 that lands next to an integer
     e = np.where(nz & (mx > E4M3_MAX * 2.0 ** e), e + 1, e)
     e = np.where(nz & (mx <= E4M3_MAX * 2.0 ** (e - 1)), e - 1, e)
-    e = np.maximum(e, -100.0)                        # all but zero channels: 2^-100
     return np.where(nz, 2.0 ** e, 1.0)
-
-
-def attend_row_block_fp8pv(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, mg_row: np.ndarray, i: int,
-                           lam: float, causal: bool, decisions: np.ndarray, bq: int = BQ, bk: int = BK,
-                           R: int = ROWS_PER_GROUP, score_fn=None, amb_window: Optional[float] = None,
-                           sum_rel: float = 0.0):
-    """O_i of the fp8 P~V variant for one query block, given the (tile, group)
-    decisions of the lambda rule ([Tn, c_w], 1 = P~V runs): m_final and l are
-    eq. 1's final running max and row sum (exact); the voted groups add
-    e4m3(2^8 exp(S - m_final)) e4m3(V / delta) and O = delta sum / 2^8 / l.
-
-    With ``amb_window`` w, also returns for every output element the most it
-    can move when a P~ within relative distance w of an E4M3 rounding
-    boundary rounds the other way (the width of that rounding step times the
-    element's V term, over 2^8 l), plus ``sum_rel`` times the sum of the
-    absolute products of every 64-key tile: the room another implementation
-    may take whose P~ differs from this one by less than w and whose tile
-    sums carry a relative error below sum_rel."""
-    N, d = Qh.shape
-    Tn = num_blocks(N, bk)
-    rows = block_rows(N, bq, i)
-    n = len(rows)
-    q_idx = np.arange(rows.start, rows.stop)
-    Qi = Qh[rows.start:rows.stop]
-    live = tile_live(N, bq, bk, causal)[i]
-    todo = [j for j in range(Tn) if mg_row[j] and live[j]]
-    S_of = {}
-    m = np.full(n, NEG_INF)
-    for j in todo:
-        keys = block_rows(N, bk, j)
-        k_idx = np.arange(keys.start, keys.stop)
-        S = _scores_float(Qi, Kh[keys.start:keys.stop]) if score_fn is None else score_fn(rows, keys)
-        if causal:
-            S = np.where(k_idx[None, :] > q_idx[:, None], NEG_INF, S)
-        S_of[j] = S
-        m = np.maximum(m, S.max(axis=1))
-    m_sub = np.where(np.isfinite(m), m, 0.0)
-    l = np.zeros(n)
-    delta = v_channel_scales(Vh)
-    Vq = e4m3_round(Vh / delta[None, :])
-    acc = np.zeros((n, Vh.shape[1]))
-    amb = np.zeros_like(acc)
-    for j in todo:
-        keys = block_rows(N, bk, j)
-        with np.errstate(invalid="ignore"):
-            P = np.exp(S_of[j] - m_sub[:, None])
-        l += P.sum(axis=1)
-        Pq = e4m3_round(PV8_P_SCALE * P)
-        if amb_window is not None:
-            step = np.abs(e4m3_round(PV8_P_SCALE * P * (1 + amb_window)) -
-                          e4m3_round(PV8_P_SCALE * P * (1 - amb_window)))
-        for g in range(decisions.shape[1]):
-            if decisions[j, g] != 1:
-                continue
-            gi = np.arange(g * R, min(n, g * R + R))
-            acc[gi] += Pq[gi] @ Vq[keys.start:keys.stop]
-            if amb_window is not None:
-                amb[gi] += (step[gi] + sum_rel * np.abs(Pq[gi])) @ np.abs(Vq[keys.start:keys.stop])
-    out = np.zeros_like(acc)
-    nz = l > 0
-    out[nz] = acc[nz] * delta[None, :] / PV8_P_SCALE / l[nz, None]
-    if amb_window is None:
-        return out
-    amb_out = np.zeros_like(amb)
-    amb_out[nz] = amb[nz] * delta[None, :] / PV8_P_SCALE / l[nz, None]
-    return out, amb_out
-
-
-def sparse_attention_fp8pv(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mg: np.ndarray, lam: float,
-                           causal: bool, blocks=None, skip_override: Optional[np.ndarray] = None,
-                           quant: Optional[dict] = None, amb_window: Optional[float] = None,
-                           sum_rel: float = 0.0):
-    """The fp8 P~V variant for Q [B, H, N, d], K/V [B, H_kv, N, d]: the lambda
-    decisions come from :func:`sparse_attention` (or ``skip_override``), the
-    output from :func:`attend_row_block_fp8pv`.  ``blocks`` restricts the work
-    to (b, h, i); other rows stay 0.  With ``amb_window``, returns (O, room)
-    with room as in :func:`attend_row_block_fp8pv`."""
-    B, H, N, d = Q.shape
-    H_kv = K.shape[1]
-    Tm = num_blocks(N, BQ)
-    _, _, dec = sparse_attention(Q, K, V, mg, lam, causal, blocks=blocks, skip_override=skip_override,
-                                 quant=quant)
-    O = np.zeros((B, H, N, V.shape[3]))
-    room = np.zeros_like(O)
-    todo = blocks if blocks is not None else [(b, h, i) for b in range(B) for h in range(H) for i in range(Tm)]
-    for b, h, i in todo:
-        hk = kv_head(h, H, H_kv)
-        score_fn = None
-        if quant is not None:
-            qc, kc = quant["q_codes"][b, h], quant["k_codes"][b, hk]
-            dq, dk = quant["q_scale"][b, h], quant["k_scale"][b, hk]
-
-            def score_fn(rows, keys, qc=qc, kc=kc, dq=dq, dk=dk, i=i):
-                j = keys.start // BK
-                return (qc[rows.start:rows.stop] @ kc[keys.start:keys.stop].T) * (dq[i] * dk[j]) / math.sqrt(d)
-        r = block_rows(N, BQ, i)
-        res = attend_row_block_fp8pv(Q[b, h], K[b, hk], V[b, hk], mg[b, h, i], i, lam, causal, dec[b, h, i],
-                                     score_fn=score_fn, amb_window=amb_window, sum_rel=sum_rel)
-        if amb_window is None:
-            O[b, h, r.start:r.stop] = res
-        else:
-            O[b, h, r.start:r.stop], room[b, h, r.start:r.stop] = res
-    return O if amb_window is None else (O, room)
 
 
 # ---------------------------------------------------------------------------

@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import math
 import sys
+from typing import Optional
 
 import numpy as np
 import torch
@@ -131,10 +132,14 @@ def run_attn(q, k, v, mask, lam: float, causal: bool, **kw):
 
 def check_attention(o_gpu: torch.Tensor, counts: torch.Tensor, dbg: torch.Tensor, Q, K, V,
                     mg: np.ndarray, lam: float, causal: bool, out_dtype: str, blocks=None,
-                    quant=None, int8: bool = False) -> dict:
+                    quant=None, int8: bool = False, o16: Optional[torch.Tensor] = None,
+                    o16_dtype: Optional[str] = None) -> dict:
     """Compares the GPU output (and counters, decisions) with the oracle given
     the same mask, replaying the GPU's lambda decisions.  ``o_gpu`` is the
-    float32 output (``out_dtype`` "f32") or a 16-bit one."""
+    float32 output (``out_dtype`` "f32") or a 16-bit one.  ``o16`` (of type
+    ``o16_dtype``), the product's 16-bit output, is scored too: its relative
+    L1 must meet the same bound (its max-abs is logged, not bounded: bf16
+    storage alone moves a value near 4 by up to 2^-7)."""
     B, H, N, d = Q.shape
     Tm, Tn = O.num_blocks(N, O.BQ), O.num_blocks(N, O.BK)
     cw = O.BQ // O.ROWS_PER_GROUP
@@ -171,9 +176,103 @@ def check_attention(o_gpu: torch.Tensor, counts: torch.Tensor, dbg: torch.Tensor
         assert rep["rel_l1"] <= INT8_REL_L1 and rep["cos"] >= INT8_COS, rep
     else:
         assert rep["max_abs"] <= ATTN_MAX_ABS and rep["rel_l1"] <= ATTN_REL_L1, rep
+    if o16 is not None:
+        o_n = O.widen(to_bits(o16), o16_dtype)
+        g16 = np.concatenate([o_n[b, h, O.block_rows(N, O.BQ, i).start:O.block_rows(N, O.BQ, i).stop]
+                              for b, h, i in todo])
+        rep["max_abs_16"] = float(np.max(np.abs(g16 - orf))) if g16.size else 0.0
+        rep["rel_l1_16"] = rel_l1(orf, g16)
+        assert rep["rel_l1_16"] <= (INT8_REL_L1 if int8 else ATTN_REL_L1), rep
+        log(f"   {o16_dtype} output: rel_l1={rep['rel_l1_16']:.2e} max_abs={rep['max_abs_16']:.2e}")
     if blocks is None:
         c = fb.counts_dict(counts)
         for k in O.COUNT_NAMES:
             assert c[k] == cnt_ref[k], (k, c, cnt_ref)
         rep["counts"] = c
+    return rep
+
+
+# ---------------------------------------------------------------------------
+# fp8 P~V acceptance against the oracle (Algorithm 1's order)
+# ---------------------------------------------------------------------------
+# The oracle rounds P~ = exp(S - m_ij) to E4M3 at each step's running max and
+# rescales exactly; the kernel rounds exp(S - m_final) once, in its second
+# pass.  V's 8-bit values are the same on both sides.  One E4M3 rounding of
+# x = 2^8 p moves it by at most 2^-4 x in the normal range and by at most
+# 2^-10 (half the subnormal step) below it, and never by more than x itself,
+# so either side's weight lies within min(p, max(2^-4 p, 2^-18)) of the
+# exact p = exp(S - m_final) (the later rescalings of the oracle's order
+# only shrink both terms).  The kernel adds float32 scores, exponentials and
+# sums: 2^-7 p covers them (sums of up to 2^13 products lose at most
+# 2^13 * 2^-23 of their absolute size), and 2^-10 |O| covers its float32 l.
+# Hence, per output element, the room
+#   sum over voted keys of (2 min(p, max(2^-4 p, 2^-18)) + 2^-7 p) |V8 delta|
+#   / l + 2^-10 |O|.
+# Beside it, two whole-output statistics: relative L1 <= 2^-4 (the largest
+# relative move of one rounding) and cosine >= 0.998 (= 1 - (2^-4)^2 / 2).
+FP8_REL_L1 = 2.0 ** -4
+FP8_COS = 0.998
+
+
+def fp8_room(Q, K, V, mg, causal, decisions, blocks, quant=None, ref=None):
+    """The element-wise room above for the (b, h, i) blocks in ``blocks``
+    (other rows 0), given the GPU's lambda decisions [B, H, Tm, Tn, c_w]."""
+    B, H, N, d = Q.shape
+    Hkv = K.shape[1]
+    R = O.ROWS_PER_GROUP
+    room = np.zeros((B, H, N, V.shape[3]))
+    v8 = {}
+    for b, h, i in blocks:
+        hk = O.kv_head(h, H, Hkv)
+        if (b, hk) not in v8:
+            delta = O.v_channel_scales(V[b, hk])
+            v8[b, hk] = np.abs(O.e4m3_round(V[b, hk] / delta[None, :]) * delta[None, :])
+        av = v8[b, hk]
+        rows = O.block_rows(N, O.BQ, i)
+        q_idx = np.arange(rows.start, rows.stop)
+        live = O.tile_live(N, O.BQ, O.BK, causal)[i]
+        todo = [j for j in range(O.num_blocks(N, O.BK)) if mg[b, h, i, j] and live[j]]
+        S_of = {}
+        m = np.full(len(rows), -np.inf)
+        for j in todo:
+            keys = O.block_rows(N, O.BK, j)
+            if quant is None:
+                S = Q[b, h, rows.start:rows.stop] @ K[b, hk, keys.start:keys.stop].T / math.sqrt(d)
+            else:
+                S = (quant["q_codes"][b, h, rows.start:rows.stop] @ quant["k_codes"][b, hk, keys.start:keys.stop].T
+                     * (quant["q_scale"][b, h, i] * quant["k_scale"][b, hk, j]) / math.sqrt(d))
+            if causal:
+                S = np.where(np.arange(keys.start, keys.stop)[None, :] > q_idx[:, None], -np.inf, S)
+            S_of[j] = S
+            m = np.maximum(m, S.max(axis=1))
+        msub = np.where(np.isfinite(m), m, 0.0)
+        l = np.zeros(len(rows))
+        acc = np.zeros((len(rows), V.shape[3]))
+        for j in todo:
+            keys = O.block_rows(N, O.BK, j)
+            with np.errstate(invalid="ignore"):
+                P = np.exp(S_of[j] - msub[:, None])
+            l += P.sum(axis=1)
+            e = 2.0 * np.minimum(P, np.maximum(2.0 ** -4 * P, 2.0 ** -18)) + 2.0 ** -7 * P
+            for g in range(decisions.shape[-1]):
+                if decisions[b, h, i, j, g] == 1:
+                    gi = np.arange(g * R, min(len(rows), g * R + R))
+                    acc[gi] += e[gi] @ av[keys.start:keys.stop]
+        nz = l > 0
+        room[b, h, rows.start:rows.stop][nz] = acc[nz] / l[nz, None]
+    if ref is not None:
+        room += 2.0 ** -10 * np.abs(ref)
+    return room
+
+
+def check_fp8(og: np.ndarray, ref: np.ndarray, room: np.ndarray, rows=None) -> dict:
+    """The fp8 acceptance on the selected rows (an index array over N, all if
+    None): every element within the room, relative L1 and cosine bounds."""
+    if rows is not None:
+        og, ref, room = og[..., rows, :], ref[..., rows, :], room[..., rows, :]
+    over = np.abs(og - ref) - room
+    rep = {"rel_l1": rel_l1(ref, og), "cos": cosine(ref, og), "max_abs": float(np.max(np.abs(og - ref))),
+           "max_over_room": float(over.max()), "room_max": float(room.max())}
+    assert rep["max_over_room"] <= 0.0, rep
+    assert rep["rel_l1"] <= FP8_REL_L1 and rep["cos"] >= FP8_COS, rep
     return rep

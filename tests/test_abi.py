@@ -139,7 +139,17 @@ def test_permute_rejects_bad_arguments():
                                     None) == fb.SPARGE_EINVAL
     assert L.sparge_hilbert_permute(FAKE, ctypes.byref(x), FAKE, ctypes.byref(x), fb.BF16, FAKE, 0,
                                     None) == fb.SPARGE_EINVAL           # x == y
-    y8 = fb.SpargeTensor(1, 2, 100, 8, 2 * 100 * 16, 100 * 16, 16)   # 8-byte rows, 16-byte stride
+    # x spans 1 * 2 * 100 * 64 bf16 = 25600 bytes: a y that starts inside it overlaps,
+    # one that starts at its end does not (the launch is never reached: perm is null)
+    base = 1 << 20
+    for off, rc in ((25600 - 16, fb.SPARGE_EINVAL), (16, fb.SPARGE_EINVAL), (-16, fb.SPARGE_EINVAL),
+                    (25600, fb.SPARGE_EINVAL), (-25600, fb.SPARGE_EINVAL)):
+        got = L.sparge_hilbert_permute(ctypes.c_void_p(base), ctypes.byref(x), ctypes.c_void_p(base + off),
+                                       ctypes.byref(x), fb.BF16, None, 0, None)
+        assert got == rc
+        msg = L.sparge_last_error().decode()
+        assert ("overlap" in msg) == (abs(off) < 25600), (off, msg)
+    y8 =fb.SpargeTensor(1, 2, 100, 8, 2 * 100 * 16, 100 * 16, 16)   # 8-byte rows, 16-byte stride
     assert L.sparge_hilbert_permute(FAKE, ctypes.byref(y8), ctypes.c_void_p(1 << 21), ctypes.byref(y8),
                                     fb.I8, FAKE, 0, None) == fb.SPARGE_EUNSUPPORTED  # 8-byte rows
 

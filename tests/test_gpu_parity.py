@@ -48,6 +48,42 @@ def test_predict_mask_matches_oracle(label, wid, over):
     log(f"   near_theta={rep['near_theta']} ambiguous={rep['ambiguous']} s_err={rep['max_s_err']:.2e}")
 
 
+@pytest.mark.parametrize("tau", [1.0, float(np.nextafter(1.0, 0.0)), 0.999])
+@pytest.mark.parametrize("label,wid,over", [CASES[0], CASES[3]], ids=[CASES[0][0], CASES[3][0]])
+def test_predict_mask_at_tau_near_one(label, wid, over, tau):
+    """tau = 1 (the dense end of the hyper-parameter search) and the doubles
+    just below it: the TopCdf threshold is ceil(tau * sum) in fixed point,
+    at most the sum, so the radix select always finds its boundary.  At
+    tau = 1 a selective row keeps every column whose probability reaches
+    2^-61 (its fixed-point value is then non-zero)."""
+    w, q, k, v = _case(wid, **over)
+    log(f"[predict tau] {label}: tau={tau!r} N={w.N} causal={w.causal}")
+    qd, kd = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    mask = fb.predict_mask(qd, kd, tau, w.theta, w.causal)
+    torch.cuda.synchronize()
+    Q, K = O.widen(q, w.dtype), O.widen(k, w.dtype)
+    rep = check_mask(mask, Q, K, tau, w.theta, w.causal)
+    log(f"   near_theta={rep['near_theta']} ambiguous={rep['ambiguous']}")
+    if tau == 1.0:
+        mg = mask.mg.cpu().numpy().astype(bool)
+        kept_small = 0
+        for b in range(w.B):
+            for h in range(w.H):
+                r = O.predict_mask_head(Q[b, h], K[b, O.kv_head(h, w.H, w.H_kv)], tau, w.theta, w.causal)
+                for i in np.nonzero(~r["fix_q"])[0]:
+                    z = r["shat"][i]
+                    fin = np.isfinite(z)
+                    if not fin.any():
+                        continue
+                    p = np.zeros_like(z)
+                    p[fin] = np.exp(z[fin] - z[fin].max())
+                    p /= p.sum()
+                    big = p >= 2.0 ** -61
+                    assert np.all(mg[b, h, i][big]), (b, h, i)
+                    kept_small += int(np.sum(big & (p < 1e-6)))
+        log(f"   every column with p >= 2^-61 kept ({kept_small} of them below 1e-6)")
+
+
 @pytest.mark.parametrize("label,wid,over", CASES, ids=[c[0] for c in CASES])
 def test_attention_given_oracle_mask(label, wid, over):
     w, q, k, v = _case(wid, **over)
@@ -57,7 +93,7 @@ def test_attention_given_oracle_mask(label, wid, over):
     mg = torch.from_numpy(ref["mg"].astype(np.uint8)).to(DEV)
     qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
     o, o32, counts, dbg = run_attn(qd, kd, vd, mg, w.lam, w.causal)
-    rep = check_attention(o32, counts, dbg, Q, K, V, ref["mg"], w.lam, w.causal, "f32")
+    rep = check_attention(o32, counts, dbg, Q, K, V, ref["mg"], w.lam, w.causal, "f32", o16=o, o16_dtype=w.dtype)
     log(f"   max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} flips={rep['lambda_flips']} "
         f"counts={rep['counts']}")
 
@@ -84,7 +120,7 @@ def test_attention_random_mask_edge_rows(dtype, d, causal):
     for lam in (-2.0, -math.inf):
         log(f"[attn-random] dtype={dtype} d={d} causal={causal} lam={lam}")
         o, o32, counts, dbg = run_attn(qd, kd, vd, mg, lam, causal)
-        rep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32")
+        rep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32", o16=o, o16_dtype=dtype)
         log(f"   max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} counts={rep['counts']}")
         assert rep["counts"]["empty_rows"] >= 128
         if lam == -2.0:
@@ -131,7 +167,7 @@ def test_attention_dense_rows_in_packs(causal):
     for lam in (-3.0, -math.inf):
         log(f"[attn-packs] causal={causal} lam={lam} dense blocks={dense_rows}")
         o, o32, counts, dbg = run_attn(qd, kd, vd, mg, lam, causal)
-        rep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32")
+        rep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32", o16=o, o16_dtype="bf16")
         log(f"   max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} counts={rep['counts']}")
 
 
@@ -162,7 +198,7 @@ def test_short_sequences_whole_path(N, d, causal):
     rep = check_mask(mask, Q, K, tau, theta, causal)
     mg_np = mask.mg.cpu().numpy().astype(bool)
     o, o32, counts, dbg = run_attn(qd, kd, vd, mask.mg, lam, causal)
-    arep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32")
+    arep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32", o16=o, o16_dtype="bf16")
     log(f"   mask ambiguous={rep['ambiguous']}; max_abs={arep['max_abs']:.2e} counts={arep['counts']}")
     assert arep["counts"]["rows"] == H * N
     if O.num_blocks(N, 64) >= 2:
@@ -206,7 +242,8 @@ def test_strided_layouts_and_batches(causal):
     assert all(torch.equal(x, y) for x, y in zip(a8, b8))
     rep = check_mask(m2, Q, K, w.tau, w.theta, causal)
     o, o32, counts, dbg = run_attn(qs, ks, vs, m2, w.lam, causal)
-    arep = check_attention(o32, counts, dbg, Q, K, V, m2.mg.cpu().numpy().astype(bool), w.lam, causal, "f32")
+    arep = check_attention(o32, counts, dbg, Q, K, V, m2.mg.cpu().numpy().astype(bool), w.lam, causal, "f32",
+                           o16=o, o16_dtype=w.dtype)
     log(f"   mask ambiguous={rep['ambiguous']}; max_abs={arep['max_abs']:.2e} rel_l1={arep['rel_l1']:.2e} "
         f"counts={arep['counts']}")
 
@@ -336,7 +373,8 @@ def test_int8_attention_matches_oracle(v_dtype, d, causal):
     ref_mask = O.predict_mask(Q, K, w.tau, w.theta, w.causal)["mg"]
     assert np.array_equal(mask.mg.cpu().numpy().astype(bool), ref_mask)
     quant = O.quantize_qk(Q, K)
-    rep = check_attention(o32, counts, dbg, Q, K, V, ref_mask, w.lam, w.causal, "f32", quant=quant,
+    rep = check_attention(o32, counts, dbg, Q, K, V, ref_mask, w.lam, w.causal, "f32", quant=quant, o16=o,
+                          o16_dtype=v_dtype,
                           int8=True)
     log(f"[int8] rel_l1={rep['rel_l1']:.2e} cos={rep['cos']:.6f} max_abs={rep['max_abs']:.2e} "
         f"flips={rep['lambda_flips']}")
@@ -367,6 +405,33 @@ def test_hilbert_permute_roundtrip(dtype, d):
     ys = fb.hilbert_permute(big[..., :d], perm_d)
     torch.cuda.synchronize()
     assert np.array_equal(to_bits(ys), O.permute_tokens(x, p_ref))
+
+
+def test_hilbert_permute_skips_out_of_range_entries():
+    """A malformed order (entries -1, N, N + 5 and 2^31 - 1) moves nothing for
+    those entries: the gather leaves their rows of y as they were, the
+    scatter writes nothing from them, and every other row moves as usual."""
+    N, d, H = 300, 64, 2
+    rng = np.random.default_rng(21)
+    x = I.to_bits(rng.standard_normal((1, H, N, d)), "bf16")
+    perm = rng.permutation(N).astype(np.int32)
+    bad = np.array([0, 7, 150, N - 1])
+    perm[bad] = np.array([-1, N, N + 5, 2**31 - 1], dtype=np.int32)
+    ok = np.setdiff1d(np.arange(N), bad)
+    xd = to_dev(x, "bf16")
+    perm_d = torch.from_numpy(perm).to(DEV)
+    sentinel = torch.full((1, H, N, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    y = fb.hilbert_permute(xd, perm_d, out=sentinel.clone())
+    z = fb.hilbert_permute(xd, perm_d, inverse=True, out=sentinel.clone())
+    torch.cuda.synchronize()
+    yb, zb, sb = to_bits(y), to_bits(z), to_bits(sentinel)
+    assert np.array_equal(yb[:, :, ok], x[:, :, perm[ok]])
+    assert np.array_equal(yb[:, :, bad], sb[:, :, bad])
+    written = perm[ok]
+    assert np.array_equal(zb[:, :, written], x[:, :, ok])
+    untouched = np.setdiff1d(np.arange(N), written)
+    assert untouched.size == bad.size and np.array_equal(zb[:, :, untouched], sb[:, :, untouched])
+    log(f"[permute bad entries] {bad.size} skipped, {ok.size} rows moved")
 
 
 def test_video_pipeline_with_hilbert_order():

@@ -80,3 +80,11 @@ def test_search_result_is_pinned_by_the_oracle(wid):
     log(f"   oracle L1 {e_or:.5f} vs measured {res.l1:.5f}; mask ambiguous={rep['ambiguous']}")
     assert abs(e_or - res.l1) <= L1_TOL
     assert e_or <= l2 + L1_TOL
+    # every mask the search judged by, the tau = 1 dense ends included, is the oracle's
+    pairs = sorted({(e.tau, e.theta) for e in res.trace})
+    assert any(t == 1.0 for t, _ in pairs)
+    for tau, theta in pairs:
+        m = fb.predict_mask(qd, kd, tau, theta, w.causal)
+        torch.cuda.synchronize()
+        r = check_mask(m, Q, K, tau, theta, w.causal)
+        log(f"   trace mask tau={tau:.4f} theta={theta}: ambiguous={r['ambiguous']} near_theta={r['near_theta']}")

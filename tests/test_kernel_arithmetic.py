@@ -144,3 +144,151 @@ def test_block_sum_tree_equals_halving_loop():
             y = y + y[np.arange(64) ^ off]
             off >>= 1
         assert y[0] == x[0]
+
+
+# ---------------------------------------------------------------------------
+# mask_rows' TopCdf: a radix select over the probabilities' bit patterns with
+# exact 2^-62 fixed-point sums, replayed in Python integers
+# ---------------------------------------------------------------------------
+
+def topcdf_threshold(F, tau):
+    """The kernel's fixed-point threshold TF = ceil(tau * F), from tau's
+    integer mantissa m and exponent (tau = m * 2^-s) and the exact product
+    m * F, as mask_rows computes it in 128-bit integers."""
+    bits = int(np.array([tau], dtype=np.float64).view(np.uint64)[0])
+    ex = (bits >> 52) & 0x7FF
+    m = bits & ((1 << 52) - 1)
+    s = 1074
+    if ex:
+        m |= 1 << 52
+        s = 1075 - ex
+    if m == 0 or F == 0:
+        return 0
+    if s >= 117:
+        return 1
+    prod = m * F
+    assert prod < 1 << 128
+    return (prod + (1 << s) - 1) >> s
+
+
+def topcdf_radix_select(pr, tau):
+    """mask_rows' selection for one row of probabilities ``pr`` (float64, in
+    ascending column order): returns the kept mask.  Raises if no histogram
+    bin crosses the threshold (the kernel would then read its boundary
+    digit uninitialised)."""
+    key = pr.view(np.uint64).astype(object)
+    fx = [int(x) for x in np.floor(pr * 2.0 ** 62)]   # (uint64)(pr * 2^62): a truncation
+    F = sum(fx)
+    TF = topcdf_threshold(F, tau)
+    prefix, above = 0, 0
+    for pas in range(8):
+        shift = 56 - 8 * pas
+        cnt = [0] * 256
+        sums = [0] * 256
+        for k, f in zip(key, fx):
+            if (k >> shift) >> 8 == prefix:
+                cnt[(k >> shift) & 255] += 1
+                sums[(k >> shift) & 255] += f
+        cum, digit = above, None
+        for dgt in range(255, -1, -1):
+            if cum < TF <= cum + sums[dgt]:
+                digit, new_above = dgt, cum
+            cum += sums[dgt]
+        if digit is None:
+            raise AssertionError("no bin crosses the threshold")
+        prefix = (prefix << 8) | digit
+        above = new_above
+        if pas < 7 and cnt[digit] == 1:
+            prefix = next(k for k in key if (k >> shift) == prefix)
+            break
+    v = prefix
+    fv = int(np.floor(np.array([v], dtype=np.uint64).view(np.float64)[0] * 2.0 ** 62))
+    n_ties = sum(1 for k in key if k == v)
+    tie_keep = n_ties if fv == 0 else min(n_ties, (TF - above + fv - 1) // fv)
+    keep = np.zeros(len(pr), dtype=bool)
+    rank = 0
+    for x, k in enumerate(key):
+        if k > v:
+            keep[x] = True
+        elif k == v:
+            keep[x] = rank < tie_keep
+            rank += 1
+    return keep, F, TF
+
+
+def topcdf_fixed_point_definition(pr, TF):
+    """Eq. 8 on the fixed-point values: in the order (p descending, column
+    ascending), entry r is kept iff its exclusive prefix is below TF."""
+    fx = [int(x) for x in np.floor(pr * 2.0 ** 62)]
+    order = sorted(range(len(pr)), key=lambda x: (-pr[x], x))
+    keep = np.zeros(len(pr), dtype=bool)
+    excl = 0
+    for x in order:
+        keep[x] = excl < TF
+        excl += fx[x]
+    return keep
+
+
+def _rows(rng, n_rows):
+    for r in range(n_rows):
+        n = int(rng.integers(1, 300))
+        z = rng.standard_normal(n) * rng.choice([0.1, 1.0, 5.0, 40.0])
+        if r % 4 == 0:                       # exact ties
+            z = np.round(z * 4) / 4
+        e = np.exp(z - z.max())
+        yield e / e.sum()
+
+
+def test_radix_select_equals_the_sorted_prefix_rule():
+    rng = np.random.default_rng(8)
+    for tau in (0.05, 0.5, 0.9, 0.95, np.nextafter(1.0, 0.0), 1.0):
+        for pr in _rows(rng, 60):
+            keep, F, TF = topcdf_radix_select(pr, tau)
+            assert TF <= F
+            assert np.array_equal(keep, topcdf_fixed_point_definition(pr, TF))
+            assert keep.any()
+
+
+def test_tau_one_keeps_every_entry_with_a_nonzero_fixed_point_value():
+    rng = np.random.default_rng(9)
+    for pr in _rows(rng, 120):
+        keep, _, _ = topcdf_radix_select(pr, 1.0)
+        assert np.array_equal(keep, np.floor(pr * 2.0 ** 62) > 0)
+
+
+def test_threshold_is_the_exact_ceiling():
+    """TF = ceil(tau * F) for every tau in (0, 1] (normal, subnormal, 1 and
+    the double below it) and F up to 2^64, against exact rational arithmetic;
+    so 1 <= TF <= F and an integer prefix c < tau * F iff c < TF.  A float64
+    product tau * (double)F would not do: near 2^62, (double)F is F rounded
+    to a multiple of 2^9, on either side of F."""
+    import math
+    from fractions import Fraction
+    rng = np.random.default_rng(13)
+    taus = [1.0, np.nextafter(1.0, 0.0), 0.5, 0.9, 0.95, 1e-300, 5e-324, 2.0 ** -60]
+    taus += list(rng.uniform(0, 1, 200))
+    Fs = [1, 2, 3, (1 << 62) - 1, 1 << 62, (1 << 62) + 12345, (1 << 64) - 1]
+    Fs += [int(x) for x in rng.integers(1, 1 << 62, 50, dtype=np.int64)]
+    overshoot = 0
+    for tau in taus:
+        for F in Fs:
+            TF = topcdf_threshold(F, float(tau))
+            assert TF == math.ceil(Fraction(float(tau)) * F)
+            assert 1 <= TF <= F
+            overshoot += int(float(tau) * float(F)) > F
+    assert overshoot > 0        # the float64 route does overshoot
+
+
+def test_radix_select_agrees_with_the_float64_oracle_outside_its_window():
+    """Against the oracle's float64 rule (sorted cumulative sum, exclusive
+    prefix < tau * sum): the two may differ only where the oracle's
+    exclusive prefix lies within 1e-4 of tau * sum, the window the GPU
+    parity tests exclude."""
+    from oracle import sparge_oracle as O
+    rng = np.random.default_rng(12)
+    for tau in (0.5, 0.9, 0.95, 1.0):
+        for pr in _rows(rng, 60):
+            keep, _, _ = topcdf_radix_select(pr, tau)
+            ref, info = O.topcdf(pr, tau)
+            near = np.abs(info["excl"] - info["thresh"]) <= 1e-4
+            assert np.array_equal(keep & ~near, ref & ~near)

@@ -569,9 +569,10 @@ def test_fp8pv_equals_exact_attention_when_nothing_rounds():
     mg = np.ones((1, 1, 1, 2), dtype=bool)
     Q, K, V = Qh[None, None], Kh[None, None], Vh[None, None]
     exact, _, dec = O.sparse_attention(Q, K, V, mg, -np.inf, False)
-    o8 = O.attend_row_block_fp8pv(Qh, Kh, Vh, mg[0, 0, 0], 0, -np.inf, False, dec[0, 0, 0])
-    # 19 attended keys per row with equal weight 1/19: P~ = 1 exactly, and the
-    # others underflow to 0 after scaling
+    o8 = O.sparse_attention(Q, K, V, mg, -np.inf, False, pv8=True)[0][0, 0]
+    # 19 attended keys per row with equal weight 1/19: P~ = 1 exactly at the
+    # running max (25 from the first tile on), and the others underflow to 0
+    # after scaling
     assert np.max(np.abs(o8 - exact[0, 0])) < 1e-12
 
 
@@ -583,9 +584,11 @@ def test_fp8pv_error_within_the_rounding_bound():
     mg = np.ones((1, 1, 2, 4), dtype=bool)
     for causal in (False, True):
         exact, _, dec = O.sparse_attention(Q, K, V, mg, -np.inf, causal)
-        o8 = O.sparse_attention_fp8pv(Q, K, V, mg, -np.inf, causal)
+        o8 = O.sparse_attention(Q, K, V, mg, -np.inf, causal, pv8=True)[0]
         # per element: |p^ - p| <= 2^-4 p + 2^-18 (P~ scaled by 2^8, step 2^-9
-        # below 2^-6) and |v^ delta - v| <= 2^-4 |v| + 2^-10 delta
+        # below 2^-6; in Algorithm 1's order p is rounded at the step's max
+        # and then scaled down by the later rescalings, which only shrinks
+        # both terms) and |v^ delta - v| <= 2^-4 |v| + 2^-10 delta
         S = Q[0, 0] @ K[0, 0].T / math.sqrt(d)
         if causal:
             S = np.where(np.triu(np.ones((N, N), dtype=bool), 1), -np.inf, S)
@@ -598,3 +601,125 @@ def test_fp8pv_error_within_the_rounding_bound():
         err = np.abs(o8[0, 0] - exact[0, 0])
         assert np.all(err <= bound + 1e-12), float(np.max(err - bound))
         assert O.rel_l1(exact, o8) < 0.05
+
+
+def test_fp8pv_two_tile_worked_example():
+    """tests/golden/fp8_two_tile.json: a row whose running max moves between
+    its two tiles.  Algorithm 1's order rounds P~ = exp(S - m_ij) at each
+    step's max, then rescales; the worked E4M3 roundings give O = (35/24,
+    25/24) / l.  Rounding exp(S - m_final) instead (the two-pass order) gives
+    (47/32, 17/16) / l: the orders round differently, and the oracle follows
+    the pages'."""
+    import json
+    import os
+    from fractions import Fraction
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fp8_two_tile.json")))
+    N, d = 128, 64
+    S_row = np.full(N, -1000.0)
+    S_row[0], S_row[1], S_row[64] = 0.0, -1.0, math.log(3.0)
+
+    def score_fn(rows, keys):
+        return np.tile(S_row[keys.start:keys.stop], (len(rows), 1))
+
+    V = np.zeros((N, d))
+    V[:, 0] = g["v_channel_0"]["all"]
+    for key, val in g["v_channel_1"].items():
+        V[int(key), 1] = val
+    delta = O.v_channel_scales(V)
+    assert delta[0] == 2.0 ** -8 and delta[1] == 2.0 ** -7 and delta[2] == 1.0
+    V8 = O.e4m3_round(V / delta)
+    assert np.array_equal(V8, V / delta)                 # exact on the grid
+    # the worked roundings
+    assert O.e4m3_round(256 * math.exp(-1.0)) == 96.0
+    assert O.e4m3_round(256 / 3.0) == 88.0
+    assert O.e4m3_round(256 * math.exp(-1.0) / 3.0) == 32.0
+    dummy = np.zeros((N, d))
+    out, cnt, dec = O.attend_row_block(dummy, dummy, V, np.array([True, True]), 0, -np.inf, False,
+                                       score_fn=score_fn, pv8=(V8, delta))
+    l = (1.0 + math.exp(-1.0)) / 3.0 + 1.0
+    want = [float(Fraction(*g["running_max_numerators"][c])) / l for c in ("ch0", "ch1")]
+    other = [float(Fraction(*g["final_max_numerators"][c])) / l for c in ("ch0", "ch1")]
+    for r in range(N):
+        assert abs(out[r, 0] - want[0]) < 1e-12 and abs(out[r, 1] - want[1]) < 1e-12
+        assert np.all(out[r, 2:] == 0.0)
+    assert min(abs(want[0] - other[0]), abs(want[1] - other[1])) > 5e-3
+    assert cnt["pv_exec"] == 8 and np.all(dec == 1)
+    # unquantised, channel 0 is exactly 1 (it averages ones)
+    exact, _, _ = O.attend_row_block(dummy, dummy, V, np.array([True, True]), 0, -np.inf, False,
+                                     score_fn=score_fn)
+    assert np.allclose(exact[:, 0], 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(exact[:, 1], (2.0 / 3 - math.exp(-1.0) / 3 + 0.5) / l, rtol=0, atol=1e-14)
+
+
+def test_fp8pv_keeps_the_lambda_decisions_and_counts():
+    """The 8-bit operands enter only the P~V product: m, the votes, l and the
+    counters are those of the unquantised recurrence."""
+    rng = np.random.default_rng(9)
+    N, d = 300, 64
+    u = rng.standard_normal(d)
+    Q = rng.standard_normal((1, 2, N, d)) + u
+    K = rng.standard_normal((1, 1, N, d))
+    K[0, 0, :64] += 2.0 * u                  # the first key tile dominates every row
+    V = rng.standard_normal((1, 1, N, d))
+    mg = rng.random((1, 2, 3, 5)) < 0.7
+    for causal in (False, True):
+        a, ca, da = O.sparse_attention(Q, K, V, mg, -0.5, causal)
+        b, cb, db = O.sparse_attention(Q, K, V, mg, -0.5, causal, pv8=True)
+        assert ca == cb and np.array_equal(da, db)
+        assert ca["pv_skip"] > 0 and ca["pv_exec"] > 0
+        assert 0 < O.rel_l1(a, b) < 0.05
+
+
+# ---------------------------------------------------------------------------
+# the TopCdf ambiguity window the GPU parity tests exclude
+# ---------------------------------------------------------------------------
+# Dyadic rows: every prefix sum is exact, so the distance of an exclusive
+# prefix from tau * sum is the offset put into tau.  Each case lists, by
+# hand, the entries that must be flagged (exclusive prefix within 1e-4 of
+# tau * sum, or a relative near-tie within 1e-6 with the last kept entry
+# shared by another entry).
+AMBIGUITY_CASES = [
+    # p = .5, .25, .125, .0625, .0625: exclusive prefixes 0, .5, .75, .875, .9375
+    ("prefix .75 at tau*sum - 0.5e-4 (kept)", [.5, .25, .125, .0625, .0625], .75 + .5e-4, {2}, {0, 1, 2}),
+    ("prefix .75 at tau*sum + 0.5e-4 (dropped)", [.5, .25, .125, .0625, .0625], .75 - .5e-4, {2}, {0, 1}),
+    ("prefix .75 at tau*sum - 2e-4", [.5, .25, .125, .0625, .0625], .75 + 2e-4, set(), {0, 1, 2}),
+    ("prefix .75 at tau*sum + 2e-4", [.5, .25, .125, .0625, .0625], .75 - 2e-4, set(), {0, 1}),
+    # the two .0625 entries tie exactly and straddle the cut: 3 kept, 4 not
+    ("exact tie across the cut", [.5, .25, .125, .0625, .0625], .9, {3, 4}, {0, 1, 2, 3}),
+    # a near-tie (relative 2e-7) of the last kept entry and the first dropped one
+    ("near-tie across the cut", [.5, .25, .125 * (1 + 1e-7), .125 * (1 - 1e-7)], .8, {2, 3}, {0, 1, 2}),
+    # a near-tie well inside the kept set, not involving the last kept entry
+    ("near-tie away from the cut", [.3 * (1 + 1e-7), .3 * (1 - 1e-7), .25, .15], .7, set(), {0, 1, 2}),
+    # a near-tie of 2e-6 relative is not a tie
+    ("no tie at 2e-6", [.5, .25, .125 * (1 + 2e-6), .125 * (1 - 2e-6)], .8, set(), {0, 1, 2}),
+]
+
+
+@pytest.mark.parametrize("label,p,tau,flagged,kept", AMBIGUITY_CASES, ids=[c[0] for c in AMBIGUITY_CASES])
+def test_topcdf_ambiguity_marks_exactly_the_window(label, p, tau, flagged, kept):
+    p = np.array(p)
+    keep, info = O.topcdf(p, tau)
+    assert set(np.nonzero(keep)[0]) == kept
+    amb = O.topcdf_ambiguous(p, keep, info)
+    assert set(np.nonzero(amb)[0]) == flagged
+
+
+@pytest.mark.parametrize("label,p,tau,flagged,kept", AMBIGUITY_CASES, ids=[c[0] for c in AMBIGUITY_CASES])
+def test_predict_mask_head_flags_the_same_entries(label, p, tau, flagged, kept):
+    """The same rows end to end: query blocks whose mean is e_0 and key blocks
+    whose mean is sqrt(d) ln(p_j) e_0 (every token of a block equal, so every
+    block is selective) give the compressed row ln(p_j), whose softmax is p.
+    predict_mask_head flags the same entries in every query block row."""
+    p = np.array(p)
+    d, n = 64, len(p)
+    N = 64 * n
+    Q = np.zeros((N, d))
+    Q[:, 0] = 1.0
+    K = np.zeros((N, d))
+    for j in range(n):
+        K[64 * j:64 * j + 64, 0] = math.sqrt(d) * math.log(p[j] / p.sum())
+    r = O.predict_mask_head(Q, K, tau, 0.5, False)
+    assert not r["fix_q"].any() and not r["fix_k"].any()
+    for i in range(r["mg"].shape[0]):
+        assert set(np.nonzero(r["mg"][i])[0]) == kept, i
+        assert set(np.nonzero(r["ambiguous"][i])[0]) == flagged, i
