@@ -1,25 +1,39 @@
 #!/usr/bin/env python3
 """Benchmark of the SpargeAttn hot path on one MI355X.
 
-Workload: 128K-token GQA causal prefill (B=1, 32 query heads, 8 kv heads,
-N=131072, d=128, bf16; AR(1)+sink synthetic Q/K, N(0,1) V; tau=0.9,
+Headline workload: 128K-token GQA causal prefill (B=1, 32 query heads, 8 kv
+heads, N=131072, d=128, bf16; AR(1)+sink synthetic Q/K, N(0,1) V; tau=0.9,
 theta=0.5, lambda=-6).  One step = stage 1 (sparge_predict_mask: pooling,
 self-similarity, compressed map, TopCdf, forcing, row lists) + stage 2
 (sparge_attn: block-sparse attention with the lambda rule) over the resident
-inputs.  The int8 variant (sparge_quant_qk_int8 + int8-QK / fp16-PV attention)
-is timed after it and reported beside the headline.
+inputs.  The int8 variant (sparge_quant_qk_int8 + int8-QK / fp16-PV
+attention) and the fp8 P~V variant are timed after it and reported beside
+the headline.
 
-Prints one JSON line (rank 0).  The metric is dense-equivalent attention
-TFLOPS = (4 N^2 d H / 2 for causal) / step time, with the achieved sparsity
-and the mask-prediction share of the step; ``roofline`` is the attention
-kernel's executed MFMA flops per second against the bf16 dense peak.
+Also reported, each on its own resident inputs with the same warm-up and
+step counts:
+* ``configs``: the other synthetic workloads (tiny, image_dit, llm_32k, and
+  video_dit in raster and in 3D Hilbert order), each with dense-equivalent
+  TFLOPS, the three sparsities, the mask-prediction share and the attention
+  call's MFMA fraction on executed tiles; the Hilbert run also times the
+  token gather of Q, K, V and the scatter of O (sparge_hilbert_permute) and
+  reports their HBM rate;
+* ``mask_share_vs_n``: the llm_32k recipe at N = 8K ... 128K, the share of
+  the step that mask prediction takes (the analogue of the pages' Table 3);
+* ``cpu_baseline``: the float64 oracle on a bounded sample of the headline
+  workload, on the host's cores.
+
+Prints one JSON line.  The metric is dense-equivalent attention TFLOPS =
+(4 N^2 d H, halved for causal) / step time, with the achieved sparsity and
+the mask-prediction share of the step; ``roofline`` is the attention call's
+executed MFMA flops per second against the bf16 dense peak.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
+import resource
 import sys
 import time
 
@@ -32,6 +46,14 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0
+BQ, BK, ROWS = 128, 64, 32
+
+CONFIG_NAMES = ("tiny", "image_dit", "llm_32k", "video_dit_raster", "video_dit_hilbert")
+SWEEP_N = (8192, 16384, 32768, 65536, 131072)
+# the pages' Table 3 (prediction ms vs full-attention ms; hardware, heads and
+# head dim not stated), quoted as context beside the sweep
+PAGES_TABLE3 = {8192: (0.251, 6.649), 16384: (0.487, 26.83), 32768: (0.972, 106.68),
+                65536: (2.599, 424.24), 131072: (8.764, 1696.2)}
 
 
 def log(msg):
@@ -43,10 +65,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-headline", action="store_true", help="skip the 128K GQA steps (profiling runs)")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8 variant")
     ap.add_argument("--no-fp8pv", action="store_true", help="skip the fp8 P~V variant")
+    ap.add_argument("--configs", default=",".join(CONFIG_NAMES),
+                    help="comma list of the other workloads to time, or 'none'")
+    ap.add_argument("--sweep", default=",".join(str(n) for n in SWEEP_N),
+                    help="comma list of N for the mask-share sweep (llm_32k recipe), or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=150,
+    ap.add_argument("--cpu-rows", type=int, default=64,
                     help="query blocks of head 0 the CPU oracle attends (sample size)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
@@ -54,13 +81,26 @@ def parse():
     return ap.parse_args()
 
 
-def dense_equiv_flops(N, d, H, causal):
-    f = 4.0 * N * N * d * H
+def dense_equiv_flops(N, d, H, causal, B=1):
+    f = 4.0 * N * N * d * H * B
     return f / 2 if causal else f
 
 
-def executed_flops(c, d, bq=128, bk=64, rows=32):
-    return c["qk_exec"] * 2.0 * bq * bk * d + c["pv_exec"] * 2.0 * rows * bk * d
+def executed_flops(c, d):
+    return c["qk_exec"] * 2.0 * BQ * BK * d + c["pv_exec"] * 2.0 * ROWS * BK * d
+
+
+def sparsity(c, d):
+    live = c["live_tiles"] * 4.0 * BQ * BK * d
+    return {
+        "headline": 1.0 - executed_flops(c, d) / live if live else 0.0,
+        "mg_block": 1.0 - c["qk_exec"] / c["live_tiles"] if c["live_tiles"] else 0.0,
+        "lambda_skip_of_executed_groups": c["pv_skip"] / max(1, c["pv_exec"] + c["pv_skip"]),
+    }
+
+
+def stats(ms):
+    return {"mean": float(np.mean(ms)), "median": float(np.median(ms)), "min": float(np.min(ms))}
 
 
 def attn_source_digest() -> str:
@@ -74,39 +114,154 @@ def attn_source_digest() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(w, q, k, v, nblocks):
-    """The float64 oracle on a bounded sample: stage 1 for query head 0 (its
-    kv head pooled in full) and stage 2 for ``nblocks`` evenly spaced query
-    blocks of head 0.  Returns a dict with dense-equivalent TFLOPS of the
-    sampled work."""
+def cpu_baseline(w, q, k, v, nrows):
+    """The float64 oracle on a bounded sample of the workload: stage 1 for
+    query head 0 in full (its kv head pooled over all tokens) and stage 2 for
+    ``nrows`` query blocks of head 0, blocks 0, 1, 2, 3, Tm/2 - 1, Tm - 1 and
+    the rest seeded-random.  Returns the sampled work's dense-equivalent
+    TFLOPS, seconds per query block and the linear extrapolation to the whole
+    workload, and the cores the process actually kept busy (CPU time / wall
+    time)."""
     from oracle import sparge_oracle as O
-    try:
-        import threadpoolctl
-        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    ru0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
     Q0 = O.widen(q[0, 0], w.dtype)
     K0 = O.widen(k[0, 0], w.dtype)
     V0 = O.widen(v[0, 0], w.dtype)
     pred = O.predict_mask_head(Q0, K0, w.tau, w.theta, w.causal)
+    t1 = time.perf_counter()
     Tm = O.num_blocks(w.N, O.BQ)
-    blocks = sorted(set(np.linspace(0, Tm - 1, nblocks).round().astype(int).tolist()))
+    fixed = [0, 1, 2, 3, Tm // 2 - 1, Tm - 1]
+    rng = np.random.Generator(np.random.Philox(np.random.SeedSequence([20250225, 4, 99])))
+    rest = [int(x) for x in rng.permutation(Tm) if int(x) not in fixed][:max(0, nrows - len(fixed))]
+    blocks = sorted(set(fixed + rest))[:nrows]
     dense = 0.0
     for i in blocks:
         O.attend_row_block(Q0, K0, V0, pred["mg"][i], i, w.lam, w.causal)
         r = O.block_rows(w.N, O.BQ, i)
-        if w.causal:
-            pairs = sum(q_ + 1 for q_ in range(r.start, r.stop))
-        else:
-            pairs = len(r) * w.N
+        pairs = sum(q_ + 1 for q_ in range(r.start, r.stop)) if w.causal else len(r) * w.N
         dense += 4.0 * pairs * w.d
-    dt = time.perf_counter() - t0
-    return {"value": dense / dt / 1e12, "unit": "TFLOPS (dense-equivalent)", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"float64 oracle: stage 1 for query head 0 of the workload (its kv head pooled "
-                      f"over all {w.N} tokens) + stage 2 for {len(blocks)} evenly spaced query blocks "
-                      f"of head 0; {dt:.1f} s wall; dense-equivalent flops of the sampled blocks / time"}
+    t2 = time.perf_counter()
+    ru1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu_s = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+    wall = t2 - t0
+    per_block = (t2 - t1) / len(blocks)
+    extrap = (t1 - t0) * w.H * w.B + per_block * Tm * w.H * w.B
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"value": dense / (t2 - t1) / 1e12, "unit": "TFLOPS (dense-equivalent)",
+            "cores": max(1, int(round(cpu_s / wall))), "kind": "oracle",
+            "sample": (f"float64 oracle, single process: stage 1 (mask prediction) for query head 0 of the "
+                       f"128K GQA workload in full ({t1 - t0:.1f} s), then stage 2 for {len(blocks)} of its "
+                       f"{Tm} query blocks (0-3, {Tm // 2 - 1}, {Tm - 1} and seeded-random ones; "
+                       f"{t2 - t1:.1f} s, {per_block:.3f} s per block); value = the sampled blocks' "
+                       f"dense-equivalent flops / stage-2 time"),
+            "stage1_s_per_head": t1 - t0, "stage2_s_per_block": per_block,
+            "linear_extrapolation_s": extrap,
+            "cpu_s": cpu_s, "wall_s": wall, "host_cpus_in_affinity": affinity}
+
+
+class Timer:
+    """HIP events on the current stream, one row per timed step."""
+
+    def __init__(self, torch, steps, marks):
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(steps)]
+
+    def intervals(self):
+        return [[e[k].elapsed_time(e[k + 1]) for e in self.ev] for k in range(len(self.ev[0]) - 1)]
+
+
+def run_steps(torch, step, steps, warmup, marks):
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    tm = Timer(torch, steps, marks)
+    t0 = time.perf_counter()
+    out = None
+    for s in range(steps):
+        out = step(tm.ev[s])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return out, tm.intervals(), wall_ms
+
+
+def upload(torch, dev, bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(dev)
+
+
+def run_config(torch, fb, I, name, steps, warmup, dev, **over):
+    """One workload's step (predict + attend; for the Hilbert order also the
+    gather of Q, K, V and the scatter of O), timed with HIP events."""
+    base = {"tiny": 0, "image_dit": 1, "llm_32k": 2, "video_dit_raster": 3, "video_dit_hilbert": 3,
+            "llm_sweep": 2}[name]
+    w = I.workload(base, **over)
+    q, k, v = I.make_qkv(w, workers=16)
+    qd, kd, vd = (upload(torch, dev, x, w.dtype) for x in (q, k, v))
+    del q, k, v
+    hilbert = name == "video_dit_hilbert"
+    perm = None
+    if hilbert:
+        p, _ = fb.hilbert_index(*w.grid)
+        perm = torch.from_numpy(p).to(dev)
+        bufs = [torch.empty_like(x) for x in (qd, kd, vd)]
+        obuf = torch.empty_like(qd)
+    ws = fb.workspace(qd, kd)
+    torch.cuda.synchronize()
+
+    def step(ev):
+        qa, ka, va = qd, kd, vd
+        if ev is not None:
+            ev[0].record()
+        if hilbert:
+            qa, ka, va = (fb.hilbert_permute(x, perm, out=b) for x, b in zip((qd, kd, vd), bufs))
+        if ev is not None:
+            ev[1].record()
+        mask = fb.predict_mask(qa, ka, w.tau, w.theta, w.causal, ws=ws)
+        if ev is not None:
+            ev[2].record()
+        o, counts, _ = fb.attn(qa, ka, va, mask, w.lam, w.causal, ws=ws)
+        if ev is not None:
+            ev[3].record()
+        if hilbert:
+            o = fb.hilbert_permute(o, perm, inverse=True, out=obuf)
+        if ev is not None:
+            ev[4].record()
+        return counts, mask
+
+    (counts, mask), iv, wall = run_steps(torch, step, steps, warmup, 5)
+    c = fb.counts_dict(counts)
+    perm_ms = np.array(iv[0]) + np.array(iv[3])
+    pred_ms, attn_ms = iv[1], iv[2]
+    t_attn = float(np.mean(pred_ms) + np.mean(attn_ms))
+    dense = dense_equiv_flops(w.N, w.d, w.H, w.causal, w.B)
+    exe = executed_flops(c, w.d)
+    rec = {
+        "workload": name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "d": w.d, "dtype": w.dtype,
+        "causal": w.causal, "tau": w.tau, "theta": w.theta, "lambda": w.lam,
+        "order": "hilbert" if hilbert else "raster",
+        "dense_equiv_tflops": dense / (t_attn * 1e-3) / 1e12,
+        "sparsity": sparsity(c, w.d),
+        "mask_pred_share": float(np.mean(pred_ms)) / t_attn,
+        "predict_ms": stats(pred_ms), "attn_ms": stats(attn_ms),
+        "mfma_frac_executed": exe / (float(np.mean(attn_ms)) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "mean_s_q": float(mask.s_q.mean().item()), "mean_s_k": float(mask.s_k.mean().item()),
+        "counts": c,
+    }
+    if hilbert:
+        moved = 2.0 * (qd.numel() + kd.numel() + vd.numel() + qd.numel()) * qd.element_size()
+        rec["permute_ms"] = stats(perm_ms)
+        rec["permute_gbs"] = moved / (float(np.mean(perm_ms)) * 1e-3) / 1e9
+        rec["permute_bytes"] = moved
+    log(f"[bench] {name}: predict {np.mean(pred_ms):.3f} ms, attn {np.mean(attn_ms):.3f} ms, "
+        f"{rec['dense_equiv_tflops']:.0f} dense-equiv TFLOPS, sparsity {rec['sparsity']['headline']:.3f}"
+        + (f", permute {np.mean(perm_ms):.3f} ms ({rec['permute_gbs']:.0f} GB/s)" if hilbert else ""))
+    del qd, kd, vd, ws
+    if hilbert:
+        del bufs, obuf
+    return rec
 
 
 def main():
@@ -119,171 +274,156 @@ def main():
     import free_block_sparse_mask_amd as fb
     from free_block_sparse_mask_amd import inputs as I
 
-    w = I.workload(4)
     dev = torch.device("cuda:0")
-    t0 = time.perf_counter()
-    q, k, v = I.make_qkv(w, workers=16)
-    log(f"[bench] generated inputs in {time.perf_counter() - t0:.1f} s")
-
-    def up(bits, dtype):
-        t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16 if dtype == "bf16" else torch.float16)
-        return t.to(dev)
-
-    qd, kd, vd = up(q, "bf16"), up(k, "bf16"), up(v, "bf16")
-    vd16 = vd.float().to(torch.float16) if not args.no_int8 else None
-    ws = fb.workspace(qd, kd)
-    torch.cuda.synchronize()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
-        if ev is not None:
-            ev[1].record()
-        o, counts, _ = fb.attn(qd, kd, vd, mask, w.lam, w.causal)
-        if ev is not None:
-            ev[2].record()
-        return o, counts, mask
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        o, counts, mask = step(evs[s])
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
-    pred_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    c = fb.counts_dict(counts)
-    log(f"[bench] bf16 step: wall {wall_ms:.3f} ms, predict {np.mean(pred_ms):.3f} ms, "
-        f"attn {np.mean(attn_ms):.3f} ms, counts {c}")
-
-    dense = dense_equiv_flops(w.N, w.d, w.H, w.causal)
-    step_ms = float(np.mean(pred_ms) + np.mean(attn_ms))
-    live_flops = c["live_tiles"] * 4.0 * 128 * 64 * w.d
-    exe = executed_flops(c, w.d)
-    attn_avg = float(np.mean(attn_ms))
-    achieved = exe / (attn_avg * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                tj = json.load(f)
-            if tj.get("kernel_source_sha256") == attn_source_digest():
-                traffic = tj.get("attn_fwd_bytes_per_launch")
-        except Exception:
-            traffic = None
-    result = {
-        "metric": "dense-equiv attn TFLOPS + sparsity @128K GQA prefill; mask-pred % of time",
-        "value": dense / (wall_ms * 1e-3) / 1e12,
-        "unit": "TFLOPS (dense-equivalent)",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": wall_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded AR(1)+sink Q/K, N(0,1) V; no trained weights)",
-        "config": {"workload": "gqa_128k_causal_prefill", "B": w.B, "H": w.H, "H_kv": w.H_kv,
-                   "N": w.N, "d": w.d, "causal": w.causal, "tau": w.tau, "theta": w.theta,
-                   "lambda": w.lam, "bq": 128, "bk": 64},
-        "sparsity": {
-            "headline": 1.0 - exe / live_flops,
-            "mg_block": 1.0 - c["qk_exec"] / c["live_tiles"],
-            "lambda_skip_of_executed_groups": c["pv_skip"] / max(1, c["pv_exec"] + c["pv_skip"]),
-        },
-        "mask_pred_share": float(np.mean(pred_ms)) / step_ms,
-        "predict_ms": float(np.mean(pred_ms)),
-        "predict_ms_median_min": [float(np.median(pred_ms)), float(np.min(pred_ms))],
-        "attn_ms": attn_avg,
-        "attn_ms_median_min": [float(np.median(attn_ms)), float(np.min(attn_ms))],
-        "event_step_ms": step_ms,
-        "counts": c,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "transpose_v + build_packs + attn_stats (packed, then single) + sum_counts + attn_pv "
-                               "<128, bf16, causal> (one sparge_attn call)",
-                     "flops_per_launch": exe},
-    }
-
-    if not args.no_int8:
-        del o, mask
+    result = {}
+    w = I.workload(4)
+    q = k = v = None
+    if not args.no_headline:
+        t0 = time.perf_counter()
+        q, k, v = I.make_qkv(w, workers=16)
+        log(f"[bench] generated inputs in {time.perf_counter() - t0:.1f} s")
+        qd, kd, vd = (upload(torch, dev, x, "bf16") for x in (q, k, v))
+        vd16 = vd.float().to(torch.float16) if not args.no_int8 else None
+        ws = fb.workspace(qd, kd)
         torch.cuda.synchronize()
 
-        def step8(ev=None):
-            if ev is not None:
-                ev[0].record()
-            q8, k8, qs, ks = fb.quant_qk_int8(qd, kd, ws=ws)
-            if ev is not None:
-                ev[1].record()
-            mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
-            if ev is not None:
-                ev[2].record()
-            o, counts, _ = fb.attn(q8, k8, vd16, mask, w.lam, w.causal, q_scale=qs, k_scale=ks)
-            if ev is not None:
-                ev[3].record()
-            return counts
-
-        for _ in range(args.warmup):
-            step8()
-        torch.cuda.synchronize()
-        evs8 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        t8 = time.perf_counter()
-        for s in range(args.steps):
-            counts8 = step8(evs8[s])
-        torch.cuda.synchronize()
-        wall8 = (time.perf_counter() - t8) * 1e3 / args.steps
-        quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs8]))
-        pred8 = float(np.mean([e[1].elapsed_time(e[2]) for e in evs8]))
-        attn8 = float(np.mean([e[2].elapsed_time(e[3]) for e in evs8]))
-        c8 = fb.counts_dict(counts8)
-        qk_f = c8["qk_exec"] * 2.0 * 128 * 64 * w.d
-        pv_f = c8["pv_exec"] * 2.0 * 32 * 64 * w.d
-        result["int8"] = {
-            "ms_per_step": wall8, "quant_ms": quant_ms, "predict_ms": pred8, "attn_ms": attn8,
-            "dense_equiv_tflops": dense / (wall8 * 1e-3) / 1e12,
-            "mfma_frac_executed": (qk_f / (PEAK_INT8_TOPS * 1e12) + pv_f / (PEAK_BF16_TFLOPS * 1e12))
-                                  / (attn8 * 1e-3),
-            "counts": c8,
-        }
-        log(f"[bench] int8 step: wall {wall8:.3f} ms, quant {quant_ms:.3f}, predict {pred8:.3f}, attn {attn8:.3f}")
-
-    if not args.no_fp8pv:
-        # the fp8 P~V variant (sparge_attn_fp8pv) on the same bf16 inputs
-        torch.cuda.synchronize()
-
-        def step_f8(ev=None):
+        def step(ev):
             if ev is not None:
                 ev[0].record()
             mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
             if ev is not None:
                 ev[1].record()
-            o, counts, _ = fb.attn(qd, kd, vd, mask, w.lam, w.causal, ws=ws, fp8_pv=True)
+            o, counts, _ = fb.attn(qd, kd, vd, mask, w.lam, w.causal, ws=ws)
             if ev is not None:
                 ev[2].record()
             return counts
 
-        for _ in range(args.warmup):
-            step_f8()
-        torch.cuda.synchronize()
-        evsf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        tf = time.perf_counter()
-        for s in range(args.steps):
-            countsf = step_f8(evsf[s])
-        torch.cuda.synchronize()
-        wallf = (time.perf_counter() - tf) * 1e3 / args.steps
-        predf = float(np.mean([e[0].elapsed_time(e[1]) for e in evsf]))
-        attnf = float(np.mean([e[1].elapsed_time(e[2]) for e in evsf]))
-        cf = fb.counts_dict(countsf)
-        result["fp8pv"] = {
-            "ms_per_step": wallf, "predict_ms": predf, "attn_ms": attnf,
-            "dense_equiv_tflops": dense / (wallf * 1e-3) / 1e12, "counts": cf,
+        counts, iv, wall_ms = run_steps(torch, step, args.steps, args.warmup, 3)
+        pred_ms, attn_ms = iv
+        c = fb.counts_dict(counts)
+        log(f"[bench] bf16 step: wall {wall_ms:.3f} ms, predict {np.mean(pred_ms):.3f} ms, "
+            f"attn {np.mean(attn_ms):.3f} ms, counts {c}")
+        dense = dense_equiv_flops(w.N, w.d, w.H, w.causal)
+        step_ms = float(np.mean(pred_ms) + np.mean(attn_ms))
+        exe = executed_flops(c, w.d)
+        attn_avg = float(np.mean(attn_ms))
+        achieved = exe / (attn_avg * 1e-3) / 1e12
+        traffic = None
+        if os.path.exists(args.traffic_json):
+            try:
+                with open(args.traffic_json) as f:
+                    tj = json.load(f)
+                if tj.get("kernel_source_sha256") == attn_source_digest():
+                    traffic = tj.get("attn_fwd_bytes_per_launch")
+            except Exception:
+                traffic = None
+        result = {
+            "metric": "dense-equiv attn TFLOPS + sparsity @128K GQA prefill; mask-pred % of time",
+            "value": dense / (wall_ms * 1e-3) / 1e12,
+            "unit": "TFLOPS (dense-equivalent)",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": wall_ms,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic (seeded AR(1)+sink Q/K, N(0,1) V; no trained weights)",
+            "config": {"workload": "gqa_128k_causal_prefill", "B": w.B, "H": w.H, "H_kv": w.H_kv,
+                       "N": w.N, "d": w.d, "causal": w.causal, "tau": w.tau, "theta": w.theta,
+                       "lambda": w.lam, "bq": BQ, "bk": BK},
+            "sparsity": sparsity(c, w.d),
+            "mask_pred_share": float(np.mean(pred_ms)) / step_ms,
+            "predict_ms": float(np.mean(pred_ms)),
+            "predict_ms_median_min": [float(np.median(pred_ms)), float(np.min(pred_ms))],
+            "attn_ms": attn_avg,
+            "attn_ms_median_min": [float(np.median(attn_ms)), float(np.min(attn_ms))],
+            "event_step_ms": step_ms,
+            "counts": c,
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                         "kernel": "transpose_v + build_packs + attn_stats (packed, then single) + sum_counts + "
+                                   "attn_pv <128, bf16, causal> (one sparge_attn call)",
+                         "flops_per_launch": exe},
         }
-        log(f"[bench] fp8 P~V step: wall {wallf:.3f} ms, predict {predf:.3f}, attn {attnf:.3f}")
+
+        if not args.no_int8:
+            def step8(ev):
+                if ev is not None:
+                    ev[0].record()
+                q8, k8, qs, ks = fb.quant_qk_int8(qd, kd, ws=ws)
+                if ev is not None:
+                    ev[1].record()
+                mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
+                if ev is not None:
+                    ev[2].record()
+                o, counts, _ = fb.attn(q8, k8, vd16, mask, w.lam, w.causal, q_scale=qs, k_scale=ks, ws=ws)
+                if ev is not None:
+                    ev[3].record()
+                return counts
+
+            counts8, iv8, wall8 = run_steps(torch, step8, args.steps, args.warmup, 4)
+            quant_ms, pred8, attn8 = (float(np.mean(x)) for x in iv8)
+            c8 = fb.counts_dict(counts8)
+            qk_f = c8["qk_exec"] * 2.0 * BQ * BK * w.d
+            pv_f = c8["pv_exec"] * 2.0 * ROWS * BK * w.d
+            result["int8"] = {
+                "ms_per_step": wall8, "quant_ms": quant_ms, "predict_ms": pred8, "attn_ms": attn8,
+                "attn_ms_median_min": [float(np.median(iv8[2])), float(np.min(iv8[2]))],
+                "dense_equiv_tflops": dense / (wall8 * 1e-3) / 1e12,
+                "mfma_frac_executed": (qk_f / (PEAK_INT8_TOPS * 1e12) + pv_f / (PEAK_BF16_TFLOPS * 1e12))
+                                      / (attn8 * 1e-3),
+                "counts": c8,
+            }
+            log(f"[bench] int8 step: wall {wall8:.3f} ms, quant {quant_ms:.3f}, predict {pred8:.3f}, "
+                f"attn {attn8:.3f}")
+
+        if not args.no_fp8pv:
+            def step_f8(ev):
+                if ev is not None:
+                    ev[0].record()
+                mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
+                if ev is not None:
+                    ev[1].record()
+                o, counts, _ = fb.attn(qd, kd, vd, mask, w.lam, w.causal, ws=ws, fp8_pv=True)
+                if ev is not None:
+                    ev[2].record()
+                return counts
+
+            countsf, ivf, wallf = run_steps(torch, step_f8, args.steps, args.warmup, 3)
+            cf = fb.counts_dict(countsf)
+            result["fp8pv"] = {
+                "ms_per_step": wallf, "predict_ms": float(np.mean(ivf[0])), "attn_ms": float(np.mean(ivf[1])),
+                "attn_ms_median_min": [float(np.median(ivf[1])), float(np.min(ivf[1]))],
+                "dense_equiv_tflops": dense / (wallf * 1e-3) / 1e12, "counts": cf,
+            }
+            log(f"[bench] fp8 P~V step: wall {wallf:.3f} ms, predict {np.mean(ivf[0]):.3f}, "
+                f"attn {np.mean(ivf[1]):.3f}")
+        del qd, kd, vd, vd16, ws
+        torch.cuda.synchronize()
+
+    names = [] if args.configs == "none" else [n for n in args.configs.split(",") if n]
+    if names:
+        result["configs"] = {}
+        for name in names:
+            if name not in CONFIG_NAMES:
+                raise SystemExit(f"unknown config {name}")
+            result["configs"][name] = run_config(torch, fb, I, name, args.steps, args.warmup, dev)
+
+    sweep = [] if args.sweep == "none" else [int(n) for n in args.sweep.split(",") if n]
+    if sweep:
+        rows = []
+        for n in sweep:
+            r = run_config(torch, fb, I, "llm_sweep", args.steps, args.warmup, dev, N=n)
+            pages = PAGES_TABLE3.get(n)
+            rows.append({"N": n, "predict_ms": r["predict_ms"]["mean"], "attn_ms": r["attn_ms"]["mean"],
+                         "mask_pred_share": r["mask_pred_share"],
+                         "dense_equiv_tflops": r["dense_equiv_tflops"],
+                         "sparsity_headline": r["sparsity"]["headline"], "mg_block_sparsity": r["sparsity"]["mg_block"],
+                         "pages_table3_share": None if pages is None else pages[0] / pages[1]})
+        result["mask_share_vs_n"] = {"recipe": "llm_32k (B=1, H=32, d=128, causal, AR(1)+sink), N varied",
+                                     "rows": rows}
 
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4
@@ -294,9 +434,9 @@ def main():
         torch.cuda.synchronize()
         result["copy_calib_bytes_each_way"] = n * 4
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.no_headline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_blocks)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
     print(json.dumps(result), flush=True)
 
 
