@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "support.hpp"
@@ -346,12 +347,25 @@ int sparge_predict_mask(const void* q, const sparge_tensor* qs, const void* k,
 
 namespace {
 
-int attn_impl(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
-              const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
-              int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
-              const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
-              double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
-              size_t workspace_bytes, void* stream, bool pv8) {
+// One attention call after its arguments have been checked: the launch
+// arguments (workspace pointers still unset), the caller's mask and lists,
+// and whether the lists must be built from the mask.
+struct AttnCall {
+  AttnArgs a{};
+  const uint8_t* mg = nullptr;
+  bool need_lists = false;
+  bool done = false;        // an empty problem: nothing (more) to launch
+  hipStream_t st = nullptr;
+};
+
+// Every host-side check of sparge_attn except the workspace's; on success
+// fills `c`.  An empty problem zeroes the counters and sets c.done.
+int attn_prepare(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+                 const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+                 int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+                 const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+                 double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* stream, bool pv8,
+                 AttnCall& c) {
   int kind;
   if (qk_dtype == SPARGE_F16 && pv_dtype == SPARGE_F16) kind = 0;
   else if (qk_dtype == SPARGE_BF16 && pv_dtype == SPARGE_BF16) kind = 1;
@@ -389,24 +403,21 @@ int attn_impl(const void* q, const sparge_tensor* qs, const void* k, const sparg
   if (causal != 0 && causal != 1) return fail(SPARGE_EINVAL, "causal must be 0 or 1");
   if ((row_cnt == nullptr) != (row_idx == nullptr))
     return fail(SPARGE_EINVAL, "row_cnt and row_idx are given together or not at all");
+  c.st = static_cast<hipStream_t>(stream);
   if (empty_problem(qs)) {
     if (counts != nullptr) {
       const hipError_t e =
-          launch_zero_counts(reinterpret_cast<unsigned long long*>(counts), SPARGE_NUM_COUNTERS,
-                             static_cast<hipStream_t>(stream));
+          launch_zero_counts(reinterpret_cast<unsigned long long*>(counts), SPARGE_NUM_COUNTERS, c.st);
       if (e != hipSuccess) return hip_fail(e, "counter reset");
     }
-    return ok();
+    c.done = true;
+    return SPARGE_OK;
   }
   if (!q || !k || !v || !o || !mg || !counts) return fail(SPARGE_EINVAL, "null pointer");
   if (kind >= 2 && (!q_scale || !k_scale)) return fail(SPARGE_EINVAL, "int8 needs q_scale and k_scale");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(SPARGE_EINVAL, "q, k, v, o must be 16-byte aligned");
-  const bool need_lists = row_cnt == nullptr;
-  if (workspace == nullptr || workspace_bytes < sparge_workspace_size(qs, ks))
-    return fail(SPARGE_EWORKSPACE, "workspace needs %zu bytes", sparge_workspace_size(qs, ks));
-
-  AttnArgs a{};
+  AttnArgs& a = c.a;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -440,9 +451,16 @@ int attn_impl(const void* q, const sparge_tensor* qs, const void* k, const sparg
   a.lam_log2 = (float)(lambda * 1.4426950408889634);
   a.counts = reinterpret_cast<unsigned long long*>(counts);
   a.dbg = pv_dbg;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  void* base = reinterpret_cast<void*>(align256((size_t)workspace));
-  Workspace w = carve_workspace(base, a.B, a.H, a.Hkv, a.N, a.d);
+  a.row_cnt = row_cnt;
+  a.row_idx = row_idx;
+  c.mg = mg;
+  c.need_lists = row_cnt == nullptr;
+  return SPARGE_OK;
+}
+
+// Points the call at its scratch regions in `w` and launches it.
+int attn_launch(AttnCall& c, const Workspace& w) {
+  AttnArgs& a = c.a;
   a.vt = w.vt;
   a.Np = (int64_t)a.Tn * kBk;
   a.row_m = w.row_m;
@@ -456,23 +474,131 @@ int attn_impl(const void* q, const sparge_tensor* qs, const void* k, const sparg
   a.cnt_part = w.cnt_part;
   a.vpart = reinterpret_cast<float*>(w.ksum_part);   // free during an attention call
   hipError_t e = hipSuccess;   // the attention kernels overwrite every counter
-  if (need_lists) {
-    e = launch_compact(mg, (int64_t)a.B * a.H * a.Tm, a.Tm, a.Tn, a.N, causal, w.list_cnt, w.list_idx, st);
+  if (c.need_lists) {
+    e = launch_compact(c.mg, (int64_t)a.B * a.H * a.Tm, a.Tm, a.Tn, a.N, a.causal, w.list_cnt, w.list_idx, c.st);
     if (e != hipSuccess) return hip_fail(e, "mask compaction launch");
     a.row_cnt = w.list_cnt;
     a.row_idx = w.list_idx;
-  } else {
-    a.row_cnt = row_cnt;
-    a.row_idx = row_idx;
   }
-  e = launch_attn(a, st);
+  e = launch_attn(a, c.st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
+}
+
+int attn_impl(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+              const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+              int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+              const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+              double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* workspace,
+              size_t workspace_bytes, void* stream, bool pv8) {
+  AttnCall c;
+  int r = attn_prepare(q, qs, k, ks, v, vs, o, os, qk_dtype, pv_dtype, o_dtype, q_scale, k_scale, mg, row_cnt,
+                       row_idx, lambda, causal, counts, pv_dbg, stream, pv8, c);
+  if (r != SPARGE_OK || c.done) return r == SPARGE_OK ? ok() : r;
+  if (workspace == nullptr || workspace_bytes < sparge_workspace_size(qs, ks))
+    return fail(SPARGE_EWORKSPACE, "workspace needs %zu bytes", sparge_workspace_size(qs, ks));
+  void* base = reinterpret_cast<void*>(align256((size_t)workspace));
+  return attn_launch(c, carve_workspace(base, c.a.B, c.a.H, c.a.Hkv, c.a.N, c.a.d));
+}
+
+// ---------------------------------------------------------------------------
+// sparge_attn_noalloc: the scratch of one attention call in a static array
+// ---------------------------------------------------------------------------
+// Each GPU the library runs on holds its own copy of `scratch` for the life of
+// the process.  In host code the array's name is only a host-side stand-in:
+// its device address comes from hipGetSymbolAddress, once per device, and only
+// that address is ever handed to kernels.
+constexpr size_t kScratchBytes = SPARGE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device that work on `st` runs on.
+int stream_device(hipStream_t st, int& dev) {
+  hipError_t e = st == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return hip_fail(e, "finding the stream's device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPARGE_EUNSUPPORTED, "device %d out of range", dev);
+  return SPARGE_OK;
+}
+
+// Device address of `scratch` on `dev`, looked up on the first call there
+// (with that device current) and kept.
+int scratch_on(int dev, void*& ptr) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(SPARGE_EHIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = p;
+  }
+  ptr = g_scratch_ptr[dev];
+  return SPARGE_OK;
+}
+
+// The attention share of the workspace layout: only the regions the attention
+// kernels touch (the same regions, in a tighter layout, as in the full one).
+Workspace carve_attn_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d) {
+  Workspace w{};
+  const int64_t Tm = ceil_div(N, kBq), Tn = ceil_div(N, kBk);
+  const int64_t chunks = ceil_div(N, kQuantChunkRows);
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off = align256(off + bytes);
+    return r;
+  };
+  w.ksum_part = reinterpret_cast<double*>(take(8 * (size_t)(B * Hkv * chunks * d)));
+  w.list_cnt = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * H * Tm)));
+  w.list_idx = reinterpret_cast<uint16_t*>(take(2 * (size_t)(B * H * Tm * Tn)));
+  w.vt = reinterpret_cast<unsigned short*>(take(2 * (size_t)(B * Hkv * d * Tn * kBk)));
+  w.row_m = reinterpret_cast<float*>(take(4 * (size_t)(B * H * N)));
+  w.row_l = reinterpret_cast<float*>(take(4 * (size_t)(B * H * N)));
+  w.ulist = reinterpret_cast<uint32_t*>(take(4 * (size_t)(B * H * Tm * Tn)));
+  w.ucnt = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * H * Tm)));
+  w.vscale = reinterpret_cast<float*>(take(4 * (size_t)(B * Hkv * d)));
+  w.packs = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv) * (size_t)pack_slots((int)H, (int)Hkv, (int)Tm)));
+  w.npack = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
+  w.pack_next = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
+  w.cnt_part = reinterpret_cast<unsigned long long*>(take(8 * (size_t)kCountSlots * SPARGE_NUM_COUNTERS));
+  w.total = off;
+  return w;
 }
 
 }  // namespace
 
 extern "C" {
+
+int sparge_attn_noalloc(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+                        const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+                        int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+                        const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+                        double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* stream) {
+  AttnCall c;
+  int r = attn_prepare(q, qs, k, ks, v, vs, o, os, qk_dtype, pv_dtype, o_dtype, q_scale, k_scale, mg, row_cnt,
+                       row_idx, lambda, causal, counts, pv_dbg, stream, false, c);
+  if (r != SPARGE_OK || c.done) return r == SPARGE_OK ? ok() : r;
+  const size_t need = carve_attn_workspace(nullptr, qs->B, qs->H, ks->H, qs->N, qs->d).total;
+  if (need > kScratchBytes)
+    return fail(SPARGE_EWORKSPACE, "the problem needs %zu bytes of scratch; the static scratch holds %zu", need,
+                kScratchBytes);
+  int dev = 0;
+  if ((r = stream_device(c.st, dev)) != SPARGE_OK) return r;
+  void* base = nullptr;
+  if ((r = scratch_on(dev, base)) != SPARGE_OK) return r;
+  return attn_launch(c, carve_attn_workspace(base, c.a.B, c.a.H, c.a.Hkv, c.a.N, c.a.d));
+}
 
 int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
                 const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,

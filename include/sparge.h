@@ -200,6 +200,36 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
                 size_t workspace_bytes, void* stream);
 
 /*
+ * sparge_attn for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * arguments, results and errors are those of sparge_attn (SPARGE_F16 /
+ * SPARGE_BF16 / int8 QK with 16-bit P~V), without `workspace` and
+ * `workspace_bytes`: the call's scratch (the transposed V, the per-row
+ * softmax statistics and executed-tile lists passed between the two
+ * attention kernels, the row lists built from mg when row_cnt/row_idx are
+ * NULL, the pairing of dense query blocks and the partial counters) lives
+ * in a static device array of SPARGE_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends.  The call allocates nothing
+ * and frees nothing; its first use on a device looks up that device's copy
+ * of the array.
+ * A problem whose scratch exceeds the array returns SPARGE_EWORKSPACE before
+ * anything is launched; the scratch grows as
+ *   2 B H_kv d 64 Tn + 8 B H N + 6 B H Tm Tn + 8 B H_kv d ceil(N / 1024)
+ *   + small terms (bytes), which allows, e.g., B = 1, H = 8, H_kv = 2,
+ *   d = 128 up to N = 65536.
+ * Every call on one GPU shares that GPU's array and leaves its last contents
+ * there; each call rewrites every region it reads before reading it.  Calls
+ * that can overlap on one GPU (different streams, or host threads) race on
+ * the array and must not be issued.
+ */
+#define SPARGE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sparge_attn_noalloc(const void* q, const sparge_tensor* qs, const void* k, const sparge_tensor* ks,
+                        const void* v, const sparge_tensor* vs, void* o, const sparge_tensor* os,
+                        int qk_dtype, int pv_dtype, int o_dtype, const float* q_scale, const float* k_scale,
+                        const uint8_t* mg, const int32_t* row_cnt, const uint16_t* row_idx,
+                        double lambda, int causal, int64_t* counts, uint8_t* pv_dbg, void* stream);
+
+/*
  * The "SpargeAttn + Sage2" variant of stage 2 ([Review] Fig. 9): the same
  * block-sparse attention and lambda rule as sparge_attn, with P~V on 8-bit
  * floats (OCP E4M3: 4 exponent bits, bias 7, 3 mantissa bits, largest 448,

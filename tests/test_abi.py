@@ -209,3 +209,28 @@ def test_grid_order_and_l1_reject_bad_arguments():
                             None) == fb.SPARGE_EINVAL
     assert L.sparge_l1_sums(FAKE, ctypes.byref(x), fb.F16, FAKE, ctypes.byref(x), fb.F16, FAKE, FAKE, ws - 1,
                             None) == fb.SPARGE_EWORKSPACE
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """The static scratch of sparge_attn_noalloc holds 64 MiB: at B = 1,
+    H = 8, H_kv = 2, d = 128 that is N up to 65536.  A larger problem is
+    refused on the host, before any device call, naming both sizes."""
+    L = fb.lib()
+    text = open(HEADER).read()
+    assert "#define SPARGE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    q, k = _t(1, 8, 70000, 128), _t(1, 2, 70000, 128)
+    rc = L.sparge_attn_noalloc(FAKE, ctypes.byref(q), FAKE, ctypes.byref(k), FAKE, ctypes.byref(k), FAKE,
+                               ctypes.byref(q), fb.BF16, fb.BF16, fb.BF16, None, None, FAKE, None, None,
+                               -5.0, 1, FAKE, None, None)
+    assert rc == fb.SPARGE_EWORKSPACE
+    msg = L.sparge_last_error().decode()
+    assert "scratch" in msg and str(64 << 20) in msg, msg
+    # the scratch formula of the header, evaluated here, agrees on both sides of the limit
+    def need(H, Hkv, N, d):
+        Tm, Tn = -(-N // 128), -(-N // 64)
+        return 2 * Hkv * d * 64 * Tn + 8 * H * N + 6 * H * Tm * Tn + 8 * Hkv * d * -(-N // 1024)
+    assert need(8, 2, 70000, 128) > 64 << 20 > need(8, 2, 65536, 128)
+    # the other argument checks are sparge_attn's
+    assert L.sparge_attn_noalloc(FAKE, ctypes.byref(q), FAKE, ctypes.byref(k), FAKE, ctypes.byref(k), FAKE,
+                                 ctypes.byref(q), fb.BF16, fb.BF16, fb.BF16, None, None, FAKE, None, None,
+                                 0.5, 1, FAKE, None, None) == fb.SPARGE_EINVAL
