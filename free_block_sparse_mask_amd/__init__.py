@@ -33,6 +33,7 @@ SPARGE_EUNSUPPORTED = -2
 SPARGE_EWORKSPACE = -3
 SPARGE_EHIP = -4
 F16, BF16, I8, F32 = 0, 1, 2, 3
+PATH_AUTO, PATH_TWO_PASS, PATH_FUSED = 0, 1, 2
 ORDER_HILBERT, ORDER_ROWMAJOR, ORDER_TIMEMAJOR = 0, 1, 2
 BQ, BK = 128, 64
 COUNTER_NAMES = ("live_tiles", "qk_exec", "qk_skip", "pv_exec", "pv_skip", "pv_void",
@@ -58,6 +59,7 @@ _SIGNATURES = {
     "sparge_last_error": (ctypes.c_char_p, []),
     "sparge_rows_per_wave": (ctypes.c_int, []),
     "sparge_workspace_size": (ctypes.c_size_t, [_TP, _TP]),
+    "sparge_attn_path": (ctypes.c_int, [ctypes.c_int]),
     "sparge_hilbert_index": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "sparge_hilbert_permute": (ctypes.c_int, [_vp, _TP, _vp, _TP, ctypes.c_int, _vp, ctypes.c_int, _vp]),
     "sparge_quant_qk_int8": (ctypes.c_int, [_vp, _TP, _vp, _TP, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
@@ -106,6 +108,17 @@ def _check(fn: str, rc: int) -> None:
 
 def rows_per_wave() -> int:
     return lib().sparge_rows_per_wave()
+
+
+def attn_path(path: Optional[int] = None) -> int:
+    """The stage-2 path of later calls, process-wide (sparge_attn_path):
+    PATH_AUTO (a pilot on the device chooses per call), PATH_TWO_PASS or
+    PATH_FUSED.  With ``path`` None, only returns the current setting;
+    otherwise sets it and returns the previous one."""
+    rc = lib().sparge_attn_path(-1 if path is None else int(path))
+    if rc < 0:
+        _check("sparge_attn_path", rc)
+    return rc
 
 
 def desc(x) -> SpargeTensor:

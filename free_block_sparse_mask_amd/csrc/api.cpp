@@ -1,6 +1,7 @@
 // C ABI of libsparge: argument checks, workspace carving and kernel launches.
 // Every check runs on the host before anything is enqueued.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -15,6 +16,7 @@ namespace sparge {
 namespace {
 
 thread_local std::string g_last_error;
+std::atomic<int> g_attn_path{kPathAuto};   // sparge_attn_path()
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -123,6 +125,8 @@ Workspace carve_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t
   w.npack = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
   w.pack_next = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
   w.cnt_part = reinterpret_cast<unsigned long long*>(take(8 * (size_t)kCountSlots * SPARGE_NUM_COUNTERS));
+  w.path_flag = reinterpret_cast<int32_t*>(take(4));
+  w.pilot_cnt = reinterpret_cast<unsigned long long*>(take(16));
   w.total = off;
   return w;
 }
@@ -138,6 +142,13 @@ int sparge_version(void) { return 10000; }
 const char* sparge_last_error(void) { return g_last_error.c_str(); }
 
 int sparge_rows_per_wave(void) { return kRowsPerWave; }
+
+int sparge_attn_path(int path) {
+  if (path != -1 && path != SPARGE_PATH_AUTO && path != SPARGE_PATH_TWO_PASS && path != SPARGE_PATH_FUSED)
+    return fail(SPARGE_EINVAL, "unknown attention path %d", path);
+  if (path == -1) return g_attn_path.load();
+  return g_attn_path.exchange(path);
+}
 
 size_t sparge_workspace_size(const sparge_tensor* q, const sparge_tensor* k) {
   if (q == nullptr || k == nullptr || q->B < 0 || q->H < 0 || q->N < 0 || q->d <= 0 || k->H <= 0)
@@ -473,6 +484,9 @@ int attn_launch(AttnCall& c, const Workspace& w) {
   a.pack_next = w.pack_next;
   a.cnt_part = w.cnt_part;
   a.vpart = reinterpret_cast<float*>(w.ksum_part);   // free during an attention call
+  a.path_flag = w.path_flag;
+  a.pilot_cnt = w.pilot_cnt;
+  a.path = g_attn_path.load(std::memory_order_relaxed);
   hipError_t e = hipSuccess;   // the attention kernels overwrite every counter
   if (c.need_lists) {
     e = launch_compact(c.mg, (int64_t)a.B * a.H * a.Tm, a.Tm, a.Tn, a.N, a.causal, w.list_cnt, w.list_idx, c.st);
@@ -572,6 +586,8 @@ Workspace carve_attn_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, in
   w.npack = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
   w.pack_next = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
   w.cnt_part = reinterpret_cast<unsigned long long*>(take(8 * (size_t)kCountSlots * SPARGE_NUM_COUNTERS));
+  w.path_flag = reinterpret_cast<int32_t*>(take(4));
+  w.pilot_cnt = reinterpret_cast<unsigned long long*>(take(16));
   w.total = off;
   return w;
 }

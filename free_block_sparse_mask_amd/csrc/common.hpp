@@ -70,8 +70,20 @@ struct Workspace {
   int32_t* npack;      // [B,Hkv]
   int32_t* pack_next;  // [B,Hkv] next unclaimed pack of each kv head
   unsigned long long* cnt_part;   // [kCountSlots][SPARGE_NUM_COUNTERS]
+  // attention path of the call (two passes or one fused pass) and the
+  // pilot's vote counts that choose it
+  int32_t* path_flag;             // [1]
+  unsigned long long* pilot_cnt;  // [2]: sampled (tile, wavefront) votes, sampled pairs
   size_t total;
 };
+
+// attention paths (the values of SPARGE_PATH_* in include/sparge.h)
+constexpr int kPathAuto = 0;
+constexpr int kPathTwoPass = 1;
+constexpr int kPathFused = 2;
+// pilot: at most this many sampled query blocks, this many listed tiles each
+constexpr int kPilotBlocks = 256;
+constexpr int kPilotTiles = 4;
 
 constexpr int kQuantChunkRows = 1024;       // tokens per partial K column sum
 
@@ -114,6 +126,9 @@ struct AttnArgs {
   float lam_log2;     // lambda * log2(e)
   unsigned long long* counts;
   uint8_t* dbg;
+  int path;           // kPathAuto, kPathTwoPass or kPathFused (requested)
+  int32_t* path_flag;             // workspace: the path the call takes; null: two passes, no flag
+  unsigned long long* pilot_cnt;  // workspace: the pilot's counts
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 

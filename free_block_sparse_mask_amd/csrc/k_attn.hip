@@ -201,6 +201,12 @@ __device__ __forceinline__ bool map_block(const AttnArgs& p, int T, int& b, int&
   return r >= 0 && b < p.B;
 }
 
+// Whether the call's path flag (written on the device by pilot_decide) names
+// `path`; a call without a flag always takes two passes.
+__device__ __forceinline__ bool path_is(const AttnArgs& p, int path) {
+  return p.path_flag != nullptr && __builtin_amdgcn_readfirstlane(*p.path_flag) == path;
+}
+
 // ---------------------------------------------------------------------------
 // Geometry shared by both passes
 // ---------------------------------------------------------------------------
@@ -486,6 +492,7 @@ void attn_stats(AttnArgs p) {
   __shared__ unsigned long long red[NW][4];
   __shared__ int pick[2];
 
+  if (path_is(p, kPathFused)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int member = wave / kWavesPerBlock, wq = wave % kWavesPerBlock;
   int b, h, i;
@@ -855,6 +862,7 @@ void attn_pv(AttnArgs p) {
   constexpr int VCWX = PV8 ? G::V8CW : G::VCW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
+  if (path_is(p, kPathFused)) return;
   int b, h, i;
   if (!map_block(p, p.Tm, b, h, i)) return;
   Lane<D, KIND, kWavesPerBlock> L;
@@ -1047,6 +1055,387 @@ void attn_pv(AttnArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One fused pass in Algorithm 1's order, and the pilot that chooses it
+// ---------------------------------------------------------------------------
+// The two passes above pay for their split with a second QK^T on every tile
+// some wavefront votes for.  When most (tile, wavefront) pairs vote that is
+// most of the tiles, and one pass that streams V beside K is cheaper.  The
+// pilot estimates the vote rate of the call from a sample; pilot_decide
+// writes the path every later kernel of the call reads.
+
+// Row maxima of one tile of S^T for this wavefront (log2 units, scaled):
+// the QK^T MFMAs on the K tile at `kt`, the dead scores masked.  The scores
+// stay in `sv`.
+template <int D, int KIND, bool CAUSAL>
+__device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KIND, kWavesPerBlock>& L,
+                                             const unsigned char* kt, int j, f32x16 (&sv)[2]) {
+  using G = Geo<D, KIND>;
+  constexpr int KLA = 2;      // k-steps the operand reads run ahead of the MFMAs
+  u32x4 kf[G::QS][2];
+#pragma unroll
+  for (int s = 0; s < G::QS; ++s)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      kf[s][t] = *reinterpret_cast<const u32x4*>(kt + t * 32 * G::KROW + (L.k_rd ^ (32u * s)));
+  sv[0] = f32x16{};
+  sv[1] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < G::QS; ++s)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sv[t] = mfma16<KIND == 1>(kf[s][t], L.qf[s], sv[t]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * KLA, 0);
+#pragma unroll
+  for (int s = 0; s < G::QS - KLA; ++s) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * KLA, 0);
+  mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
+  float mq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int o = 8 * (q & 1);
+    float m = kNegInf;
+#pragma unroll
+    for (int x = 0; x < 8; x += 2) m = fmaxf(fmaxf(m, sv[q >> 1][o + x]), sv[q >> 1][o + x + 1]);
+    mq[q] = m;
+  }
+  return max_halves(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * p.scale_log2;
+}
+
+// Pilot: sampled query block g * stride + stride / 2 of the B H Tm (in
+// (b, h, i) order).  Its first listed tile seeds the running max; up to
+// kPilotTiles - 1 further listed tiles, one from each equal stratum of the
+// rest of the list, are visited in list order, each voting per wavefront
+// against the running max of the sample so far, as the lambda rule votes
+// against the running max.  Every sampled tile stands for the listed tiles
+// of its stratum (the first for itself), so the counts weigh long rows by
+// their work.  The weighted votes and (tile, wavefront) pairs with a visible
+// key go to pilot_cnt[0] and [1].  The sampled K tiles go through
+// kPilotSlots LDS slots, that many loads in flight at a time.
+constexpr int kPilotSlots = 4;
+template <int D, int KIND>
+size_t pilot_lds_bytes() {
+  return (size_t)kPilotSlots * Geo<D, KIND>::K_BYTES;
+}
+template <int D, int KIND, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
+  static_assert(KIND <= 1, "the fused path takes 16-bit Q/K only");
+  static_assert(kPilotTiles % kPilotSlots == 0, "whole rounds of slots");
+  static_assert(kPilotTiles - 1 <= 7 && 840 % 7 == 0, "840 = lcm(1..8) divides by every stratum count");
+  using G = Geo<D, KIND>;
+  using LN = Lane<D, KIND, kWavesPerBlock>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const long long total = (long long)p.B * p.H * p.Tm;
+  long long g = (long long)blockIdx.x * stride + stride / 2;
+  if (g >= total) g = (long long)blockIdx.x * stride;
+  if (g >= total) return;
+  const int i = (int)(g % p.Tm);
+  const int bh = (int)(g / p.Tm);
+  const int b = bh / p.H, h = bh % p.H;
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  LN L;
+  L.init(p, b, h, i, wave);
+  const int n_live = live_tiles<CAUSAL>(p, i);
+  const int UC = p.row_cnt[L.row_id];
+  const bool dense = UC == n_live;
+  const uint16_t* gl = p.row_idx + L.row_id * p.Tn;
+  // the same in every wavefront of the block: strata after the first tile,
+  // and tiles loaded
+  const int S = UC > 1 ? min(kPilotTiles - 1, UC - 1) : 0;
+  const int NL = UC > 0 ? 1 + S : 0;
+  const uint32_t slots = lds_addr(smem);
+  // sample k: the first listed entry (k = 0), or the middle of stratum k - 1
+  // of entries 1 .. UC - 1
+  auto tile_of = [&](int k) -> int {
+    const int e = k == 0 ? 0 : 1 + (int)((long long)(2 * k - 1) * (UC - 1) / (2 * S));
+    return __builtin_amdgcn_readfirstlane(dense ? e : (int)gl[e]);
+  };
+  float mk[kPilotTiles];
+#pragma unroll
+  for (int r0 = 0; r0 < kPilotTiles; r0 += kPilotSlots) {
+    if (r0 < NL) {
+#pragma unroll
+      for (int u = 0; u < kPilotSlots; ++u)
+        if (r0 + u < NL) L.issue_k(p, tile_of(r0 + u), slots + (uint32_t)(u * G::K_BYTES));
+      wait_barrier<0>();      // the round's tiles have landed for every wavefront
+#pragma unroll
+      for (int u = 0; u < kPilotSlots; ++u) {
+        mk[r0 + u] = kNegInf;
+        if (r0 + u < NL) {
+          f32x16 sv[2];
+          mk[r0 + u] = tile_scores<D, KIND, CAUSAL>(p, L, smem + u * G::K_BYTES, tile_of(r0 + u), sv);
+        }
+      }
+      __syncthreads();        // every wavefront is done with the slots
+    } else {
+#pragma unroll
+      for (int u = 0; u < kPilotSlots; ++u) mk[r0 + u] = kNegInf;
+    }
+  }
+  // the first tile votes wherever a row sees a key (m_new = its own max)
+  unsigned long long v_first = __any(mk[0] > kNegInf) ? 1 : 0;
+  unsigned long long votes = 0, pairs = 0;
+  float m_run = mk[0];
+#pragma unroll
+  for (int k = 1; k < kPilotTiles; ++k) {
+    if (k < NL) {
+      const float m_new = fmaxf(m_run, mk[k]);
+      const bool fin = mk[k] > kNegInf;
+      const bool v = fin && !(mk[k] - m_new < p.lam_log2);
+      if (__any(fin)) {
+        pairs += 1;
+        votes += __any(v) ? 1 : 0;
+      }
+      m_run = m_new;
+    }
+  }
+  const unsigned long long w_first = 840, w_stratum = S > 0 ? (unsigned long long)(UC - 1) * (840 / S) : 0;
+  if (lane == 0 && (pairs > 0 || v_first > 0)) {
+    atomicAdd(p.pilot_cnt, votes * w_stratum + v_first * w_first);
+    atomicAdd(p.pilot_cnt + 1, pairs * w_stratum + v_first * w_first);
+  }
+}
+
+// The call's path: the requested one, or for kPathAuto the fused pass when
+// at least nine tenths of the pilot's weighted (tile, wavefront) pairs voted.
+// A short sample sets new maxima more often than the whole row does, so the
+// pilot can only overstate the rate: it reads 0.67 where 26% of the pairs
+// vote (the llm recipe at 8K) and 1.0 where all do (image, video).  The fused
+// pass pays off only near full rates (it is 28% faster at 100% and 9%
+// slower at 12%), hence the high bar.
+__global__ void pilot_decide(AttnArgs p) {
+  if (threadIdx.x != 0) return;
+  int path = p.path;
+  if (path != kPathTwoPass && path != kPathFused) {
+    const unsigned long long v = p.pilot_cnt[0], n = p.pilot_cnt[1];
+    path = (n > 0 && 10 * v >= 9 * n) ? kPathFused : kPathTwoPass;
+  }
+  *p.path_flag = path;
+}
+
+template <int D, int KIND>
+size_t fused_lds_bytes(int Tn) {
+  using G = Geo<D, KIND>;
+  return (size_t)G::NS2 * G::E_BYTES + (size_t)2 * ((Tn + 1) & ~1) + (size_t)4 * kWavesPerBlock * ((Tn + 15) / 16);
+}
+
+// The fused pass: one workgroup of 4 wavefronts per query block (the grid
+// order of attn_pv), its listed K tiles and V^T tiles through a ring of LDS
+// slots (the slots and loads of attn_pv).  Per tile, as Algorithm 1 orders
+// it: S = Q K^T, the running max m and row sum l (eq. 1), the wavefront's
+// lambda vote, and, when the vote runs P~V, O = exp(m_old - m_new) O +
+// P~ V with P~ = exp(S - m_new) rounded to V's type.  O is rescaled whenever
+// m grows, whether or not the tile runs P~V.  A tile whose rows all lie more
+// than kFarLog2 below their running max leaves m, l and O as they are (their
+// P~ are below 2^-40; see attn_stats); its vote is still counted.  The votes,
+// the decision map and the counters are those of attn_stats.
+template <int D, int KIND, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fused(AttnArgs p) {
+  static_assert(KIND <= 1, "the fused path takes 16-bit Q/K only");
+  using G = Geo<D, KIND>;
+  using LN = Lane<D, KIND, kWavesPerBlock>;
+  constexpr int NS = G::NS2;
+  constexpr int EB = G::E_BYTES;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ unsigned long long red[kWavesPerBlock][4];
+
+  if (!path_is(p, kPathFused)) return;
+  int b, h, i;
+  if (!map_block(p, p.Tm, b, h, i)) return;
+  LN L;
+  L.init(p, b, h, i, (int)(threadIdx.x >> 6));
+  const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
+  const long long row_id = L.row_id;
+  const int last_q = min(p.N, (i + 1) * kBq) - 1;
+  const int n_live = live_tiles<CAUSAL>(p, i);
+  const int UC = p.row_cnt[row_id];
+  const bool dense = UC == n_live;             // the list is 0, 1, ..., live - 1
+  const int nwords = (p.Tn + 15) / 16;
+  uint16_t* lst = reinterpret_cast<uint16_t*>(smem + NS * EB);
+  uint32_t* votes = reinterpret_cast<uint32_t*>(smem + NS * EB + 2 * ((p.Tn + 1) & ~1));
+  if (!dense) {
+    const uint16_t* gl = p.row_idx + row_id * p.Tn;
+    for (int e = tid; e < UC; e += kThreads) lst[e] = gl[e];
+  }
+  __syncthreads();
+  auto entry_tile = [&](int e) -> int { return dense ? e : (int)lst[e]; };
+
+  // V^T tiles: rows of 128 bytes, granules XOR-swizzled by row / 2 (attn_pv)
+  const unsigned char* vtbase =
+      reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + L.hk) * D) * p.Np * 2;
+  const int v_row0 = 16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP) + lane / 8;
+  const uint32_t v_off = (uint32_t)(v_row0 * p.Np * 2) + (uint32_t)(((lane % 8) ^ ((v_row0 / 2) % 8)) * 16);
+  const uint32_t v_wl = (uint32_t)((16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP)) * G::VROW);
+  const int vsw = (l32 / 2) % 8;
+  const uint32_t v_rd = (uint32_t)(l32 * G::VROW) + (uint32_t)((vsw & ~1) * 16) + (uint32_t)((hl ^ (vsw & 1)) * 16);
+  const uint32_t ring_lds = lds_addr(smem);
+  auto issue = [&](int e, int slot) {
+    const int j = __builtin_amdgcn_readfirstlane(entry_tile(e));
+    const uint32_t sl = ring_lds + (uint32_t)(slot * EB);
+    L.issue_k(p, j, sl);
+#pragma unroll
+    for (int c = 0; c < G::VCW; ++c) {
+      const int row_c = 16 * c * (4 / G::VGRP);
+      const unsigned char* base = uniform_ptr(vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2);
+      dma16(base, v_off, (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + row_c * G::VROW + v_wl)));
+    }
+  };
+
+  f32x16 oacc[G::OT];
+#pragma unroll
+  for (int t = 0; t < G::OT; ++t) oacc[t] = f32x16{};
+  float m_run = kNegInf;      // running max, log2 units
+  float l_half = 0.0f;        // this lane half's share of the row sum
+  int n_exec = 0, n_skip = 0, n_void = 0;
+  uint32_t vw = 0;
+
+  // entry e is used in step e; entries e+1 .. e+NS-2 are in flight when step e
+  // starts, and step e refills the slot entry e-1 used with entry e+NS-1
+  const int pre = min(UC, NS - 1);
+  for (int t = 0; t < pre; ++t) issue(t, t);
+  for (int e = 0; e < UC; ++e) {
+    const int pend = min(UC - 1, e + NS - 2) - e;
+    wait_pending<LN::KCW + G::VCW, NS - 2>(pend);
+    if (e + NS - 1 < UC) issue(e + NS - 1, (e + NS - 1) % NS);
+    const int j = __builtin_amdgcn_readfirstlane(entry_tile(e));
+    const unsigned char* kt = smem + (e % NS) * EB;
+    const unsigned char* vt = kt + G::K_BYTES;
+    f32x16 sv[2];
+    const float mloc = tile_scores<D, KIND, CAUSAL>(p, L, kt, j, sv);
+    const float m_new = fmaxf(m_run, mloc);
+    const bool finite_row = mloc > kNegInf;
+    const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
+    const bool any_finite = __any(finite_row);
+    const bool exec = __any(wants_pv);
+    const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
+    if (!far) {
+      const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[t][r] = fast_exp2(fmaf(sv[t][r], p.scale_log2, neg_m));
+      float ps[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x16& vv = sv[q >> 2];
+        const int o = 4 * (q & 3);
+        ps[q] = (vv[o] + vv[o + 1]) + (vv[o + 2] + vv[o + 3]);
+      }
+      l_half = alpha * l_half + (((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      }
+      if (exec) {
+        // P~ in V's type as the B operand of 4 k-steps, then O^T += V_j^T P~^T
+        u32x4 pb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int tt = s >> 1, r0 = 8 * (s & 1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pb[s][q] = pack2<G::PVBF>(sv[tt][r0 + 2 * q], sv[tt][r0 + 2 * q + 1]);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t off = v_rd ^ (32u * s);
+#pragma unroll
+          for (int t = 0; t < G::OT; ++t) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(vt + t * 32 * G::VROW + off);
+            oacc[t] = mfma16<G::PVBF>(a, pb[s], oacc[t]);
+          }
+        }
+      }
+    }
+    m_run = m_new;
+    const uint32_t code = exec ? 1u : (any_finite ? 2u : 3u);
+    n_exec += exec ? 1 : 0;
+    n_skip += (!exec && any_finite) ? 1 : 0;
+    n_void += any_finite ? 0 : 1;
+    vw |= code << (2 * (e & 15));
+    if ((e & 15) == 15 || e == UC - 1) {
+      votes[wave * nwords + (e >> 4)] = vw;
+      vw = 0;
+    }
+  }
+  wait_barrier<0>();                       // every vote word is written
+
+  // ---- epilogue: O / l, as attn_pv stores it ----
+  const float l_tot = sum_halves(l_half);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (L.qvalid && p.out_f32) {
+    float* ob = static_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)L.qrow * p.o_sn;
+#pragma unroll
+    for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x4 w = {__float_as_uint(oacc[t][4 * g + 0] * inv), __float_as_uint(oacc[t][4 * g + 1] * inv),
+                   __float_as_uint(oacc[t][4 * g + 2] * inv), __float_as_uint(oacc[t][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x4*>(ob + 32 * t + 8 * g + 4 * hl) = w;
+      }
+  } else if (L.qvalid) {
+    unsigned short* ob =
+        static_cast<unsigned short*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)L.qrow * p.o_sn;
+#pragma unroll
+    for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          y[q] = oacc[t][4 * g + q] * inv;
+          asm volatile("" : "+v"(y[q]));
+        }
+        u32x2 w = {pack2<G::PVBF>(y[0], y[1]), pack2<G::PVBF>(y[2], y[3])};
+        *reinterpret_cast<u32x2*>(ob + 32 * t + 8 * g + 4 * hl) = w;
+      }
+  }
+
+  // ---- decision map and counters, as attn_stats writes them ----
+  if (p.dbg != nullptr) {
+    uint8_t* drow = p.dbg + row_id * p.Tn * kWavesPerBlock;
+    for (int x = tid; x < UC * kWavesPerBlock; x += kThreads) {
+      const int e2 = x / kWavesPerBlock, w = x % kWavesPerBlock;
+      if (i * kBq + w * kRowsPerWave < p.N)
+        drow[entry_tile(e2) * kWavesPerBlock + w] =
+            (uint8_t)((votes[w * nwords + (e2 >> 4)] >> (2 * (e2 & 15))) & 3u);
+    }
+  }
+  const bool empty = L.qvalid && hl == 0 && !(l_tot > 0.0f);
+  const unsigned long long n_empty = __popcll(__ballot(empty));
+  if (lane == 0) {
+    red[wave][0] = (unsigned long long)n_exec;
+    red[wave][1] = (unsigned long long)n_skip;
+    red[wave][2] = (unsigned long long)n_void;
+    red[wave][3] = n_empty;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long ex = 0, sk = 0, vo = 0, em = 0;
+    unsigned long long* cp = p.cnt_part + (blockIdx.x % kCountSlots) * SPARGE_NUM_COUNTERS;
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      if (i * kBq + w * kRowsPerWave >= p.N) continue;   // no rows: no group
+      ex += red[w][0];
+      sk += red[w][1];
+      vo += red[w][2];
+      em += red[w][3];
+    }
+    atomicAdd(cp + SPARGE_CNT_LIVE, (unsigned long long)n_live);
+    atomicAdd(cp + SPARGE_CNT_QK_EXEC, (unsigned long long)UC);
+    atomicAdd(cp + SPARGE_CNT_QK_SKIP, (unsigned long long)(n_live - UC));
+    atomicAdd(cp + SPARGE_CNT_PV_EXEC, ex);
+    atomicAdd(cp + SPARGE_CNT_PV_SKIP, sk);
+    atomicAdd(cp + SPARGE_CNT_PV_VOID, vo);
+    atomicAdd(cp + SPARGE_CNT_EMPTY_ROWS, em);
+    atomicAdd(cp + SPARGE_CNT_ROWS, (unsigned long long)(last_q - i * kBq + 1));
+  }
+}
+
 // V [B,Hkv,N,D] (strided, 16-bit) -> V^T [B,Hkv,D,Np], zero past N; 64 x 64 tiles.
 __global__ __launch_bounds__(kThreads) void transpose_v(AttnArgs p) {
   __shared__ __attribute__((aligned(16))) unsigned short tile[64][72];
@@ -1178,14 +1567,44 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 }
 
 template <int D, int KIND, bool CAUSAL, bool PV8>
-hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
+  // 16-bit Q/K with 16-bit P~V may take the fused pass; the others always
+  // take two passes (no path flag)
+  constexpr bool FUSABLE = KIND <= 1 && !PV8;
+  AttnArgs a = a0;
+  if (!FUSABLE) a.path_flag = nullptr;
   const long long blocks = (long long)a.B * a.H * a.Tm;
   const long long packs = (long long)a.B * a.Hkv * (pack_slots(a.H, a.Hkv, a.Tm) / kPackBlocks);
   const size_t lds1 = stats_lds_bytes<D, KIND, 1>(a.Tn);
   const size_t lds1p = stats_lds_bytes<D, KIND, kPackBlocks>(a.Tn);
   const size_t lds2 = pv_lds_bytes<D, KIND, PV8>(a.Tn);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL, 1>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+  hipError_t e = hipSuccess;
+  if constexpr (FUSABLE) {
+    // the path of this call, on the device: the pilot's estimate or the request
+    if (a.path != kPathTwoPass && a.path != kPathFused) {
+      hipLaunchKernelGGL(zero_u64, dim3(1), dim3(64), 0, st, a.pilot_cnt, 2);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const long long stride = (blocks + kPilotBlocks - 1) / kPilotBlocks;
+      const long long n = (blocks + stride - 1) / stride;
+      const size_t ldsp = pilot_lds_bytes<D, KIND>();
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pilot<D, KIND, CAUSAL>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsp);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_pilot<D, KIND, CAUSAL>), dim3((unsigned)n), dim3(kThreads), ldsp, st, a,
+                         (int)stride);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(pilot_decide, dim3(1), dim3(64), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fused_lds_bytes<D, KIND>(a.Tn));
+    if (e != hipSuccess) return e;
+  }
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL, 1>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL, kPackBlocks>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1p);
@@ -1204,6 +1623,12 @@ hipError_t launch_passes(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL, 1>), dim3((unsigned)blocks), dim3(kThreads), lds1, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (FUSABLE) {
+    const size_t ldsf = fused_lds_bytes<D, KIND>(a.Tn);
+    hipLaunchKernelGGL((attn_fused<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), ldsf, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(sum_counts, dim3(1), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -81,6 +81,35 @@ const char* sparge_last_error(void);
  * rows I_w of warp i_w). */
 int sparge_rows_per_wave(void);
 
+/*
+ * How sparge_attn (and sparge_attn_noalloc) run stage 2 for 16-bit Q/K/V.
+ * Both paths compute the same method ([Review] eq. 1, the sparse warp online
+ * softmax rule, Algorithm 1) with the same lambda decisions and counters;
+ * they round P~ at different points:
+ *   SPARGE_PATH_TWO_PASS: a statistics pass (running max, row sums, votes;
+ *     K only) and a P~V pass over the tiles some wavefront voted for, which
+ *     recomputes S there and uses P~ = exp(S - final row max).  Cheap when few
+ *     (tile, wavefront) pairs vote.
+ *   SPARGE_PATH_FUSED: one pass streaming K and V together, Algorithm 1's own
+ *     order (P~ = exp(S - running max), O rescaled as the max grows), P~V
+ *     skipped for the wavefronts whose vote says so.  Cheap when most vote.
+ *   SPARGE_PATH_AUTO (the default): per call, a pilot on the device takes
+ *     up to 256 sampled query blocks, seeds a running max with each block's
+ *     first listed tile, and votes 3 more listed tiles (one per stratum of
+ *     the list) against it; the call takes the fused path when at least nine
+ *     tenths of the sampled (tile, wavefront) pairs vote, each sample
+ *     weighted by the listed tiles it stands for.  Nothing is read back to
+ *     the host.
+ * int8 Q/K and the fp8 P~V variant always take two passes.
+ * sparge_attn_path(p) sets the path of later calls process-wide and returns
+ * the previous setting; sparge_attn_path(-1) only returns it.  An unknown p
+ * returns SPARGE_EINVAL.
+ */
+#define SPARGE_PATH_AUTO 0
+#define SPARGE_PATH_TWO_PASS 1
+#define SPARGE_PATH_FUSED 2
+int sparge_attn_path(int path);
+
 /* Bytes of device workspace any entry point below needs for Q of `q` and K/V
  * of `k` (same B, N, d; k->H = H_kv).  0 for invalid shapes. */
 size_t sparge_workspace_size(const sparge_tensor* q, const sparge_tensor* k);

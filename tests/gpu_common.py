@@ -16,6 +16,7 @@ Acceptance (per component):
 """
 from __future__ import annotations
 
+import contextlib
 import math
 import sys
 from typing import Optional
@@ -276,3 +277,13 @@ def check_fp8(og: np.ndarray, ref: np.ndarray, room: np.ndarray, rows=None) -> d
     assert rep["max_over_room"] <= 0.0, rep
     assert rep["rel_l1"] <= FP8_REL_L1 and rep["cos"] >= FP8_COS, rep
     return rep
+
+
+@contextlib.contextmanager
+def attn_path(path: int):
+    """Runs the body with the stage-2 path forced process-wide, then restores it."""
+    old = fb.attn_path(path)
+    try:
+        yield
+    finally:
+        fb.attn_path(old)

@@ -229,3 +229,22 @@ def test_largest_supported_sequence(H, H_kv, causal):
     log(f"   counts {c}")
     _check_heads(w, q, k, v, mask, dbg, o32, list(range(w.H)), o16=o16,
                  extra_blocks=_random_blocks(w, 8, seed=150 + w.H))
+
+
+def test_full_size_llm_32k_fused_path():
+    """The fused stage-2 path forced on the llm_32k workload (causal, 32
+    heads, lists up to 512 tiles; the automatic choice takes two passes
+    there): sampled mask rows and blocks against the oracle, whole-output
+    properties, and the two-pass path's counters."""
+    from gpu_common import attn_path
+    w = I.workload(2)
+    log(f"[full] {w.name} on the fused path")
+    q, k, v = I.make_qkv(w, workers=16)
+    with attn_path(fb.PATH_FUSED):
+        mask, counts, dbg, o16, o32 = _run(w, q, k, v)
+    with attn_path(fb.PATH_TWO_PASS):
+        _, counts2, dbg2, _, _ = _run(w, q, k, v)
+    assert torch.equal(counts, counts2) and torch.equal(dbg, dbg2)
+    c = _check_whole(w, mask, counts, o16, o32)
+    log(f"   counts {c}")
+    _check_heads(w, q, k, v, mask, dbg, o32, [0, 31], o16=o16, extra_blocks=_random_blocks(w, 24, seed=170))

@@ -1,0 +1,205 @@
+"""GPU parity of the fused stage-2 path (one pass in Algorithm 1's order,
+sparge_attn_path(SPARGE_PATH_FUSED)) against the float64 oracle, on the same
+inputs and acceptance as the two-pass parity tests, and of the automatic
+choice between the two paths.
+
+The fused path rounds P~ at the running max of each step (the oracle's
+order) where the two-pass path rounds it at the final max, so the two give
+different bits within the same tolerance; their lambda decisions, decision
+maps and counters are identical.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import free_block_sparse_mask_amd as fb
+from free_block_sparse_mask_amd import inputs as I
+from oracle import sparge_oracle as O
+
+from gpu_common import DEV, attn_path, check_attention, check_mask, log, run_attn, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("tiny_full", 0, {}),
+    ("tiny_ragged", 0, {"N": 1000}),
+    ("llm_gqa_ragged", 2, {"N": 1000, "H": 4, "H_kv": 2}),
+    ("llm_small_causal", 2, {"N": 2048, "H": 2, "H_kv": 2}),
+    ("image_small", 1, {"N": 64 + 24 * 24, "H": 2, "H_kv": 2, "grid": (24, 24), "text_tokens": 64}),
+    ("video_small", 3, {"N": 4 * 16 * 12, "H": 2, "H_kv": 1, "grid": (4, 16, 12)}),
+]
+
+
+def _both_paths(qd, kd, vd, mask, lam, causal, **kw):
+    """The call on each forced path: (o16, o32, counts, dbg) per path."""
+    out = {}
+    for path in (fb.PATH_TWO_PASS, fb.PATH_FUSED):
+        with attn_path(path):
+            out[path] = run_attn(qd, kd, vd, mask, lam, causal, **kw)
+    return out
+
+
+@pytest.mark.parametrize("label,wid,over", CASES, ids=[c[0] for c in CASES])
+def test_fused_matches_oracle(label, wid, over):
+    w = I.workload(wid, **over)
+    q, k, v = I.make_qkv(w)
+    log(f"[fused] {label}: B={w.B} H={w.H} Hkv={w.H_kv} N={w.N} d={w.d} causal={w.causal} lam={w.lam}")
+    Q, K, V = (O.widen(x, w.dtype) for x in (q, k, v))
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    res = _both_paths(qd, kd, vd, mask, w.lam, w.causal)
+    o16, o32, counts, dbg = res[fb.PATH_FUSED]
+    _, _, counts2, dbg2 = res[fb.PATH_TWO_PASS]
+    assert torch.equal(counts, counts2) and torch.equal(dbg, dbg2)
+    mg = mask.mg.cpu().numpy().astype(bool)
+    rep = check_attention(o32, counts, dbg, Q, K, V, mg, w.lam, w.causal, "f32", o16=o16, o16_dtype=w.dtype)
+    log(f"   max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} flips={rep['lambda_flips']} counts={rep['counts']}")
+
+
+@pytest.mark.parametrize("dtype,d,causal", [("f16", 128, False), ("bf16", 64, True), ("bf16", 128, True),
+                                            ("f16", 64, False)])
+def test_fused_random_mask_edge_rows(dtype, d, causal):
+    """The random mask of the two-pass edge-row test (empty block rows, a
+    dominant early block that makes lambda skip, a ragged N), lambda finite
+    and -inf, on the fused path."""
+    N, H, Hkv = 777, 3, 1
+    rng = np.random.default_rng(5)
+    Qf = rng.standard_normal((1, H, N, d)) * 2.0
+    Kf = rng.standard_normal((1, Hkv, N, d)) * 2.0
+    Kf[0, 0, :64] += 3.0 * Qf[0, 0, :64].mean(axis=0)
+    Vf = rng.standard_normal((1, Hkv, N, d))
+    q, k, v = (I.to_bits(x, dtype) for x in (Qf, Kf, Vf))
+    Q, K, V = (O.widen(x, dtype) for x in (q, k, v))
+    Tm, Tn = O.num_blocks(N, 128), O.num_blocks(N, 64)
+    mg_np = rng.random((1, H, Tm, Tn)) < 0.6
+    mg_np[0, 0, 2] = False
+    mg_np[0, 1, :, 0] = True
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    mg = torch.from_numpy(mg_np.astype(np.uint8)).to(DEV)
+    for lam in (-2.0, -math.inf):
+        with attn_path(fb.PATH_FUSED):
+            o, o32, counts, dbg = run_attn(qd, kd, vd, mg, lam, causal)
+        rep = check_attention(o32, counts, dbg, Q, K, V, mg_np, lam, causal, "f32", o16=o, o16_dtype=dtype)
+        log(f"[fused random] {dtype} d={d} causal={causal} lam={lam}: max_abs={rep['max_abs']:.2e} "
+            f"rel_l1={rep['rel_l1']:.2e} counts={rep['counts']}")
+        assert rep["counts"]["empty_rows"] >= 128
+        if lam == -2.0:
+            assert rep["counts"]["pv_skip"] > 0
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 127, 129])
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_fused_short_sequences(N, d, causal):
+    """One token up to just past one query block, on the fused path: a single
+    ragged tile, wavefronts whose rows all lie beyond N, empty lists."""
+    H, Hkv = 3, 1
+    rng = np.random.default_rng(1000 + N + d)
+    Qf = rng.standard_normal((1, H, N, d))
+    Kf = rng.standard_normal((1, Hkv, N, d))
+    Vf = rng.standard_normal((1, Hkv, N, d))
+    Qf[0, 1] = Qf[0, 1, :1] + 0.05 * Qf[0, 1]
+    Kf[0, 0] = Kf[0, 0, :1] + 0.05 * Kf[0, 0]
+    q, k, v = (I.to_bits(x, "bf16") for x in (Qf, Kf, Vf))
+    Q, K, V = (O.widen(x, "bf16") for x in (q, k, v))
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    mask = fb.predict_mask(qd, kd, 0.1, 0.9, causal)
+    with attn_path(fb.PATH_FUSED):
+        o, o32, counts, dbg = run_attn(qd, kd, vd, mask.mg, -1.0, causal)
+    rep = check_attention(o32, counts, dbg, Q, K, V, mask.mg.cpu().numpy().astype(bool), -1.0, causal, "f32",
+                          o16=o, o16_dtype="bf16")
+    log(f"[fused short] N={N} d={d} causal={causal}: max_abs={rep['max_abs']:.2e} counts={rep['counts']}")
+    assert rep["counts"]["rows"] == H * N
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fused_strided_layouts_and_batches(causal):
+    """[B, N, H, d] strides, two batches, GQA, ragged N on the fused path: the
+    same bits as contiguous inputs, and the oracle's result."""
+    w = I.workload(2, N=700, H=4, H_kv=2, B=2, causal=causal)
+    q, k, v = I.make_qkv(w)
+    Q, K, V = (O.widen(x, w.dtype) for x in (q, k, v))
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+
+    def bshd(x):
+        return x.transpose(1, 2).contiguous().transpose(1, 2)
+
+    qs, ks, vs = bshd(qd), bshd(kd), bshd(vd)
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, causal)
+    with attn_path(fb.PATH_FUSED):
+        o1, c1, _ = fb.attn(qd, kd, vd, mask, w.lam, causal)
+        out = torch.empty(w.B, w.N, w.H, w.d, dtype=vd.dtype, device=DEV).transpose(1, 2)
+        o2, c2, _ = fb.attn(qs, ks, vs, mask, w.lam, causal, out=out)
+        o, o32, counts, dbg = run_attn(qs, ks, vs, mask, w.lam, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(c1, c2) and torch.equal(o1, o)
+    rep = check_attention(o32, counts, dbg, Q, K, V, mask.mg.cpu().numpy().astype(bool), w.lam, causal, "f32",
+                          o16=o, o16_dtype=w.dtype)
+    log(f"[fused strided] causal={causal}: rel_l1={rep['rel_l1']:.2e} counts={rep['counts']}")
+
+
+def test_fused_repeat_calls_bit_identical():
+    w = I.workload(3, N=4 * 16 * 12, H=4, H_kv=2, grid=(4, 16, 12))
+    q, k, v = I.make_qkv(w)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    with attn_path(fb.PATH_FUSED):
+        runs = [fb.attn(qd, kd, vd, mask, w.lam, w.causal, dbg=True, ws=torch.empty_like(fb.workspace(qd, kd)))
+                for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, c, d in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(c, runs[0][1]) and torch.equal(d, runs[0][2])
+
+
+@pytest.mark.parametrize("label,wid,over,expect", [
+    ("image_small", 1, {"N": 64 + 24 * 24, "H": 2, "H_kv": 2, "grid": (24, 24), "text_tokens": 64}, "fused"),
+    ("video_small", 3, {"N": 4 * 16 * 12, "H": 2, "H_kv": 1, "grid": (4, 16, 12)}, "fused"),
+    ("llm_16k_causal", 2, {"N": 16384, "H": 4, "H_kv": 2}, "two_pass"),
+], ids=["image_small", "video_small", "llm_16k_causal"])
+def test_auto_path_follows_the_vote_rate(label, wid, over, expect):
+    """With SPARGE_PATH_AUTO the pilot takes the fused path where nearly every
+    (tile, wavefront) votes (image and video recipes) and two passes where
+    few do (the LLM recipe's sink rows): the automatic call's bits equal
+    those of the forced path it chose, and its counters both paths'."""
+    w = I.workload(wid, **over)
+    q, k, v = I.make_qkv(w)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    outs = {}
+    for path in (fb.PATH_AUTO, fb.PATH_TWO_PASS, fb.PATH_FUSED):
+        with attn_path(path):
+            outs[path] = fb.attn(qd, kd, vd, mask, w.lam, w.causal, out_f32=True)
+    torch.cuda.synchronize()
+    c = fb.counts_dict(outs[fb.PATH_AUTO][1])
+    rate = c["pv_exec"] / max(1, c["pv_exec"] + c["pv_skip"])
+    want = fb.PATH_FUSED if expect == "fused" else fb.PATH_TWO_PASS
+    other = fb.PATH_TWO_PASS if expect == "fused" else fb.PATH_FUSED
+    log(f"[auto] {label}: vote rate {rate:.3f}, expected {expect}")
+    assert torch.equal(outs[fb.PATH_AUTO][0], outs[want][0])
+    assert not torch.equal(outs[fb.PATH_AUTO][0], outs[other][0])
+    for path in (fb.PATH_TWO_PASS, fb.PATH_FUSED):
+        assert torch.equal(outs[path][1], outs[fb.PATH_AUTO][1])
+
+
+def test_int8_and_fp8_take_two_passes_whatever_the_request():
+    """int8 Q/K and fp8 P~V have no fused form: a forced fused path changes
+    none of their bits."""
+    w = I.workload(2, N=1000, H=2, H_kv=1)
+    q, k, _ = I.make_qkv(w)
+    v = I.make_tensor(w, I.TENSOR_V, dtype="f16")
+    qd, kd, vd = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, "f16")
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    q8, k8, qs, ks = fb.quant_qk_int8(qd, kd)
+    res = {}
+    for path in (fb.PATH_TWO_PASS, fb.PATH_FUSED):
+        with attn_path(path):
+            res[path] = (fb.attn(q8, k8, vd, mask, w.lam, w.causal, q_scale=qs, k_scale=ks)[0],
+                         fb.attn(qd, kd, to_dev(I.make_tensor(w, I.TENSOR_V, dtype=w.dtype), w.dtype), mask,
+                                 w.lam, w.causal, fp8_pv=True)[0])
+    torch.cuda.synchronize()
+    assert torch.equal(res[fb.PATH_TWO_PASS][0], res[fb.PATH_FUSED][0])
+    assert torch.equal(res[fb.PATH_TWO_PASS][1], res[fb.PATH_FUSED][1])
