@@ -319,6 +319,7 @@ struct Lane {
     // through LDS-DMA: each tile would wait for the next one to land.
 #pragma unroll
     for (int s = 0; s < G::QS; ++s) asm volatile("" : "+v"(qf[s]));
+    asm volatile("" : "+v"(qscale));   // the int8 row-block scale, likewise
     loads_k = wave < G::KCH;
     k_row0 = G::KR * wave + lane / G::KG;
     k_gran = (uint32_t)(((lane % G::KG) ^ ((k_row0 / G::KSW) % G::KG)) * 16);
