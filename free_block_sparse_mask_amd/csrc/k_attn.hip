@@ -372,19 +372,24 @@ __device__ __forceinline__ auto mfma_qk(u32x4 a, u32x4 b,
     return mfma16<KIND == 1>(a, b, c);
 }
 
-// whether tile j has dead scores for the wavefront whose rows start at q0:
-// keys beyond N, rows beyond N, or (causal) keys after some row
+// Tile j has dead scores for the wavefront whose rows start at q0 (keys
+// beyond N, rows beyond N, or, causal, keys after some row) exactly when
+// j >= first_masked_tile(q0): with rows past N every tile has them; else
+// j*64 + 64 > N holds from j = floor(N / 64) on, and j*64 + 63 > q0 from
+// j = floor((q0 + 1) / 64) on.
 template <bool CAUSAL>
-__device__ __forceinline__ bool tile_needs_mask(const AttnArgs& p, int j, int q0) {
-  return (j * kBk + kBk > p.N) || (q0 + kRowsPerWave > p.N) || (CAUSAL && j * kBk + kBk - 1 > q0);
+__device__ __forceinline__ int first_masked_tile(const AttnArgs& p, int q0) {
+  if (q0 + kRowsPerWave > p.N) return 0;
+  const int jn = p.N / kBk;
+  return CAUSAL ? min(jn, (q0 + 1) / kBk) : jn;
 }
 
 // Dead scores of one tile set to -inf in place: keys beyond N, causal future,
-// rows beyond N (only diagonal and ragged tiles need it).
+// rows beyond N (only diagonal and ragged tiles, j >= jm, need it).
 template <bool CAUSAL>
-__device__ __forceinline__ void mask_scores(const AttnArgs& p, f32x16 (&sv)[2], int j, int q0, int qrow, bool qvalid,
+__device__ __forceinline__ void mask_scores(const AttnArgs& p, f32x16 (&sv)[2], int j, int jm, int qrow, bool qvalid,
                                             int hl) {
-  if (tile_needs_mask<CAUSAL>(p, j, q0)) {
+  if (j >= jm) {
     // key = j*64 + 4*hl + off(t, r) is dead iff key > last, the last visible
     // key of this row (-1 for a row beyond N): off > last - j*64 - 4*hl
     const int last = !qvalid ? -1 : (CAUSAL ? min(qrow, p.N - 1) : p.N - 1);
@@ -551,6 +556,7 @@ void attn_stats(AttnArgs p) {
   }
   LN L;
   L.init(p, b, h, i, wq);
+  const int jm = first_masked_tile<CAUSAL>(p, L.q0);
   const long long row_id = L.row_id;
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
   const int n_live = live_tiles<CAUSAL>(p, i);
@@ -583,7 +589,6 @@ void attn_stats(AttnArgs p) {
 
   float m_run = kNegInf;      // running max, log2 units
   float l_half = 0.0f;        // this lane half's share of the row sum
-  int n_exec = 0, n_skip = 0, n_void = 0;
   uint32_t vw = 0;            // votes of the current 16 entries
 
   // tile(e): entry e's scores and softmax for this wavefront (the tile has
@@ -632,7 +637,7 @@ void attn_stats(AttnArgs p) {
     float mx;
     bool have_sv = true;
     if constexpr (G::I8) {
-      if (!tile_needs_mask<CAUSAL>(p, j, L.q0)) {
+      if (j < jm) {
         int mi[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -659,7 +664,7 @@ void attn_stats(AttnArgs p) {
     };
     if (have_sv) {
       to_float();
-      mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
+      mask_scores<CAUSAL>(p, sv, j, jm, L.qrow, L.qvalid, L.hl);
       float mq[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -700,10 +705,8 @@ void attn_stats(AttnArgs p) {
       l_half = alpha * l_half + psum;
     }
     m_run = m_new;
-    const uint32_t code = exec ? 1u : (any_finite ? 2u : 3u);
-    n_exec += exec ? 1 : 0;
-    n_skip += (!exec && any_finite) ? 1 : 0;
-    n_void += any_finite ? 0 : 1;
+    // 1: P~V runs, 2: skipped, 3: no finite score (a vote implies a finite one)
+    const uint32_t code = 3u - (any_finite ? 1u : 0u) - (exec ? 1u : 0u);
     vw |= code << (2 * (e & 15));
     if ((e & 15) == 15 || e == UC - 1) {
       votes[wave * nwords + (e >> 4)] = vw;
@@ -814,7 +817,21 @@ void attn_stats(AttnArgs p) {
     }
   }
 
-  // ---- counters ----
+  // ---- counters: the wavefront's vote codes, counted from its vote words ----
+  int n_exec = 0, n_skip = 0, n_void = 0;
+  for (int x = lane; x < (UC + 15) / 16; x += 64) {
+    const uint32_t w = votes[wave * nwords + x];
+    const uint32_t lo = w & 0x55555555u, hi = (w >> 1) & 0x55555555u;
+    n_exec += __popc(lo & ~hi);
+    n_skip += __popc(hi & ~lo);
+    n_void += __popc(lo & hi);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    n_exec += __shfl_xor(n_exec, o);
+    n_skip += __shfl_xor(n_skip, o);
+    n_void += __shfl_xor(n_void, o);
+  }
   const bool empty = L.qvalid && L.hl == 0 && !(l_tot > 0.0f);
   const unsigned long long n_empty = __popcll(__ballot(empty));
   if (lane == 0) {
@@ -868,6 +885,7 @@ void attn_pv(AttnArgs p) {
   if (!map_block(p, p.Tm, b, h, i)) return;
   Lane<D, KIND, kWavesPerBlock> L;
   L.init(p, b, h, i, (int)(threadIdx.x >> 6));
+  const int jm = first_masked_tile<CAUSAL>(p, L.q0);
   const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
   const long long row_id = L.row_id;
   const int U = p.ucnt[row_id];
@@ -962,7 +980,7 @@ void attn_pv(AttnArgs p) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
-      mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, hl);
+      mask_scores<CAUSAL>(p, sv, j, jm, L.qrow, L.qvalid, hl);
       if constexpr (PV8) {
         // P = exp(S - m_final) * 2^8 as E4M3: byte 16t + r of the lane's 32
         // holds sv[t][r], the key order the fp8 V^T rows use
@@ -1070,7 +1088,7 @@ void attn_pv(AttnArgs p) {
 // stay in `sv`.
 template <int D, int KIND, bool CAUSAL>
 __device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KIND, kWavesPerBlock>& L,
-                                             const unsigned char* kt, int j, f32x16 (&sv)[2]) {
+                                             const unsigned char* kt, int j, int jm, f32x16 (&sv)[2]) {
   using G = Geo<D, KIND>;
   constexpr int KLA = 2;      // k-steps the operand reads run ahead of the MFMAs
   u32x4 kf[G::QS][2];
@@ -1092,7 +1110,7 @@ __device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KI
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 2 * KLA, 0);
-  mask_scores<CAUSAL>(p, sv, j, L.q0, L.qrow, L.qvalid, L.hl);
+  mask_scores<CAUSAL>(p, sv, j, jm, L.qrow, L.qvalid, L.hl);
   float mq[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1138,6 +1156,7 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
   LN L;
   L.init(p, b, h, i, wave);
+  const int jm = first_masked_tile<CAUSAL>(p, L.q0);
   const int n_live = live_tiles<CAUSAL>(p, i);
   const int UC = p.row_cnt[L.row_id];
   const bool dense = UC == n_live;
@@ -1166,7 +1185,7 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
         mk[r0 + u] = kNegInf;
         if (r0 + u < NL) {
           f32x16 sv[2];
-          mk[r0 + u] = tile_scores<D, KIND, CAUSAL>(p, L, smem + u * G::K_BYTES, tile_of(r0 + u), sv);
+          mk[r0 + u] = tile_scores<D, KIND, CAUSAL>(p, L, smem + u * G::K_BYTES, tile_of(r0 + u), jm, sv);
         }
       }
       __syncthreads();        // every wavefront is done with the slots
@@ -1248,6 +1267,7 @@ void attn_fused(AttnArgs p) {
   if (!map_block(p, p.Tm, b, h, i)) return;
   LN L;
   L.init(p, b, h, i, (int)(threadIdx.x >> 6));
+  const int jm = first_masked_tile<CAUSAL>(p, L.q0);
   const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
   const long long row_id = L.row_id;
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
@@ -1305,7 +1325,7 @@ void attn_fused(AttnArgs p) {
     const unsigned char* kt = smem + (e % NS) * EB;
     const unsigned char* vt = kt + G::K_BYTES;
     f32x16 sv[2];
-    const float mloc = tile_scores<D, KIND, CAUSAL>(p, L, kt, j, sv);
+    const float mloc = tile_scores<D, KIND, CAUSAL>(p, L, kt, j, jm, sv);
     const float m_new = fmaxf(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
     const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
