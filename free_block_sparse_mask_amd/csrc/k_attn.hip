@@ -73,9 +73,15 @@ constexpr float kFarLog2 = 40.0f;
 // per workgroup and for packs of dense blocks
 constexpr int kStatsSlots = 2;
 constexpr int kStatsAhead = 1;
-constexpr int kPackSlots = 4;
-constexpr int kPackAhead = 2;
-constexpr int kPackPerBarrier = 2;   // pair kernel: entries per workgroup barrier
+// pair kernel: K slots, tiles loaded ahead, entries per workgroup barrier.
+// int8 K tiles are half the size, so their ring is deeper and its barriers
+// fewer (six slots, three per barrier: 20.4 against 20.9 ms at 128K GQA).
+template <bool I8>
+struct PackRing {
+  static constexpr int slots = I8 ? 6 : 4;
+  static constexpr int ahead = I8 ? 3 : 2;
+  static constexpr int per = I8 ? 3 : 2;
+};
 
 // v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
 // in the other, so combining the two gives every lane the pair (l, l ^ 32).
@@ -245,7 +251,7 @@ struct Geo {
 template <int D, int KIND, int NP>
 size_t stats_lds_bytes(int Tn) {
   using G = Geo<D, KIND>;
-  return (size_t)(NP == 1 ? kStatsSlots : kPackSlots) * G::K_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
+  return (size_t)(NP == 1 ? kStatsSlots : PackRing<G::I8>::slots) * G::K_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
          (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
 }
 template <int D, int KIND, bool PV8>
@@ -492,8 +498,8 @@ void attn_stats(AttnArgs p) {
   constexpr int NW = NP * kWavesPerBlock;
   constexpr int NT = NP * kThreads;
   using LN = Lane<D, KIND, NW>;
-  constexpr int NSLOT = PACK ? kPackSlots : kStatsSlots;
-  constexpr int PD = PACK ? kPackAhead : kStatsAhead;
+  constexpr int NSLOT = PACK ? PackRing<G::I8>::slots : kStatsSlots;
+  constexpr int PD = PACK ? PackRing<G::I8>::ahead : kStatsAhead;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ unsigned long long red[NW][4];
   __shared__ int pick[2];
@@ -717,10 +723,11 @@ void attn_stats(AttnArgs p) {
   // A ring of NSLOT K slots, PD tiles loaded ahead, one barrier per TPB
   // entries.  Single blocks (TPB = 1): at entry e's barrier its tile has
   // landed (the younger loads may still be in flight) and every wavefront is
-  // done with entry e-1, whose slot then takes entry e+PD.  Pairs (TPB = PD =
-  // 2, four slots): the barrier before entries e, e+1 follows the landing of
-  // both, and every wavefront is done with e-2 and e-1, whose slots then take
-  // e+2 and e+3; between barriers the wavefronts drift by up to a tile.
+  // done with entry e-1, whose slot then takes entry e+PD.  Pairs (TPB = PD,
+  // 2 PD slots): the barrier before entries e .. e+PD-1 follows the landing
+  // of all of them, and every wavefront is done with e-PD .. e-1, whose slots
+  // then take e+PD .. e+2PD-1; between barriers the wavefronts drift by up
+  // to PD - 1 tiles.
   static_assert(PD >= 1 && PD < NSLOT, "the refilled slot must be free");
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -732,7 +739,7 @@ void attn_stats(AttnArgs p) {
   if (UCU > 0) jd_v = entry_tile(min(PD, UCU - 1));
   // step(e): the barrier, then tile e, which refills entry e-1's slot with
   // e+PD; a packed block whose list has ended only refills
-  constexpr int TPB = PACK ? kPackPerBarrier : 1;
+  constexpr int TPB = PACK ? PackRing<G::I8>::per : 1;
   static_assert(TPB + PD <= NSLOT && NSLOT % TPB == 0 && PD >= TPB, "a period's slots must be free");
   auto step = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
@@ -763,8 +770,7 @@ void attn_stats(AttnArgs p) {
     }
     if (e < UCU) step(e, I0{});
     if (e + 1 < UCU) step(e + 1, I1{});
-  } else {
-    static_assert(NSLOT == 4, "two to four slots");
+  } else if constexpr (NSLOT == 4) {
     for (; e + 4 <= UCU; e += 4) {
       step(e, I0{});
       step(e + 1, I1{});
@@ -774,6 +780,23 @@ void attn_stats(AttnArgs p) {
     if (e < UCU) step(e, I0{});
     if (e + 1 < UCU) step(e + 1, I1{});
     if (e + 2 < UCU) step(e + 2, I2{});
+  } else {
+    static_assert(NSLOT == 6, "two, three, four or six slots");
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    for (; e + 6 <= UCU; e += 6) {
+      step(e, I0{});
+      step(e + 1, I1{});
+      step(e + 2, I2{});
+      step(e + 3, I3{});
+      step(e + 4, I4{});
+      step(e + 5, I5{});
+    }
+    if (e < UCU) step(e, I0{});
+    if (e + 1 < UCU) step(e + 1, I1{});
+    if (e + 2 < UCU) step(e + 2, I2{});
+    if (e + 3 < UCU) step(e + 3, I3{});
+    if (e + 4 < UCU) step(e + 4, I4{});
   }
   wait_barrier<0>();                       // every vote word is written
 
