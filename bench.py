@@ -45,6 +45,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 BQ, BK, ROWS = 128, 64, 32
 
@@ -112,6 +113,31 @@ def attn_source_digest() -> str:
         with open(os.path.join(ROOT, "free_block_sparse_mask_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def counted_traffic(path, key):
+    """HBM bytes per launch under ``key`` of the counter summary at ``path``,
+    or None when it is missing or was taken on other kernel sources."""
+    try:
+        with open(path) as f:
+            tj = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tj.get("kernel_source_sha256") != attn_source_digest():
+        return None
+    return tj.get(key)
+
+
+def mixed_roofline(parts, ms, kernel, traffic):
+    """Roofline of a call whose MFMA work runs at several dtype peaks:
+    ``parts`` = [(ops, peak in T/s), ...]; the peak is the rate at which the
+    whole mix would run with every part at its own peak."""
+    ops = sum(o for o, _ in parts)
+    ideal_s = sum(o / (pk * 1e12) for o, pk in parts)
+    achieved = ops / (ms * 1e-3) / 1e12
+    peak = ops / ideal_s / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+            "traffic": traffic, "kernel": kernel, "flops_per_launch": ops}
 
 
 def cpu_baseline(w, q, k, v, nrows):
@@ -308,15 +334,7 @@ def main():
         exe = executed_flops(c, w.d)
         attn_avg = float(np.mean(attn_ms))
         achieved = exe / (attn_avg * 1e-3) / 1e12
-        traffic = None
-        if os.path.exists(args.traffic_json):
-            try:
-                with open(args.traffic_json) as f:
-                    tj = json.load(f)
-                if tj.get("kernel_source_sha256") == attn_source_digest():
-                    traffic = tj.get("attn_fwd_bytes_per_launch")
-            except Exception:
-                traffic = None
+        traffic = counted_traffic(args.traffic_json, "attn_fwd_bytes_per_launch")
         result = {
             "metric": "dense-equiv attn TFLOPS + sparsity @128K GQA prefill; mask-pred % of time",
             "value": dense / (wall_ms * 1e-3) / 1e12,
@@ -375,6 +393,10 @@ def main():
                 "mfma_frac_executed": (qk_f / (PEAK_INT8_TOPS * 1e12) + pv_f / (PEAK_BF16_TFLOPS * 1e12))
                                       / (attn8 * 1e-3),
                 "counts": c8,
+                "roofline": mixed_roofline(
+                    [(qk_f, PEAK_INT8_TOPS), (pv_f, PEAK_BF16_TFLOPS)], attn8,
+                    "transpose_v + build_packs + attn_stats + sum_counts + attn_pv <128, int8 QK, fp16 P~V, causal>",
+                    counted_traffic(args.traffic_json, "int8_bytes_per_launch")),
             }
             log(f"[bench] int8 step: wall {wall8:.3f} ms, quant {quant_ms:.3f}, predict {pred8:.3f}, "
                 f"attn {attn8:.3f}")
@@ -397,6 +419,12 @@ def main():
                 "ms_per_step": wallf, "predict_ms": float(np.mean(ivf[0])), "attn_ms": float(np.mean(ivf[1])),
                 "attn_ms_median_min": [float(np.median(ivf[1])), float(np.min(ivf[1]))],
                 "dense_equiv_tflops": dense / (wallf * 1e-3) / 1e12, "counts": cf,
+                "roofline": mixed_roofline(
+                    [(cf["qk_exec"] * 2.0 * BQ * BK * w.d, PEAK_BF16_TFLOPS),
+                     (cf["pv_exec"] * 2.0 * ROWS * BK * w.d, PEAK_FP8_TFLOPS)], float(np.mean(ivf[1])),
+                    "v_absmax_partial + v_scale_final + transpose_v8 + build_packs + attn_stats + sum_counts + "
+                    "attn_pv <128, bf16 QK, fp8 P~V, causal>",
+                    counted_traffic(args.traffic_json, "fp8pv_bytes_per_launch")),
             }
             log(f"[bench] fp8 P~V step: wall {wallf:.3f} ms, predict {np.mean(ivf[0]):.3f}, "
                 f"attn {np.mean(ivf[1]):.3f}")

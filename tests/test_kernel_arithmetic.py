@@ -370,3 +370,63 @@ def test_pilot_estimate_separates_the_recipes():
         true = c["pv_exec"] / (c["pv_exec"] + c["pv_skip"])
         assert est >= true - 1e-12, (w.name, est, true)
         assert (est >= 0.9) == fused, (w.name, est, true)
+
+
+# ---------------------------------------------------------------------------
+# Attention tile bookkeeping: the first tile with dead scores, vote codes
+# ---------------------------------------------------------------------------
+def has_dead_scores(N, j, q0, causal, bq_rows=32, bk=64):
+    """The definition, score by score: some (row, key) of the tile is dead
+    (key at or beyond N, row at or beyond N, or, causal, key after the row)."""
+    rows = np.arange(q0, q0 + bq_rows)[:, None]
+    keys = np.arange(j * bk, j * bk + bk)[None, :]
+    dead = (keys >= N) | (rows >= N)
+    if causal:
+        dead |= keys > rows
+    return bool(dead.any())
+
+
+def first_masked_tile(N, q0, causal):
+    """The kernels' route: every tile from this index on has dead scores."""
+    if q0 + 32 > N:
+        return 0
+    jn = N // 64
+    return min(jn, (q0 + 1) // 64) if causal else jn
+
+
+def test_first_masked_tile_equals_the_dead_score_test():
+    for N in list(range(1, 300, 7)) + [4096, 4097, 46080, 131072 + 5]:
+        tn = (N + 63) // 64
+        for q0 in range(0, N + 32, 32):
+            if q0 > 600 and q0 + 700 < N:
+                continue                       # the middle of long rows adds nothing new
+            for causal in (False, True):
+                jm = first_masked_tile(N, q0, causal)
+                for j in range(tn):
+                    assert has_dead_scores(N, j, q0, causal) == (j >= jm), (N, q0, causal, j, jm)
+
+
+def test_vote_codes_counted_from_the_packed_words():
+    """Codes 1 (P~V), 2 (skipped) and 3 (no finite score), two bits per entry,
+    sixteen entries a word, counted by the bit masks the first pass uses."""
+    rng = np.random.default_rng(7)
+    for n in (0, 1, 15, 16, 17, 100, 2048):
+        codes = rng.integers(1, 4, size=n)
+        words = np.zeros((n + 15) // 16, dtype=np.uint64)
+        for e, c in enumerate(codes):
+            words[e >> 4] |= np.uint64(int(c) << (2 * (e & 15)))
+        n1 = n2 = n3 = 0
+        for w in words.tolist():
+            lo = w & 0x55555555
+            hi = (w >> 1) & 0x55555555
+            n1 += bin(lo & ~hi & 0xFFFFFFFF).count("1")
+            n2 += bin(hi & ~lo & 0xFFFFFFFF).count("1")
+            n3 += bin(lo & hi).count("1")
+        assert (n1, n2, n3) == (int((codes == 1).sum()), int((codes == 2).sum()), int((codes == 3).sum()))
+    # the code itself: 3 - any_finite - exec, with exec implying a finite score
+    for fin in (0, 1):
+        for ex in (0, 1):
+            if ex and not fin:
+                continue
+            want = 1 if ex else (2 if fin else 3)
+            assert 3 - fin - ex == want
