@@ -73,7 +73,7 @@ struct Workspace {
   // attention path of the call (two passes or one fused pass) and the
   // pilot's vote counts that choose it
   int32_t* path_flag;             // [1]
-  unsigned long long* pilot_cnt;  // [2]: sampled (tile, wavefront) votes, sampled pairs
+  unsigned long long* pilot_cnt;  // [kPilotBlocks][2]: per pilot workgroup, weighted votes and pairs
   size_t total;
 };
 
@@ -128,7 +128,7 @@ struct AttnArgs {
   uint8_t* dbg;
   int path;           // kPathAuto, kPathTwoPass or kPathFused (requested)
   int32_t* path_flag;             // workspace: the path the call takes; null: two passes, no flag
-  unsigned long long* pilot_cnt;  // workspace: the pilot's counts
+  unsigned long long* pilot_cnt;  // workspace: the pilot's counts per workgroup
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 

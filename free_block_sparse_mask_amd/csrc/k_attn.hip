@@ -1153,9 +1153,11 @@ __device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KI
 // against the running max of the sample so far, as the lambda rule votes
 // against the running max.  Every sampled tile stands for the listed tiles
 // of its stratum (the first for itself), so the counts weigh long rows by
-// their work.  The weighted votes and (tile, wavefront) pairs with a visible
-// key go to pilot_cnt[0] and [1].  The sampled K tiles go through
-// kPilotSlots LDS slots, that many loads in flight at a time.
+// their work.  The workgroup's weighted votes and (tile, wavefront) pairs
+// with a visible key go to its own pair of pilot_cnt slots (no atomics: one
+// address shared by every workgroup serialised them); pilot_decide adds the
+// slots up.  The sampled K tiles go through kPilotSlots LDS slots, that many
+// loads in flight at a time.
 constexpr int kPilotSlots = 4;
 template <int D, int KIND>
 size_t pilot_lds_bytes() {
@@ -1169,10 +1171,14 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
   using G = Geo<D, KIND>;
   using LN = Lane<D, KIND, kWavesPerBlock>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ unsigned long long part[kWavesPerBlock][2];
   const long long total = (long long)p.B * p.H * p.Tm;
   long long g = (long long)blockIdx.x * stride + stride / 2;
   if (g >= total) g = (long long)blockIdx.x * stride;
-  if (g >= total) return;
+  if (g >= total) {           // (not reached: the grid is ceil(total / stride))
+    if (threadIdx.x == 0) p.pilot_cnt[2 * blockIdx.x] = p.pilot_cnt[2 * blockIdx.x + 1] = 0;
+    return;
+  }
   const int i = (int)(g % p.Tm);
   const int bh = (int)(g / p.Tm);
   const int b = bh / p.H, h = bh % p.H;
@@ -1235,9 +1241,20 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
     }
   }
   const unsigned long long w_first = 840, w_stratum = S > 0 ? (unsigned long long)(UC - 1) * (840 / S) : 0;
-  if (lane == 0 && (pairs > 0 || v_first > 0)) {
-    atomicAdd(p.pilot_cnt, votes * w_stratum + v_first * w_first);
-    atomicAdd(p.pilot_cnt + 1, pairs * w_stratum + v_first * w_first);
+  if (lane == 0) {
+    part[wave][0] = votes * w_stratum + v_first * w_first;
+    part[wave][1] = pairs * w_stratum + v_first * w_first;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long v = 0, n = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      v += part[w][0];
+      n += part[w][1];
+    }
+    p.pilot_cnt[2 * blockIdx.x] = v;
+    p.pilot_cnt[2 * blockIdx.x + 1] = n;
   }
 }
 
@@ -1248,13 +1265,21 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
 // vote (the llm recipe at 8K) and 1.0 where all do (image, video).  The fused
 // pass pays off only near full rates (it is 28% faster at 100% and 9%
 // slower at 12%), hence the high bar.
-__global__ void pilot_decide(AttnArgs p) {
+// `groups`: the pilot's workgroups (0 when the path is forced).
+__global__ void pilot_decide(AttnArgs p, int groups) {
+  unsigned long long v = 0, n = 0;
+  for (int x = (int)threadIdx.x; x < groups; x += 64) {
+    v += p.pilot_cnt[2 * x];
+    n += p.pilot_cnt[2 * x + 1];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    v += __shfl_xor(v, o);
+    n += __shfl_xor(n, o);
+  }
   if (threadIdx.x != 0) return;
   int path = p.path;
-  if (path != kPathTwoPass && path != kPathFused) {
-    const unsigned long long v = p.pilot_cnt[0], n = p.pilot_cnt[1];
-    path = (n > 0 && 10 * v >= 9 * n) ? kPathFused : kPathTwoPass;
-  }
+  if (path != kPathTwoPass && path != kPathFused) path = (n > 0 && 10 * v >= 9 * n) ? kPathFused : kPathTwoPass;
   *p.path_flag = path;
 }
 
@@ -1625,12 +1650,11 @@ hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
   hipError_t e = hipSuccess;
   if constexpr (FUSABLE) {
     // the path of this call, on the device: the pilot's estimate or the request
+    int groups = 0;
     if (a.path != kPathTwoPass && a.path != kPathFused) {
-      hipLaunchKernelGGL(zero_u64, dim3(1), dim3(64), 0, st, a.pilot_cnt, 2);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
       const long long stride = (blocks + kPilotBlocks - 1) / kPilotBlocks;
-      const long long n = (blocks + stride - 1) / stride;
+      const long long n = (blocks + stride - 1) / stride;   // <= kPilotBlocks
+      groups = (int)n;
       const size_t ldsp = pilot_lds_bytes<D, KIND>();
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pilot<D, KIND, CAUSAL>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsp);
@@ -1640,7 +1664,7 @@ hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(pilot_decide, dim3(1), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(pilot_decide, dim3(1), dim3(64), 0, st, a, groups);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL>),
