@@ -69,6 +69,10 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // log2-units distance below the running max past which a whole tile's
 // exponentials cannot change a float32 row sum (see attn_stats)
 constexpr float kFarLog2 = 40.0f;
+// fused pass: the exponentials' reference max trails the running max until
+// the latter has risen this many log2 units above it, so O is rescaled only
+// then; P~ stays below 2^kLazyLog2 (see attn_fused)
+constexpr float kLazyLog2 = 8.0f;
 // attention pass 1: K ring slots and tiles loaded ahead, for one query block
 // per workgroup and for packs of dense blocks
 constexpr int kStatsSlots = 2;
@@ -1356,21 +1360,31 @@ void attn_fused(AttnArgs p) {
   f32x16 oacc[G::OT];
 #pragma unroll
   for (int t = 0; t < G::OT; ++t) oacc[t] = f32x16{};
-  float m_run = kNegInf;      // running max, log2 units
+  float m_run = kNegInf;      // running max, log2 units (the votes use it)
+  // The reference max of the exponentials, l and O: eq. 1's rescale is exact
+  // for any common reference, so it moves to the running max only once that
+  // has risen kLazyLog2 above it, and O is rescaled that seldom.  P~ is then
+  // below 2^kLazyLog2 rather than 1 (the same relative rounding), and the row
+  // maximum still contributes at least 1 to l, so a far tile's share of l
+  // keeps the bound of attn_stats.
+  float m_ref = kNegInf;
   float l_half = 0.0f;        // this lane half's share of the row sum
   int n_exec = 0, n_skip = 0, n_void = 0;
   uint32_t vw = 0;
 
   // entry e is used in step e; entries e+1 .. e+NS-2 are in flight when step e
-  // starts, and step e refills the slot entry e-1 used with entry e+NS-1
+  // starts, and step e refills the slot entry e-1 used with entry e+NS-1.  The
+  // steps run NS at a time with the slot a constant, so its LDS offsets fold
+  // into the reads.
   const int pre = min(UC, NS - 1);
   for (int t = 0; t < pre; ++t) issue(t, t);
-  for (int e = 0; e < UC; ++e) {
+  auto step = [&](int e, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
     const int pend = min(UC - 1, e + NS - 2) - e;
     wait_pending<LN::KCW + G::VCW, NS - 2>(pend);
-    if (e + NS - 1 < UC) issue(e + NS - 1, (e + NS - 1) % NS);
+    if (e + NS - 1 < UC) issue(e + NS - 1, (SL + NS - 1) % NS);
     const int j = __builtin_amdgcn_readfirstlane(entry_tile(e));
-    const unsigned char* kt = smem + (e % NS) * EB;
+    const unsigned char* kt = smem + SL * EB;
     const unsigned char* vt = kt + G::K_BYTES;
     f32x16 sv[2];
     const float mloc = tile_scores<D, KIND, CAUSAL>(p, L, kt, j, jm, sv);
@@ -1381,8 +1395,19 @@ void attn_fused(AttnArgs p) {
     const bool exec = __any(wants_pv);
     const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
     if (!far) {
-      const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
-      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
+      float alpha = 1.0f;
+      if (__any(m_new > m_ref + kLazyLog2)) {
+        // every row moves its reference to its running max (a row without a
+        // visible key yet keeps -inf and alpha 1)
+        alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_half *= alpha;
+#pragma unroll
+        for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      }
+      const float neg_m = (m_ref == kNegInf) ? 0.0f : -m_ref;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1394,13 +1419,7 @@ void attn_fused(AttnArgs p) {
         const int o = 4 * (q & 3);
         ps[q] = (vv[o] + vv[o + 1]) + (vv[o + 2] + vv[o + 3]);
       }
-      l_half = alpha * l_half + (((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int t = 0; t < G::OT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-      }
+      l_half += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
       if (exec) {
         // P~ in V's type as the B operand of 4 k-steps, then O^T += V_j^T P~^T
         u32x4 pb[4];
@@ -1431,6 +1450,29 @@ void attn_fused(AttnArgs p) {
       votes[wave * nwords + (e >> 4)] = vw;
       vw = 0;
     }
+  };
+  static_assert(NS == 2 || NS == 4, "the fused ring has two or four slots");
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int e = 0;
+  if constexpr (NS == 2) {
+    for (; e + 2 <= UC; e += 2) {
+      step(e, I0{});
+      step(e + 1, I1{});
+    }
+    if (e < UC) step(e, I0{});
+  } else {
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (; e + 4 <= UC; e += 4) {
+      step(e, I0{});
+      step(e + 1, I1{});
+      step(e + 2, I2{});
+      step(e + 3, I3{});
+    }
+    if (e < UC) step(e, I0{});
+    if (e + 1 < UC) step(e + 1, I1{});
+    if (e + 2 < UC) step(e + 2, I2{});
   }
   wait_barrier<0>();                       // every vote word is written
 
