@@ -26,7 +26,14 @@
 // has a voting wavefront, so V (half of the bytes of a K/V pass) is read for
 // a small fraction of the tiles, and pass 1 holds only K in LDS: a two-slot
 // ring for a single block, small enough that four workgroups share a CU, and
-// a four-slot ring for a pair of blocks, two workgroups per CU.
+// a four-slot (int8: six-slot) ring for a pair of blocks, two workgroups per
+// CU.
+//
+// attn_fused is the one-pass form (Algorithm 1's shape) for calls in which
+//   nearly every wavefront votes: K and V^T tiles share its ring, and the
+//   P~V of a voted tile follows its vote.  attn_pilot samples the call's
+//   blocks on the device and pilot_decide writes which path the call takes;
+//   the kernels of the other path read that flag and return at once.
 //
 // Most of pass 1's tiles belong to query blocks whose row of M_g is all
 // ones on the live tiles (the fix blocks of eq. (9) force it), so their
