@@ -126,7 +126,7 @@ Workspace carve_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, int64_t
   w.pack_next = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
   w.cnt_part = reinterpret_cast<unsigned long long*>(take(8 * (size_t)kCountSlots * SPARGE_NUM_COUNTERS));
   w.path_flag = reinterpret_cast<int32_t*>(take(4));
-  w.pilot_cnt = reinterpret_cast<unsigned long long*>(take(16 * (size_t)kPilotBlocks));
+  w.pilot_cnt = reinterpret_cast<unsigned long long*>(take(8 * (size_t)kPilotCounts * kPilotBlocks));
   w.total = off;
   return w;
 }
@@ -587,7 +587,7 @@ Workspace carve_attn_workspace(void* base, int64_t B, int64_t H, int64_t Hkv, in
   w.pack_next = reinterpret_cast<int32_t*>(take(4 * (size_t)(B * Hkv)));
   w.cnt_part = reinterpret_cast<unsigned long long*>(take(8 * (size_t)kCountSlots * SPARGE_NUM_COUNTERS));
   w.path_flag = reinterpret_cast<int32_t*>(take(4));
-  w.pilot_cnt = reinterpret_cast<unsigned long long*>(take(16 * (size_t)kPilotBlocks));
+  w.pilot_cnt = reinterpret_cast<unsigned long long*>(take(8 * (size_t)kPilotCounts * kPilotBlocks));
   w.total = off;
   return w;
 }

@@ -73,7 +73,8 @@ struct Workspace {
   // attention path of the call (two passes or one fused pass) and the
   // pilot's vote counts that choose it
   int32_t* path_flag;             // [1]
-  unsigned long long* pilot_cnt;  // [kPilotBlocks][2]: per pilot workgroup, weighted votes and pairs
+  unsigned long long* pilot_cnt;  // [kPilotBlocks][kPilotCounts]: per pilot workgroup, weighted votes and
+                                  // pairs, the sampled block's listed tiles, 1
   size_t total;
 };
 
@@ -83,6 +84,10 @@ constexpr int kPathTwoPass = 1;
 constexpr int kPathFused = 2;
 // pilot: at most this many sampled query blocks, this many listed tiles each
 constexpr int kPilotBlocks = 256;
+constexpr int kPilotCounts = 4;
+// the automatic path takes the fused pass when the sampled blocks list at
+// most this many tiles on average
+constexpr int kFusedMeanTiles = 224;
 constexpr int kPilotTiles = 4;
 
 constexpr int kQuantChunkRows = 1024;       // tokens per partial K column sum

@@ -158,9 +158,12 @@ __device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char*
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const unsigned char* sbase, uint32_t voff, uint32_t lds) {
+  // lds is uniform by contract; the read makes it an SGPR wherever the
+  // compiler kept it in a vector register
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(lds)
+               : "v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -500,6 +503,47 @@ __global__ void sum_counts(AttnArgs p) {
 // tile loads and the barriers.  With pairs (NP = 2), two workgroups share a
 // CU, four wavefronts per SIMD, and drift against each other as the single
 // workgroups do; one workgroup of four blocks per CU measured slower.
+// The next pack of dense blocks for this workgroup (pick: 2 ints of shared
+// memory).  Each (b, kv head) hands out its packs in order, heaviest first,
+// from a counter.  Workgroups go to the 8 XCDs round robin (id % 8), and the
+// workgroups of XCD x start at kv head x ng / 8 of the ng, moving on to the
+// next kv heads once those are handed out.  So the workgroups resident on
+// one XCD hold neighbouring packs (one kv head, close block indices) that
+// start together and walk the same K tiles through its L2, different XCDs
+// read different K, and an XCD whose kv heads run out takes over the rest of
+// the others'.  r0 is the pack's first (heaviest) row id, r the one of slot
+// `member` (-1 for a padding slot); false when every queue is empty.
+template <int NP>
+__device__ __forceinline__ bool take_pack(const AttnArgs& p, int* pick, int member, int& r0, int& r) {
+  const int per = pack_slots(p.H, p.Hkv, p.Tm);
+  const int ng = p.B * p.Hkv;
+  if (threadIdx.x == 0) {
+    const int g0 = (int)((long long)(blockIdx.x % 8u) * ng / 8);
+    int pg = -1, pk = 0;
+    for (int s = 0; s < ng && pg < 0; ++s) {
+      const int gg = (g0 + s) % ng;
+      // the queue head only grows, so an old value never hides packs left
+      if (__hip_atomic_load(p.pack_next + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= p.npack[gg])
+        continue;
+      const int kk = atomicAdd(p.pack_next + gg, 1);
+      if (kk < p.npack[gg]) {
+        pg = gg;
+        pk = kk;
+      }
+    }
+    pick[0] = pg;
+    pick[1] = pk;
+  }
+  __syncthreads();
+  const int g = pick[0], k = pick[1];
+  if (g < 0) return false;
+  const int32_t* pr = p.packs + (long long)g * per + (long long)k * NP;
+  // the slots are wavefront-uniform
+  r0 = __builtin_amdgcn_readfirstlane(pr[0]);
+  r = __builtin_amdgcn_readfirstlane(pr[__builtin_amdgcn_readfirstlane(member)]);
+  return true;
+}
+
 template <int D, int KIND, bool CAUSAL, int NP>
 __global__ __launch_bounds__(NP * kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void attn_stats(AttnArgs p) {
@@ -528,41 +572,11 @@ void attn_stats(AttnArgs p) {
     if (p.packs != nullptr && UC == live_tiles<CAUSAL>(p, i)) return;   // a packed dense block
     UCU = UC;
   } else {
-    // Each (b, kv head) hands out its packs in order, heaviest first, from
-    // a counter.  Workgroups go to the 8 XCDs round robin (id % 8), and the
-    // workgroups of XCD x start at kv head x ng / 8 of the ng, moving on to
-    // the next kv heads once those are handed out.  So the workgroups
-    // resident on one XCD hold neighbouring packs (one kv head, close block
-    // indices) that start together and walk the same K tiles through its L2,
-    // different XCDs read different K, and an XCD whose kv heads run out
-    // takes over the rest of the others'.  The grid has a workgroup for
-    // every pack slot; those that find every queue empty return.
-    const int per = pack_slots(p.H, p.Hkv, p.Tm);
-    const int ng = p.B * p.Hkv;
-    if (tid == 0) {
-      const int g0 = (int)((long long)(blockIdx.x % 8u) * ng / 8);
-      int pg = -1, pk = 0;
-      for (int s = 0; s < ng && pg < 0; ++s) {
-        const int gg = (g0 + s) % ng;
-        // the queue head only grows, so an old value never hides packs left
-        if (__hip_atomic_load(p.pack_next + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= p.npack[gg])
-          continue;
-        const int kk = atomicAdd(p.pack_next + gg, 1);
-        if (kk < p.npack[gg]) {
-          pg = gg;
-          pk = kk;
-        }
-      }
-      pick[0] = pg;
-      pick[1] = pk;
-    }
-    __syncthreads();
-    const int g = pick[0], k = pick[1];
-    if (g < 0) return;
-    const int32_t* pr = p.packs + (long long)g * per + (long long)k * NP;
-    // the pack's first block is the heaviest; the slots are wavefront-uniform
-    const int r0 = __builtin_amdgcn_readfirstlane(pr[0]);
-    int r = __builtin_amdgcn_readfirstlane(pr[__builtin_amdgcn_readfirstlane(member)]);
+    // the next pack from the per-kv-head queues (take_pack); the grid has a
+    // workgroup for every pack slot, and those that find every queue empty
+    // return
+    int r0, r;
+    if (!take_pack<NP>(p, pick, member, r0, r)) return;
     active = r >= 0;
     r = active ? r : r0;
     i = r % p.Tm;
@@ -1120,8 +1134,8 @@ void attn_pv(AttnArgs p) {
 // Row maxima of one tile of S^T for this wavefront (log2 units, scaled):
 // the QK^T MFMAs on the K tile at `kt`, the dead scores masked.  The scores
 // stay in `sv`.
-template <int D, int KIND, bool CAUSAL>
-__device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KIND, kWavesPerBlock>& L,
+template <int D, int KIND, bool CAUSAL, int NW = kWavesPerBlock>
+__device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KIND, NW>& L,
                                              const unsigned char* kt, int j, int jm, f32x16 (&sv)[2]) {
   using G = Geo<D, KIND>;
   constexpr int KLA = 2;      // k-steps the operand reads run ahead of the MFMAs
@@ -1187,7 +1201,8 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
   long long g = (long long)blockIdx.x * stride + stride / 2;
   if (g >= total) g = (long long)blockIdx.x * stride;
   if (g >= total) {           // (not reached: the grid is ceil(total / stride))
-    if (threadIdx.x == 0) p.pilot_cnt[2 * blockIdx.x] = p.pilot_cnt[2 * blockIdx.x + 1] = 0;
+    if (threadIdx.x == 0)
+      for (int c = 0; c < kPilotCounts; ++c) p.pilot_cnt[kPilotCounts * blockIdx.x + c] = 0;
     return;
   }
   const int i = (int)(g % p.Tm);
@@ -1264,86 +1279,142 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
       v += part[w][0];
       n += part[w][1];
     }
-    p.pilot_cnt[2 * blockIdx.x] = v;
-    p.pilot_cnt[2 * blockIdx.x + 1] = n;
+    unsigned long long* pc = p.pilot_cnt + kPilotCounts * blockIdx.x;
+    pc[0] = v;
+    pc[1] = n;
+    pc[2] = (unsigned long long)UC;       // the sampled block's listed tiles
+    pc[3] = 1;
   }
 }
 
 // The call's path: the requested one, or for kPathAuto the fused pass when
-// at least nine tenths of the pilot's weighted (tile, wavefront) pairs voted.
+// at least nine tenths of the pilot's weighted (tile, wavefront) pairs voted,
+// or when the sampled blocks list at most kFusedMeanTiles tiles on average.
 // A short sample sets new maxima more often than the whole row does, so the
-// pilot can only overstate the rate: it reads 0.67 where 26% of the pairs
-// vote (the llm recipe at 8K) and 1.0 where all do (image, video).  The fused
-// pass pays off only near full rates (it is 28% faster at 100% and 9%
-// slower at 12%), hence the high bar.
+// pilot overstates lower rates and hardly separates them: it reads 0.64 to
+// 0.72 on the llm recipe from N 4096 (36% of the pairs vote) to 131072 (5%),
+// and 1.0 where all vote (image, video).  The fused pass wins near full
+// rates (30% faster on video) and on short rows (12 to 28% faster at N 4096
+// to 32768, about 150 listed tiles per block or fewer), and loses on long
+// rows of low rates (4% slower at 65536, 15% at 131072, some 300 and more).
 // `groups`: the pilot's workgroups (0 when the path is forced).
 __global__ void pilot_decide(AttnArgs p, int groups) {
-  unsigned long long v = 0, n = 0;
+  unsigned long long v = 0, n = 0, uc = 0, nb = 0;
   for (int x = (int)threadIdx.x; x < groups; x += 64) {
-    v += p.pilot_cnt[2 * x];
-    n += p.pilot_cnt[2 * x + 1];
+    const unsigned long long* pc = p.pilot_cnt + kPilotCounts * x;
+    v += pc[0];
+    n += pc[1];
+    uc += pc[2];
+    nb += pc[3];
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     v += __shfl_xor(v, o);
     n += __shfl_xor(n, o);
+    uc += __shfl_xor(uc, o);
+    nb += __shfl_xor(nb, o);
   }
   if (threadIdx.x != 0) return;
   int path = p.path;
-  if (path != kPathTwoPass && path != kPathFused) path = (n > 0 && 10 * v >= 9 * n) ? kPathFused : kPathTwoPass;
+  if (path != kPathTwoPass && path != kPathFused)
+    path = (n > 0 && (10 * v >= 9 * n || uc <= (unsigned long long)kFusedMeanTiles * nb)) ? kPathFused
+                                                                                           : kPathTwoPass;
   *p.path_flag = path;
 }
 
-template <int D, int KIND>
-size_t fused_lds_bytes(int Tn) {
-  using G = Geo<D, KIND>;
-  return (size_t)G::NS2 * G::E_BYTES + (size_t)2 * ((Tn + 1) & ~1) + (size_t)4 * kWavesPerBlock * ((Tn + 15) / 16);
+// The fused pass runs dense blocks in packs only when rows are long: a mean
+// of at least 192 live tiles per query block (Tn, or Tn / 2 causal).  Packs
+// halve the K and V^T streams but couple two blocks' wavefronts at every
+// barrier; on short rows that costs more than it saves (llm recipe: 0.43
+// against 0.38 ms at N 8192, 3.56 against 3.97 ms at 32768; video 24.96
+// against 25.45 ms).
+template <bool CAUSAL>
+__device__ __forceinline__ bool fused_packs(const AttnArgs& p) {
+  return (CAUSAL ? p.Tn / 2 : p.Tn) >= 192;
 }
 
-// The fused pass: one workgroup of 4 wavefronts per query block (the grid
-// order of attn_pv), its listed K tiles and V^T tiles through a ring of LDS
-// slots (the slots and loads of attn_pv).  Per tile, as Algorithm 1 orders
-// it: S = Q K^T, the running max m and row sum l (eq. 1), the wavefront's
-// lambda vote, and, when the vote runs P~V, O = exp(m_old - m_new) O +
-// P~ V with P~ = exp(S - m_new) rounded to V's type.  O is rescaled whenever
-// m grows, whether or not the tile runs P~V.  A tile whose rows all lie more
-// than kFarLog2 below their running max leaves m, l and O as they are (their
-// P~ are below 2^-40; see attn_stats); its vote is still counted.  The votes,
-// the decision map and the counters are those of attn_stats.
-template <int D, int KIND, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int KIND, int NP>
+size_t fused_lds_bytes(int Tn) {
+  using G = Geo<D, KIND>;
+  return (size_t)G::NS2 * G::E_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
+         (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16);
+}
+
+// The fused pass: the query blocks of a call in the grid order of attn_pv
+// (NP = 1, one workgroup of 4 wavefronts each), except the dense ones, which
+// run in the packs of attn_stats (NP = 2, one workgroup of 8 wavefronts per
+// pack of two blocks of one kv head, handed out from the same per-kv-head
+// queues): the pack's blocks list the same tiles (prefixes, causal), so one
+// stream of K and V^T tiles through a ring of LDS slots (the slots and loads
+// of attn_pv) serves both.  Per tile, as Algorithm 1 orders it: S = Q K^T,
+// the running max m and row sum l (eq. 1), the wavefront's lambda vote, and,
+// when the vote runs P~V, O = exp(m_old - m_new) O + P~ V with P~ = exp(S -
+// m_new) rounded to V's type.  A tile whose rows all lie more than kFarLog2
+// below their running max leaves m, l and O as they are (their P~ are below
+// 2^-40; see attn_stats); its vote is still counted.  The votes, the decision
+// map and the counters are those of attn_stats.
+template <int D, int KIND, bool CAUSAL, int NP>
+__global__ __launch_bounds__(NP * kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fused(AttnArgs p) {
   static_assert(KIND <= 1, "the fused path takes 16-bit Q/K only");
   using G = Geo<D, KIND>;
-  using LN = Lane<D, KIND, kWavesPerBlock>;
+  constexpr bool PACK = NP > 1;
+  constexpr int NW = NP * kWavesPerBlock;
+  constexpr int NT = NP * kThreads;
+  using LN = Lane<D, KIND, NW>;
   constexpr int NS = G::NS2;
   constexpr int EB = G::E_BYTES;
+  constexpr int VCWN = G::V_BYTES / 1024 / NW;    // V^T chunks per wavefront and tile
+  static_assert(VCWN >= 1 && G::V_BYTES == VCWN * 1024 * NW, "V^T tiles must split over the wavefronts");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ unsigned long long red[kWavesPerBlock][4];
+  __shared__ unsigned long long red[NW][4];
+  __shared__ int pick[2];
 
   if (!path_is(p, kPathFused)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int member = wave / kWavesPerBlock, wq = wave % kWavesPerBlock;
   int b, h, i;
-  if (!map_block(p, p.Tm, b, h, i)) return;
+  int UC;                     // this block's list length
+  int UCU;                    // entries the workgroup walks (the longest list)
+  bool active = true;         // the wavefront's pack slot holds a block
+  if constexpr (!PACK) {
+    if (!map_block(p, p.Tm, b, h, i)) return;
+    UC = p.row_cnt[(long long)(b * p.H + h) * p.Tm + i];
+    // a dense block taken by the pack kernel
+    if (p.packs != nullptr && fused_packs<CAUSAL>(p) && UC == live_tiles<CAUSAL>(p, i)) return;
+    UCU = UC;
+  } else {
+    if (!fused_packs<CAUSAL>(p)) return;
+    int r0, r;
+    if (!take_pack<NP>(p, pick, member, r0, r)) return;
+    active = r >= 0;
+    r = active ? r : r0;
+    i = r % p.Tm;
+    h = (r / p.Tm) % p.H;
+    b = r / p.Tm / p.H;
+    UC = active ? live_tiles<CAUSAL>(p, i) : 0;
+    UCU = live_tiles<CAUSAL>(p, r0 % p.Tm);
+  }
   LN L;
-  L.init(p, b, h, i, (int)(threadIdx.x >> 6));
+  L.init(p, b, h, i, wq);
   const int jm = first_masked_tile<CAUSAL>(p, L.q0);
-  const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
+  const int l32 = L.l32, hl = L.hl;
   const long long row_id = L.row_id;
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
   const int n_live = live_tiles<CAUSAL>(p, i);
-  const int UC = p.row_cnt[row_id];
-  const bool dense = UC == n_live;             // the list is 0, 1, ..., live - 1
+  const bool dense = PACK || UC == n_live;     // the list is 0, 1, ..., live - 1
   const int nwords = (p.Tn + 15) / 16;
   uint16_t* lst = reinterpret_cast<uint16_t*>(smem + NS * EB);
-  uint32_t* votes = reinterpret_cast<uint32_t*>(smem + NS * EB + 2 * ((p.Tn + 1) & ~1));
+  uint32_t* votes = reinterpret_cast<uint32_t*>(smem + NS * EB + (PACK ? 0 : 2 * ((p.Tn + 1) & ~1)));
   if (!dense) {
     const uint16_t* gl = p.row_idx + row_id * p.Tn;
-    for (int e = tid; e < UC; e += kThreads) lst[e] = gl[e];
+    for (int e = tid; e < UC; e += NT) lst[e] = gl[e];
   }
   __syncthreads();
   auto entry_tile = [&](int e) -> int { return dense ? e : (int)lst[e]; };
 
-  // V^T tiles: rows of 128 bytes, granules XOR-swizzled by row / 2 (attn_pv)
+  // V^T tiles: rows of 128 bytes, granules XOR-swizzled by row / 2 (attn_pv);
+  // wavefront w loads rows 8w .. 8w + 7 of every 8 NW rows
   const unsigned char* vtbase =
       reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + L.hk) * D) * p.Np * 2;
   const int v_row0 = 16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP) + lane / 8;
@@ -1357,8 +1428,8 @@ void attn_fused(AttnArgs p) {
     const uint32_t sl = ring_lds + (uint32_t)(slot * EB);
     L.issue_k(p, j, sl);
 #pragma unroll
-    for (int c = 0; c < G::VCW; ++c) {
-      const int row_c = 16 * c * (4 / G::VGRP);
+    for (int c = 0; c < VCWN; ++c) {
+      const int row_c = 16 * c * (NW / G::VGRP);
       const unsigned char* base = uniform_ptr(vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2);
       dma16(base, v_off, (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + row_c * G::VROW + v_wl)));
     }
@@ -1382,19 +1453,20 @@ void attn_fused(AttnArgs p) {
   // entry e is used in step e; entries e+1 .. e+NS-2 are in flight when step e
   // starts, and step e refills the slot entry e-1 used with entry e+NS-1.  The
   // steps run NS at a time with the slot a constant, so its LDS offsets fold
-  // into the reads.
-  const int pre = min(UC, NS - 1);
+  // into the reads.  A packed block whose list has ended only loads.
+  const int pre = min(UCU, NS - 1);
   for (int t = 0; t < pre; ++t) issue(t, t);
   auto step = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    const int pend = min(UC - 1, e + NS - 2) - e;
-    wait_pending<LN::KCW + G::VCW, NS - 2>(pend);
-    if (e + NS - 1 < UC) issue(e + NS - 1, (SL + NS - 1) % NS);
+    const int pend = min(UCU - 1, e + NS - 2) - e;
+    wait_pending<LN::KCW + VCWN, NS - 2>(pend);
+    if (e + NS - 1 < UCU) issue(e + NS - 1, (SL + NS - 1) % NS);
+    if (PACK && e >= UC) return;
     const int j = __builtin_amdgcn_readfirstlane(entry_tile(e));
     const unsigned char* kt = smem + SL * EB;
     const unsigned char* vt = kt + G::K_BYTES;
     f32x16 sv[2];
-    const float mloc = tile_scores<D, KIND, CAUSAL>(p, L, kt, j, jm, sv);
+    const float mloc = tile_scores<D, KIND, CAUSAL, NW>(p, L, kt, j, jm, sv);
     const float m_new = fmaxf(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
     const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
@@ -1463,30 +1535,30 @@ void attn_fused(AttnArgs p) {
   using I1 = std::integral_constant<int, 1>;
   int e = 0;
   if constexpr (NS == 2) {
-    for (; e + 2 <= UC; e += 2) {
+    for (; e + 2 <= UCU; e += 2) {
       step(e, I0{});
       step(e + 1, I1{});
     }
-    if (e < UC) step(e, I0{});
+    if (e < UCU) step(e, I0{});
   } else {
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    for (; e + 4 <= UC; e += 4) {
+    for (; e + 4 <= UCU; e += 4) {
       step(e, I0{});
       step(e + 1, I1{});
       step(e + 2, I2{});
       step(e + 3, I3{});
     }
-    if (e < UC) step(e, I0{});
-    if (e + 1 < UC) step(e + 1, I1{});
-    if (e + 2 < UC) step(e + 2, I2{});
+    if (e < UCU) step(e, I0{});
+    if (e + 1 < UCU) step(e + 1, I1{});
+    if (e + 2 < UCU) step(e + 2, I2{});
   }
   wait_barrier<0>();                       // every vote word is written
 
   // ---- epilogue: O / l, as attn_pv stores it ----
   const float l_tot = sum_halves(l_half);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (L.qvalid && p.out_f32) {
+  if (active && L.qvalid && p.out_f32) {
     float* ob = static_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)L.qrow * p.o_sn;
 #pragma unroll
     for (int t = 0; t < G::OT; ++t)
@@ -1496,7 +1568,7 @@ void attn_fused(AttnArgs p) {
                    __float_as_uint(oacc[t][4 * g + 2] * inv), __float_as_uint(oacc[t][4 * g + 3] * inv)};
         *reinterpret_cast<u32x4*>(ob + 32 * t + 8 * g + 4 * hl) = w;
       }
-  } else if (L.qvalid) {
+  } else if (active && L.qvalid) {
     unsigned short* ob =
         static_cast<unsigned short*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)L.qrow * p.o_sn;
 #pragma unroll
@@ -1515,13 +1587,15 @@ void attn_fused(AttnArgs p) {
   }
 
   // ---- decision map and counters, as attn_stats writes them ----
-  if (p.dbg != nullptr) {
+  const int wv0 = member * kWavesPerBlock;   // the block's first wavefront
+  const int btid = tid % kThreads;           // thread index inside the block's wavefronts
+  if (active && p.dbg != nullptr) {
     uint8_t* drow = p.dbg + row_id * p.Tn * kWavesPerBlock;
-    for (int x = tid; x < UC * kWavesPerBlock; x += kThreads) {
+    for (int x = btid; x < UC * kWavesPerBlock; x += kThreads) {
       const int e2 = x / kWavesPerBlock, w = x % kWavesPerBlock;
       if (i * kBq + w * kRowsPerWave < p.N)
         drow[entry_tile(e2) * kWavesPerBlock + w] =
-            (uint8_t)((votes[w * nwords + (e2 >> 4)] >> (2 * (e2 & 15))) & 3u);
+            (uint8_t)((votes[(wv0 + w) * nwords + (e2 >> 4)] >> (2 * (e2 & 15))) & 3u);
     }
   }
   const bool empty = L.qvalid && hl == 0 && !(l_tot > 0.0f);
@@ -1533,15 +1607,15 @@ void attn_fused(AttnArgs p) {
     red[wave][3] = n_empty;
   }
   __syncthreads();
-  if (tid == 0) {
+  if (active && btid == 0) {
     unsigned long long ex = 0, sk = 0, vo = 0, em = 0;
     unsigned long long* cp = p.cnt_part + (blockIdx.x % kCountSlots) * SPARGE_NUM_COUNTERS;
     for (int w = 0; w < kWavesPerBlock; ++w) {
       if (i * kBq + w * kRowsPerWave >= p.N) continue;   // no rows: no group
-      ex += red[w][0];
-      sk += red[w][1];
-      vo += red[w][2];
-      em += red[w][3];
+      ex += red[wv0 + w][0];
+      sk += red[wv0 + w][1];
+      vo += red[wv0 + w][2];
+      em += red[wv0 + w][3];
     }
     atomicAdd(cp + SPARGE_CNT_LIVE, (unsigned long long)n_live);
     atomicAdd(cp + SPARGE_CNT_QK_EXEC, (unsigned long long)UC);
@@ -1716,8 +1790,12 @@ hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
     hipLaunchKernelGGL(pilot_decide, dim3(1), dim3(64), 0, st, a, groups);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fused_lds_bytes<D, KIND>(a.Tn));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL, 1>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fused_lds_bytes<D, KIND, 1>(a.Tn));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL, kPackBlocks>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)fused_lds_bytes<D, KIND, kPackBlocks>(a.Tn));
     if (e != hipSuccess) return e;
   }
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL, 1>),
@@ -1741,8 +1819,14 @@ hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (FUSABLE) {
-    const size_t ldsf = fused_lds_bytes<D, KIND>(a.Tn);
-    hipLaunchKernelGGL((attn_fused<D, KIND, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), ldsf, st, a);
+    // the fused pass: dense blocks in packs, then the others
+    const size_t ldsfp = fused_lds_bytes<D, KIND, kPackBlocks>(a.Tn);
+    hipLaunchKernelGGL((attn_fused<D, KIND, CAUSAL, kPackBlocks>), dim3((unsigned)packs),
+                       dim3(kPackBlocks * kThreads), ldsfp, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t ldsf = fused_lds_bytes<D, KIND, 1>(a.Tn);
+    hipLaunchKernelGGL((attn_fused<D, KIND, CAUSAL, 1>), dim3((unsigned)blocks), dim3(kThreads), ldsf, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -92,14 +92,15 @@ int sparge_rows_per_wave(void);
  *     (tile, wavefront) pairs vote.
  *   SPARGE_PATH_FUSED: one pass streaming K and V together, Algorithm 1's own
  *     order (P~ = exp(S - running max), O rescaled as the max grows), P~V
- *     skipped for the wavefronts whose vote says so.  Cheap when most vote.
+ *     skipped for the wavefronts whose vote says so.  Cheap when most vote,
+ *     or when rows are short.
  *   SPARGE_PATH_AUTO (the default): per call, a pilot on the device takes
  *     up to 256 sampled query blocks, seeds a running max with each block's
  *     first listed tile, and votes 3 more listed tiles (one per stratum of
  *     the list) against it; the call takes the fused path when at least nine
  *     tenths of the sampled (tile, wavefront) pairs vote, each sample
- *     weighted by the listed tiles it stands for.  Nothing is read back to
- *     the host.
+ *     weighted by the listed tiles it stands for, or when the sampled blocks
+ *     list at most 224 tiles on average.  Nothing is read back to the host.
  * int8 Q/K and the fp8 P~V variant always take two passes.
  * sparge_attn_path(p) sets the path of later calls process-wide and returns
  * the previous setting; sparge_attn_path(-1) only returns it.  An unknown p

@@ -158,13 +158,16 @@ def test_fused_repeat_calls_bit_identical():
 @pytest.mark.parametrize("label,wid,over,expect", [
     ("image_small", 1, {"N": 64 + 24 * 24, "H": 2, "H_kv": 2, "grid": (24, 24), "text_tokens": 64}, "fused"),
     ("video_small", 3, {"N": 4 * 16 * 12, "H": 2, "H_kv": 1, "grid": (4, 16, 12)}, "fused"),
-    ("llm_16k_causal", 2, {"N": 16384, "H": 4, "H_kv": 2}, "two_pass"),
-], ids=["image_small", "video_small", "llm_16k_causal"])
+    ("llm_16k_causal", 2, {"N": 16384, "H": 4, "H_kv": 2}, "fused"),
+    ("llm_64k_causal", 2, {"N": 65536, "H": 2, "H_kv": 1}, "two_pass"),
+], ids=["image_small", "video_small", "llm_16k_causal", "llm_64k_causal"])
 def test_auto_path_follows_the_vote_rate(label, wid, over, expect):
     """With SPARGE_PATH_AUTO the pilot takes the fused path where nearly every
-    (tile, wavefront) votes (image and video recipes) and two passes where
-    few do (the LLM recipe's sink rows): the automatic call's bits equal
-    those of the forced path it chose, and its counters both paths'."""
+    (tile, wavefront) votes (image and video recipes) or rows are short (the
+    LLM recipe at N 16384: some 80 listed tiles per block), and two passes on
+    long rows where few vote (the LLM recipe at N 65536): the automatic
+    call's bits equal those of the forced path it chose, and its counters
+    both paths'."""
     w = I.workload(wid, **over)
     q, k, v = I.make_qkv(w)
     qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
