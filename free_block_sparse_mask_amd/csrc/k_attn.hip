@@ -76,10 +76,6 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // log2-units distance below the running max past which a whole tile's
 // exponentials cannot change a float32 row sum (see attn_stats)
 constexpr float kFarLog2 = 40.0f;
-// fused pass: the exponentials' reference max trails the running max until
-// the latter has risen this many log2 units above it, so O is rescaled only
-// then; P~ stays below 2^kLazyLog2 (see attn_fused)
-constexpr float kLazyLog2 = 8.0f;
 // attention pass 1: K ring slots and tiles loaded ahead, for one query block
 // per workgroup and for packs of dense blocks
 constexpr int kStatsSlots = 2;
@@ -1438,14 +1434,7 @@ void attn_fused(AttnArgs p) {
   f32x16 oacc[G::OT];
 #pragma unroll
   for (int t = 0; t < G::OT; ++t) oacc[t] = f32x16{};
-  float m_run = kNegInf;      // running max, log2 units (the votes use it)
-  // The reference max of the exponentials, l and O: eq. 1's rescale is exact
-  // for any common reference, so it moves to the running max only once that
-  // has risen kLazyLog2 above it, and O is rescaled that seldom.  P~ is then
-  // below 2^kLazyLog2 rather than 1 (the same relative rounding), and the row
-  // maximum still contributes at least 1 to l, so a far tile's share of l
-  // keeps the bound of attn_stats.
-  float m_ref = kNegInf;
+  float m_run = kNegInf;      // running max, log2 units
   float l_half = 0.0f;        // this lane half's share of the row sum
   int n_exec = 0, n_skip = 0, n_void = 0;
   uint32_t vw = 0;
@@ -1474,19 +1463,12 @@ void attn_fused(AttnArgs p) {
     const bool exec = __any(wants_pv);
     const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
     if (!far) {
-      float alpha = 1.0f;
-      if (__any(m_new > m_ref + kLazyLog2)) {
-        // every row moves its reference to its running max (a row without a
-        // visible key yet keeps -inf and alpha 1)
-        alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_ref - m_new);
-        m_ref = m_new;
-        l_half *= alpha;
-#pragma unroll
-        for (int t = 0; t < G::OT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-      }
-      const float neg_m = (m_ref == kNegInf) ? 0.0f : -m_ref;
+      // P~ against the running max itself, so a row's largest score gives
+      // exactly 1 (a trailing reference saved O rescales but rounded that
+      // dominant term to 16 bits too: 2^-9 of its V value, over 1e-2 where
+      // |V| > 5)
+      const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
+      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1498,7 +1480,13 @@ void attn_fused(AttnArgs p) {
         const int o = 4 * (q & 3);
         ps[q] = (vv[o] + vv[o + 1]) + (vv[o + 2] + vv[o + 3]);
       }
-      l_half += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+      l_half = alpha * l_half + (((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      }
       if (exec) {
         // P~ in V's type as the B operand of 4 k-steps, then O^T += V_j^T P~^T
         u32x4 pb[4];

@@ -213,26 +213,30 @@ def test_full_size_gqa_fp8pv():
 MAX_TN = 4096   # SPARGE_MAX_TN of include/sparge.h
 
 
-@pytest.mark.parametrize("H,H_kv,causal,int8", [(2, 1, True, False), (1, 1, False, False), (2, 1, True, True)],
-                         ids=["causal_gqa", "noncausal", "causal_gqa_int8"])
-def test_largest_supported_sequence(H, H_kv, causal, int8):
+@pytest.mark.parametrize("H,H_kv,causal,int8,fused", [(2, 1, True, False, False), (1, 1, False, False, False),
+                                                    (2, 1, True, True, False), (2, 1, True, False, True)],
+                         ids=["causal_gqa", "noncausal", "causal_gqa_int8", "causal_gqa_fused"])
+def test_largest_supported_sequence(H, H_kv, causal, int8, fused):
     """N = 64 * SPARGE_MAX_TN = 262144, the longest sequence the library takes:
     Tn = 4096 key blocks, so the widest M_g rows and row lists, the largest
     LDS lists, vote arrays and (int8) K-scale arrays of both attention
-    passes, and (causal) rows whose dense lists walk 4096 tiles.  The llm_32k
-    recipe at that length; mask rows of every head and sampled query blocks
-    against the oracle."""
+    passes, and (causal) rows whose dense lists walk 4096 tiles; with the
+    fused pass forced, its packs of two dense blocks of one kv head on those
+    rows.  The llm_32k recipe at that length; mask rows of every head and
+    sampled query blocks against the oracle."""
+    from gpu_common import attn_path
     w = I.workload(2, N=64 * MAX_TN, H=H, H_kv=H_kv, causal=causal)
     assert O.num_blocks(w.N, O.BK) == MAX_TN
-    log(f"[full] largest N: H={w.H} Hkv={w.H_kv} N={w.N} causal={w.causal} int8={int8}")
+    log(f"[full] largest N: H={w.H} Hkv={w.H_kv} N={w.N} causal={w.causal} int8={int8} fused={fused}")
     q, k, v = I.make_qkv(w, workers=16)
     if int8:
         v = I.make_tensor(w, I.TENSOR_V, dtype="f16", workers=16)
-    mask, counts, dbg, o16, o32 = _run(w, q, k, v, int8=int8)
+    with attn_path(fb.PATH_FUSED if fused else fb.PATH_AUTO):
+        mask, counts, dbg, o16, o32 = _run(w, q, k, v, int8=int8)
     c = _check_whole(w, mask, counts, o16, o32)
     log(f"   counts {c}")
     _check_heads(w, q, k, v, mask, dbg, o32, list(range(w.H)), int8=int8, v_dtype="f16" if int8 else None,
-                 o16=o16, extra_blocks=_random_blocks(w, 8, seed=150 + w.H + (7 if int8 else 0)))
+                 o16=o16, extra_blocks=_random_blocks(w, 8, seed=150 + w.H + (7 if int8 else 0) + (3 if fused else 0)))
 
 
 def test_full_size_llm_32k_fused_path():
