@@ -237,7 +237,8 @@ int sparge_attn(const void* q, const sparge_tensor* qs, const void* k, const spa
  * `workspace_bytes`: the call's scratch (the transposed V, the per-row
  * softmax statistics and executed-tile lists passed between the two
  * attention kernels, the row lists built from mg when row_cnt/row_idx are
- * NULL, the pairing of dense query blocks and the partial counters) lives
+ * NULL, the pairing of dense query blocks, the partial counters and the
+ * pilot's counts and path flag) lives
  * in a static device array of SPARGE_NOALLOC_SCRATCH_BYTES that each GPU the
  * library runs on holds until the process ends.  The call allocates nothing
  * and frees nothing; its first use on a device looks up that device's copy
