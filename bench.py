@@ -293,7 +293,7 @@ def run_config(torch, fb, I, name, steps, warmup, dev, **over):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus "
               f"{args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import torch

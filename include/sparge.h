@@ -40,7 +40,7 @@ extern "C" {
 
 #define SPARGE_OK 0
 #define SPARGE_EINVAL (-1)        /* bad argument (null pointer, shape, range)  */
-#define SPARGE_EUNSUPPORTED (-2)  /* valid but outside this build (d, N, dtype) */
+#define SPARGE_EUNSUPPORTED (-2)  /* valid but not supported (d, N, dtype)  */
 #define SPARGE_EWORKSPACE (-3)    /* workspace smaller than sparge_workspace_size */
 #define SPARGE_EHIP (-4)          /* a HIP call or kernel launch failed           */
 

@@ -1,5 +1,5 @@
 """A model of the fp8 P~V kernel's own rounding schedule.  NOT the oracle and
-not a parity reference: the GPU's fp8 variant is judged against the oracle's
+not a parity reference: the GPU's fp8 variant is scored against the oracle's
 ``sparse_attention(..., pv8=True)``, which follows Algorithm 1's order.
 
 The kernel differs from that order in one place: its second pass forms

@@ -80,7 +80,7 @@ def test_search_result_is_pinned_by_the_oracle(wid):
     log(f"   oracle L1 {e_or:.5f} vs measured {res.l1:.5f}; mask ambiguous={rep['ambiguous']}")
     assert abs(e_or - res.l1) <= L1_TOL
     assert e_or <= l2 + L1_TOL
-    # every mask the search judged by, the tau = 1 dense ends included, is the oracle's
+    # every mask the search measured, the tau = 1 dense ends included, is the oracle's
     pairs = sorted({(e.tau, e.theta) for e in res.trace})
     assert any(t == 1.0 for t, _ in pairs)
     for tau, theta in pairs:
