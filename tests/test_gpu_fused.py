@@ -116,6 +116,43 @@ def test_fused_short_sequences(N, d, causal):
     assert rep["counts"]["rows"] == H * N
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,N", [(False, 16384 - 37), (True, 32768 - 100)])
+def test_fused_packs_of_dense_blocks(d, causal, N):
+    """Rows of at least 192 live tiles (192 x 2 on a causal call), where the
+    fused path runs the dense query blocks of a kv head in pairs on one K and
+    V stream: a mask in which an odd number of block rows per kv head list
+    every live tile (so one pair has a single member) and the rest about half
+    of them, ragged N.  Both paths give the same decisions and counters, and
+    sampled blocks (paired, unpaired, the ragged last one) match the oracle."""
+    H, Hkv = 2, 1
+    w = I.workload(2, N=N, H=H, H_kv=Hkv, d=d, causal=causal)
+    q, k, v = I.make_qkv(w)
+    Q, K, V = (O.widen(x, w.dtype) for x in (q, k, v))
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
+    Tm, Tn = O.num_blocks(N, O.BQ), O.num_blocks(N, O.BK)
+    rng = np.random.default_rng(31 + d + (1 if causal else 0))
+    mg_np = rng.random((1, H, Tm, Tn)) < 0.5
+    dense = rng.random((H, Tm)) < 0.4
+    if dense.sum() % 2 == 0:
+        dense[0, Tm - 1] = not dense[0, Tm - 1]
+    mg_np[0][dense] = True
+    mg = torch.from_numpy(mg_np.astype(np.uint8)).to(DEV)
+    log(f"[fused packs] d={d} causal={causal} N={N}: Tn={Tn}, {int(dense.sum())} dense block rows")
+    res = _both_paths(qd, kd, vd, mg, w.lam, causal)
+    o16, o32, counts, dbg = res[fb.PATH_FUSED]
+    _, _, counts2, dbg2 = res[fb.PATH_TWO_PASS]
+    assert torch.equal(counts, counts2) and torch.equal(dbg, dbg2)
+    picks = [(h, i) for h in range(H) for i in (0, Tm - 1)]
+    picks += [(h, int(i)) for h in range(H) for i in np.flatnonzero(dense[h])[-3:]]
+    picks += [(h, int(i)) for h in range(H) for i in np.flatnonzero(~dense[h])[-2:]]
+    blocks = sorted({(0, h, i) for h, i in picks})
+    rep = check_attention(o32, counts, dbg, Q, K, V, mg_np, w.lam, causal, "f32", blocks=blocks,
+                          o16=o16, o16_dtype=w.dtype)
+    log(f"   {len(blocks)} blocks: max_abs={rep['max_abs']:.2e} rel_l1={rep['rel_l1']:.2e} "
+        f"flips={rep['lambda_flips']} counts={fb.counts_dict(counts)}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_fused_strided_layouts_and_batches(causal):
     """[B, N, H, d] strides, two batches, GQA, ragged N on the fused path: the
