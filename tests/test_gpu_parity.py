@@ -129,10 +129,10 @@ def test_attention_random_mask_edge_rows(dtype, d, causal):
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_attention_dense_rows_in_packs(causal):
-    """Query blocks that list every live tile share a pass-1 workgroup with up
-    to three other blocks of their kv head.  Two batches, two kv heads of two
-    query heads each, and a ragged N.  The dense blocks per kv head number 7,
-    6, 5 and 9, so packs end padded.  Their i differ, so lists of different
+    """Query blocks that list every live tile share a pass-1 workgroup with
+    another block of their kv head.  Two batches, two kv heads of two query
+    heads each, and a ragged N.  The dense blocks per kv head number 7, 6, 5
+    and 9, so three kv heads end on a pair with an empty slot.  Their i differ, so lists of different
     lengths share one K stream.  The remaining blocks are random and include
     an empty one."""
     B, H, Hkv, N, d = 2, 4, 2, 1100, 64
