@@ -30,8 +30,10 @@
 // CU.
 //
 // attn_fused is the one-pass form (Algorithm 1's shape) for calls in which
-//   nearly every wavefront votes: K and V^T tiles share its ring, and the
-//   P~V of a voted tile follows its vote.  attn_pilot samples the call's
+//   nearly every wavefront votes or rows are short: K and V^T tiles share
+//   its ring (two slots for a single block; four, one barrier per two tiles,
+//   for a pair of dense blocks), and the P~V of a voted tile follows its
+//   vote.  attn_pilot samples the call's
 //   blocks on the device and pilot_decide writes which path the call takes;
 //   the kernels of the other path read that flag and return at once.
 //
@@ -1332,7 +1334,7 @@ __device__ __forceinline__ bool fused_packs(const AttnArgs& p) {
 template <int D, int KIND, int NP>
 size_t fused_lds_bytes(int Tn) {
   using G = Geo<D, KIND>;
-  return (size_t)G::NS2 * G::E_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
+  return (size_t)(NP == 1 ? G::NS2 : 4) * G::E_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
          (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16);
 }
 
@@ -1358,7 +1360,11 @@ void attn_fused(AttnArgs p) {
   constexpr int NW = NP * kWavesPerBlock;
   constexpr int NT = NP * kThreads;
   using LN = Lane<D, KIND, NW>;
-  constexpr int NS = G::NS2;
+  // ring slots, tiles loaded ahead, tiles per barrier: a pack's workgroup
+  // (alone on its CU) passes one barrier per two tiles, as pass 1's pairs do
+  constexpr int NS = PACK ? 4 : G::NS2;
+  constexpr int PD = PACK ? 2 : G::NS2 - 1;
+  constexpr int TPB = PACK ? 2 : 1;
   constexpr int EB = G::E_BYTES;
   constexpr int VCWN = G::V_BYTES / 1024 / NW;    // V^T chunks per wavefront and tile
   static_assert(VCWN >= 1 && G::V_BYTES == VCWN * 1024 * NW, "V^T tiles must split over the wavefronts");
@@ -1439,17 +1445,23 @@ void attn_fused(AttnArgs p) {
   int n_exec = 0, n_skip = 0, n_void = 0;
   uint32_t vw = 0;
 
-  // entry e is used in step e; entries e+1 .. e+NS-2 are in flight when step e
-  // starts, and step e refills the slot entry e-1 used with entry e+NS-1.  The
-  // steps run NS at a time with the slot a constant, so its LDS offsets fold
-  // into the reads.  A packed block whose list has ended only loads.
-  const int pre = min(UCU, NS - 1);
+  // Entry e is used in step e, and step e loads entry e+PD into the slot of
+  // entry e+PD-NS.  Single blocks (TPB = 1, PD = NS-1): at step e's barrier
+  // entry e has landed (e+1 .. e+NS-2 may still be in flight) and every
+  // wavefront is done with e-1.  Packs (TPB = PD = 2, four slots): the
+  // barrier before entries e and e+1 follows the landing of both, and every
+  // wavefront is done with e-2 and e-1, whose slots then take e+2 and e+3;
+  // between barriers the wavefronts drift by up to a tile.  The steps run NS
+  // at a time with the slot a constant, so its LDS offsets fold into the
+  // reads.  A packed block whose list has ended only loads.
+  const int pre = min(UCU, PD);
   for (int t = 0; t < pre; ++t) issue(t, t);
+  static_assert(TPB + PD <= NS && NS % TPB == 0 && PD >= TPB, "a period's slots must be free");
   auto step = [&](int e, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    const int pend = min(UCU - 1, e + NS - 2) - e;
-    wait_pending<LN::KCW + VCWN, NS - 2>(pend);
-    if (e + NS - 1 < UCU) issue(e + NS - 1, (SL + NS - 1) % NS);
+    if constexpr (SL % TPB == 0)
+      wait_pending<LN::KCW + VCWN, PD - TPB>(min(UCU - 1, e + PD - 1) - min(UCU - 1, e + TPB - 1));
+    if (e + PD < UCU) issue(e + PD, (SL + PD) % NS);
     if (PACK && e >= UC) return;
     const int j = __builtin_amdgcn_readfirstlane(entry_tile(e));
     const unsigned char* kt = smem + SL * EB;
