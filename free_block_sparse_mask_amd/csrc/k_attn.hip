@@ -76,8 +76,11 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 // log2-units distance below the running max past which a whole tile's
-// exponentials cannot change a float32 row sum (see attn_stats)
-constexpr float kFarLog2 = 40.0f;
+// exponentials are skipped: each of its P~ is below 2^-32, so it adds less
+// than 64 * 2^-32 = 2^-26 to a row sum l >= 1 (a quarter of float32's half
+// ulp at 1), and the 4096 tiles of the longest row less than 2^-14 of l
+// (see attn_stats)
+constexpr float kFarLog2 = 32.0f;
 // attention pass 1: K ring slots and tiles loaded ahead, for one query block
 // per workgroup and for packs of dense blocks
 constexpr int kStatsSlots = 2;
@@ -715,8 +718,8 @@ void attn_stats(AttnArgs p) {
     // P~ always feeds l (Algorithm 1 computes it before the M_pv test).  When
     // every row's tile maximum lies more than kFarLog2 below its running max,
     // m does not move and each P~ is below 2^-kFarLog2: the tile adds less
-    // than 64 * 2^-40 to l >= 1, which a float32 sum of l cannot hold, so
-    // its exponentials are not evaluated.
+    // than 64 * 2^-32 to l >= 1, under half an ulp of l, so its exponentials
+    // are not evaluated.
     const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
     if (!far) {
       if (!have_sv) to_float();
@@ -1349,7 +1352,7 @@ size_t fused_lds_bytes(int Tn) {
 // when the vote runs P~V, O = exp(m_old - m_new) O + P~ V with P~ = exp(S -
 // m_new) rounded to V's type.  A tile whose rows all lie more than kFarLog2
 // below their running max leaves m, l and O as they are (their P~ are below
-// 2^-40; see attn_stats); its vote is still counted.  The votes, the decision
+// 2^-32; see attn_stats); its vote is still counted.  The votes, the decision
 // map and the counters are those of attn_stats.
 template <int D, int KIND, bool CAUSAL, int NP>
 __global__ __launch_bounds__(NP * kThreads) __attribute__((amdgpu_waves_per_eu(2)))
