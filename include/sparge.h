@@ -26,6 +26,10 @@
  *   the default stream).  Arguments are checked on the host before anything
  *   is enqueued; on a negative return nothing was launched (SPARGE_EHIP: a
  *   launch failed).  sparge_last_error() gives the calling thread's message.
+ * - A device call enqueues kernel launches only (no allocation, copy, memset
+ *   or synchronisation), and every launch rewrites whatever scratch a later
+ *   one reads, so a sequence of calls may be captured into a HIP graph and
+ *   replayed; calls that share a workspace must not overlap.
  * - N == 0, B == 0 or H == 0 is valid and launches nothing.
  */
 #ifndef SPARGE_H
