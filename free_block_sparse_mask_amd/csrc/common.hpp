@@ -86,8 +86,10 @@ constexpr int kPathFused = 2;
 constexpr int kPilotBlocks = 256;
 constexpr int kPilotCounts = 4;
 // the automatic path takes the fused pass when the sampled blocks list at
-// most this many tiles on average
+// most this many tiles on average (16-bit Q/K; int8 Q/K, whose first pass is
+// cheaper, at most half as many)
 constexpr int kFusedMeanTiles = 224;
+constexpr int kFusedMeanTilesI8 = 112;
 constexpr int kPilotTiles = 4;
 
 constexpr int kQuantChunkRows = 1024;       // tokens per partial K column sum

@@ -1132,13 +1132,27 @@ void attn_pv(AttnArgs p) {
 // pilot estimates the vote rate of the call from a sample; pilot_decide
 // writes the path every later kernel of the call reads.
 
-// Row maxima of one tile of S^T for this wavefront (log2 units, scaled):
-// the QK^T MFMAs on the K tile at `kt`, the dead scores masked.  The scores
-// stay in `sv`.
+// The factor that takes tile j's raw scores to log2 units: 1/sqrt(d) log2(e),
+// times the two block scales on the int8 path (the same product, in the same
+// order, as pass 1 forms).  `ks_row`: the kv head's int8 K block scales.
+template <int D, int KIND, int NW>
+__device__ __forceinline__ float tile_scale(const AttnArgs& p, const Lane<D, KIND, NW>& L, const float* ks_row,
+                                            int j) {
+  float c = p.scale_log2;
+  if constexpr (Geo<D, KIND>::I8) c = L.qscale * ks_row[j] * p.scale_log2;
+  return c;
+}
+
+// Row maxima of one tile of S^T for this wavefront (log2 units: the raw
+// maxima times c_scale > 0): the QK^T MFMAs on the K tile at `kt`, the dead
+// scores masked.  The raw scores stay in `sv` (as floats: int8 sums are
+// exact in float32, below 2^24 in magnitude).
 template <int D, int KIND, bool CAUSAL, int NW = kWavesPerBlock>
 __device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KIND, NW>& L,
-                                             const unsigned char* kt, int j, int jm, f32x16 (&sv)[2]) {
+                                             const unsigned char* kt, int j, int jm, float c_scale,
+                                             f32x16 (&sv)[2]) {
   using G = Geo<D, KIND>;
+  using Acc = typename std::conditional<G::I8, i32x16, f32x16>::type;
   constexpr int KLA = 2;      // k-steps the operand reads run ahead of the MFMAs
   u32x4 kf[G::QS][2];
 #pragma unroll
@@ -1146,12 +1160,11 @@ __device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KI
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       kf[s][t] = *reinterpret_cast<const u32x4*>(kt + t * 32 * G::KROW + (L.k_rd ^ (32u * s)));
-  sv[0] = f32x16{};
-  sv[1] = f32x16{};
+  Acc acc[2] = {Acc{}, Acc{}};
 #pragma unroll
   for (int s = 0; s < G::QS; ++s)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) sv[t] = mfma16<KIND == 1>(kf[s][t], L.qf[s], sv[t]);
+    for (int t = 0; t < 2; ++t) acc[t] = mfma_qk<KIND>(kf[s][t], L.qf[s], acc[t]);
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * KLA, 0);
 #pragma unroll
   for (int s = 0; s < G::QS - KLA; ++s) {
@@ -1159,6 +1172,15 @@ __device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KI
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 2 * KLA, 0);
+  if constexpr (G::I8) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[t][r] = (float)acc[t][r];
+  } else {
+    sv[0] = acc[0];
+    sv[1] = acc[1];
+  }
   mask_scores<CAUSAL>(p, sv, j, jm, L.qrow, L.qvalid, L.hl);
   float mq[4];
 #pragma unroll
@@ -1169,7 +1191,7 @@ __device__ __forceinline__ float tile_scores(const AttnArgs& p, const Lane<D, KI
     for (int x = 0; x < 8; x += 2) m = fmaxf(fmaxf(m, sv[q >> 1][o + x]), sv[q >> 1][o + x + 1]);
     mq[q] = m;
   }
-  return max_halves(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * p.scale_log2;
+  return max_halves(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * c_scale;
 }
 
 // Pilot: sampled query block g * stride + stride / 2 of the B H Tm (in
@@ -1191,7 +1213,6 @@ size_t pilot_lds_bytes() {
 }
 template <int D, int KIND, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
-  static_assert(KIND <= 1, "the fused path takes 16-bit Q/K only");
   static_assert(kPilotTiles % kPilotSlots == 0, "whole rounds of slots");
   static_assert(kPilotTiles - 1 <= 7 && 840 % 7 == 0, "840 = lcm(1..8) divides by every stratum count");
   using G = Geo<D, KIND>;
@@ -1217,6 +1238,7 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
   const int UC = p.row_cnt[L.row_id];
   const bool dense = UC == n_live;
   const uint16_t* gl = p.row_idx + L.row_id * p.Tn;
+  const float* ks_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
   // the same in every wavefront of the block: strata after the first tile,
   // and tiles loaded
   const int S = UC > 1 ? min(kPilotTiles - 1, UC - 1) : 0;
@@ -1241,7 +1263,9 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
         mk[r0 + u] = kNegInf;
         if (r0 + u < NL) {
           f32x16 sv[2];
-          mk[r0 + u] = tile_scores<D, KIND, CAUSAL>(p, L, smem + u * G::K_BYTES, tile_of(r0 + u), jm, sv);
+          const int j = tile_of(r0 + u);
+          mk[r0 + u] = tile_scores<D, KIND, CAUSAL>(p, L, smem + u * G::K_BYTES, j, jm,
+                                                    tile_scale(p, L, ks_row, j), sv);
         }
       }
       __syncthreads();        // every wavefront is done with the slots
@@ -1290,16 +1314,18 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
 
 // The call's path: the requested one, or for kPathAuto the fused pass when
 // at least nine tenths of the pilot's weighted (tile, wavefront) pairs voted,
-// or when the sampled blocks list at most kFusedMeanTiles tiles on average.
+// or when the sampled blocks list at most `mean_tiles` tiles on average.
 // A short sample sets new maxima more often than the whole row does, so the
 // pilot overstates lower rates and hardly separates them: it reads 0.64 to
 // 0.72 on the llm recipe from N 4096 (36% of the pairs vote) to 131072 (5%),
 // and 1.0 where all vote (image, video).  The fused pass wins near full
-// rates (30% faster on video) and on short rows (12 to 28% faster at N 4096
-// to 32768, about 150 listed tiles per block or fewer), and loses on long
-// rows of low rates (4% slower at 65536, 15% at 131072, some 300 and more).
+// rates (about 30% faster on image and video) and on short rows: bf16 9 to
+// 21% faster at N 8192 to 32768 (some 150 listed tiles per block or fewer),
+// int8 Q/K, whose first pass costs less, 9 to 19% at N 8192 and 16384 (some
+// 80 or fewer) but 15% slower at 32768.  It loses on long rows of low rates
+// (bf16 9% slower at 131072; int8 22% at 65536).
 // `groups`: the pilot's workgroups (0 when the path is forced).
-__global__ void pilot_decide(AttnArgs p, int groups) {
+__global__ void pilot_decide(AttnArgs p, int groups, int mean_tiles) {
   unsigned long long v = 0, n = 0, uc = 0, nb = 0;
   for (int x = (int)threadIdx.x; x < groups; x += 64) {
     const unsigned long long* pc = p.pilot_cnt + kPilotCounts * x;
@@ -1318,8 +1344,8 @@ __global__ void pilot_decide(AttnArgs p, int groups) {
   if (threadIdx.x != 0) return;
   int path = p.path;
   if (path != kPathTwoPass && path != kPathFused)
-    path = (n > 0 && (10 * v >= 9 * n || uc <= (unsigned long long)kFusedMeanTiles * nb)) ? kPathFused
-                                                                                           : kPathTwoPass;
+    path = (n > 0 && (10 * v >= 9 * n || uc <= (unsigned long long)mean_tiles * nb)) ? kPathFused
+                                                                                      : kPathTwoPass;
   *p.path_flag = path;
 }
 
@@ -1357,7 +1383,6 @@ size_t fused_lds_bytes(int Tn) {
 template <int D, int KIND, bool CAUSAL, int NP>
 __global__ __launch_bounds__(NP * kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fused(AttnArgs p) {
-  static_assert(KIND <= 1, "the fused path takes 16-bit Q/K only");
   using G = Geo<D, KIND>;
   constexpr bool PACK = NP > 1;
   constexpr int NW = NP * kWavesPerBlock;
@@ -1408,6 +1433,7 @@ void attn_fused(AttnArgs p) {
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
   const int n_live = live_tiles<CAUSAL>(p, i);
   const bool dense = PACK || UC == n_live;     // the list is 0, 1, ..., live - 1
+  const float* ks_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
   const int nwords = (p.Tn + 15) / 16;
   uint16_t* lst = reinterpret_cast<uint16_t*>(smem + NS * EB);
   uint32_t* votes = reinterpret_cast<uint32_t*>(smem + NS * EB + (PACK ? 0 : 2 * ((p.Tn + 1) & ~1)));
@@ -1470,7 +1496,8 @@ void attn_fused(AttnArgs p) {
     const unsigned char* kt = smem + SL * EB;
     const unsigned char* vt = kt + G::K_BYTES;
     f32x16 sv[2];
-    const float mloc = tile_scores<D, KIND, CAUSAL, NW>(p, L, kt, j, jm, sv);
+    const float c_scale = tile_scale(p, L, ks_row, j);
+    const float mloc = tile_scores<D, KIND, CAUSAL, NW>(p, L, kt, j, jm, c_scale, sv);
     const float m_new = fmaxf(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
     const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
@@ -1487,7 +1514,7 @@ void attn_fused(AttnArgs p) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sv[t][r] = fast_exp2(fmaf(sv[t][r], p.scale_log2, neg_m));
+        for (int r = 0; r < 16; ++r) sv[t][r] = fast_exp2(fmaf(sv[t][r], c_scale, neg_m));
       float ps[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -1763,9 +1790,9 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 
 template <int D, int KIND, bool CAUSAL, bool PV8>
 hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
-  // 16-bit Q/K with 16-bit P~V may take the fused pass; the others always
-  // take two passes (no path flag)
-  constexpr bool FUSABLE = KIND <= 1 && !PV8;
+  // a 16-bit P~V may take the fused pass (16-bit or int8 Q/K); fp8 P~V
+  // always takes two passes (no path flag)
+  constexpr bool FUSABLE = !PV8;
   AttnArgs a = a0;
   if (!FUSABLE) a.path_flag = nullptr;
   const long long blocks = (long long)a.B * a.H * a.Tm;
@@ -1790,7 +1817,8 @@ hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(pilot_decide, dim3(1), dim3(64), 0, st, a, groups);
+    hipLaunchKernelGGL(pilot_decide, dim3(1), dim3(64), 0, st, a, groups,
+                       Geo<D, KIND>::I8 ? kFusedMeanTilesI8 : kFusedMeanTiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL, 1>),

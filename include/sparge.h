@@ -105,7 +105,8 @@ int sparge_rows_per_wave(void);
  *     tenths of the sampled (tile, wavefront) pairs vote, each sample
  *     weighted by the listed tiles it stands for, or when the sampled blocks
  *     list at most 224 tiles on average.  Nothing is read back to the host.
- * int8 Q/K and the fp8 P~V variant always take two passes.
+ * Both paths take 16-bit or int8 Q/K; the fp8 P~V variant always takes two
+ * passes.
  * sparge_attn_path(p) sets the path of later calls process-wide and returns
  * the previous setting; sparge_attn_path(-1) only returns it.  An unknown p
  * returns SPARGE_EINVAL.

@@ -225,21 +225,75 @@ def test_auto_path_follows_the_vote_rate(label, wid, over, expect):
         assert torch.equal(outs[path][1], outs[fb.PATH_AUTO][1])
 
 
-def test_int8_and_fp8_take_two_passes_whatever_the_request():
-    """int8 Q/K and fp8 P~V have no fused form: a forced fused path changes
-    none of their bits."""
+def test_fp8pv_takes_two_passes_whatever_the_request():
+    """fp8 P~V has no fused form: a forced fused path changes none of its
+    bits."""
     w = I.workload(2, N=1000, H=2, H_kv=1)
-    q, k, _ = I.make_qkv(w)
-    v = I.make_tensor(w, I.TENSOR_V, dtype="f16")
-    qd, kd, vd = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, "f16")
+    q, k, v = I.make_qkv(w)
+    qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
     mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
-    q8, k8, qs, ks = fb.quant_qk_int8(qd, kd)
     res = {}
     for path in (fb.PATH_TWO_PASS, fb.PATH_FUSED):
         with attn_path(path):
-            res[path] = (fb.attn(q8, k8, vd, mask, w.lam, w.causal, q_scale=qs, k_scale=ks)[0],
-                         fb.attn(qd, kd, to_dev(I.make_tensor(w, I.TENSOR_V, dtype=w.dtype), w.dtype), mask,
-                                 w.lam, w.causal, fp8_pv=True)[0])
+            res[path] = fb.attn(qd, kd, vd, mask, w.lam, w.causal, fp8_pv=True, dbg=True)
     torch.cuda.synchronize()
-    assert torch.equal(res[fb.PATH_TWO_PASS][0], res[fb.PATH_FUSED][0])
-    assert torch.equal(res[fb.PATH_TWO_PASS][1], res[fb.PATH_FUSED][1])
+    for x, y in zip(res[fb.PATH_TWO_PASS], res[fb.PATH_FUSED]):
+        assert torch.equal(x, y)
+
+
+INT8_CASES = [
+    # label, workload, overrides, V type, sampled blocks (None: every block), automatic path
+    ("llm_gqa_ragged_causal_f16", 2, {"N": 1100, "H": 4, "H_kv": 2}, "f16", None, "fused"),
+    ("llm_ragged_d64_bf16", 2, {"N": 1100, "H": 4, "H_kv": 2, "d": 64, "causal": False}, "bf16", None, "fused"),
+    ("image_small_bf16", 1, {"N": 64 + 24 * 24, "H": 2, "H_kv": 2, "grid": (24, 24), "text_tokens": 64}, "bf16",
+     None, "fused"),
+    ("video_small_f16", 3, {"N": 4 * 16 * 12, "H": 2, "H_kv": 1, "grid": (4, 16, 12)}, "f16", None, "fused"),
+    ("llm_32k_pairs_causal_f16", 2, {"N": 32768 - 100, "H": 2, "H_kv": 1}, "f16", 10, "two_pass"),
+    ("llm_64k_causal_f16", 2, {"N": 65536, "H": 2, "H_kv": 1}, "f16", 6, "two_pass"),
+]
+
+
+@pytest.mark.parametrize("label,wid,over,v_dtype,n_blocks,auto", INT8_CASES, ids=[c[0] for c in INT8_CASES])
+def test_int8_both_paths_match_oracle(label, wid, over, v_dtype, n_blocks, auto):
+    """int8 Q/K (with fp16 or bf16 P~V) on each stage-2 path: the same lambda
+    decisions, decision map and counters on both, each output within the
+    int8 bar of the oracle (codes and scales of the oracle's quantisation),
+    and the automatic choice: fused where nearly every wavefront votes or
+    rows are short (for int8 at most 112 listed tiles per block on average,
+    half the 16-bit bound), two passes on the LLM recipe from N 32768 on.
+    The long causal rows run the fused pass's pairs of dense blocks; there
+    the oracle checks sampled blocks (the last, the first and seeded random
+    ones)."""
+    w = I.workload(wid, **over)
+    q, k, _ = I.make_qkv(w)
+    v = I.make_tensor(w, I.TENSOR_V, dtype=v_dtype)
+    Q, K, V = O.widen(q, w.dtype), O.widen(k, w.dtype), O.widen(v, v_dtype)
+    qd, kd, vd = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, v_dtype)
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    q8, k8, qs, ks = fb.quant_qk_int8(qd, kd)
+    kw = dict(q_scale=qs, k_scale=ks)
+    res = _both_paths(q8, k8, vd, mask, w.lam, w.causal, **kw)
+    with attn_path(fb.PATH_AUTO):
+        o_auto = fb.attn(q8, k8, vd, mask, w.lam, w.causal, out_f32=True, **kw)[0]
+    torch.cuda.synchronize()
+    _, o32_two, counts, dbg = res[fb.PATH_TWO_PASS]
+    _, o32_fused, counts_f, dbg_f = res[fb.PATH_FUSED]
+    assert torch.equal(counts, counts_f) and torch.equal(dbg, dbg_f)
+    assert torch.equal(o_auto, o32_fused if auto == "fused" else o32_two)
+    assert not torch.equal(o32_two, o32_fused)
+    mg = mask.mg.cpu().numpy().astype(bool)
+    quant = O.quantize_qk(Q, K)
+    Tm = O.num_blocks(w.N, O.BQ)
+    blocks = None
+    if n_blocks is not None:
+        rng = np.random.default_rng(300 + w.N % 997)
+        picks = {(h, Tm - 1) for h in range(w.H)} | {(0, 0)}
+        picks |= {(int(rng.integers(w.H)), int(i)) for i in rng.choice(Tm, size=n_blocks, replace=False)}
+        blocks = sorted((0, h, i) for h, i in picks)
+    for path in (fb.PATH_TWO_PASS, fb.PATH_FUSED):
+        o16, o32 = res[path][0], res[path][1]
+        rep = check_attention(o32, counts, dbg, Q, K, V, mg, w.lam, w.causal, "f32", blocks=blocks, quant=quant,
+                              int8=True, o16=o16, o16_dtype=v_dtype)
+        log(f"[int8 {label}] {'fused' if path == fb.PATH_FUSED else 'two-pass'}: rel_l1={rep['rel_l1']:.2e} "
+            f"cos={rep['cos']:.6f} flips={rep['lambda_flips']}")
+    log(f"   counts {fb.counts_dict(counts)}")

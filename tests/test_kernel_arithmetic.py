@@ -355,6 +355,7 @@ def pilot_estimate(Q, K, mg, lam, causal, blocks_cap=256, tiles=4):
 
 
 FUSED_MEAN_TILES = 224    # kFusedMeanTiles of csrc/common.hpp
+FUSED_MEAN_TILES_I8 = 112  # kFusedMeanTilesI8 (int8 Q/K)
 
 
 def test_pilot_estimate_separates_the_recipes():
@@ -382,6 +383,24 @@ def test_pilot_estimate_separates_the_recipes():
             assert est >= true - 1e-12, (w.name, est, true)
         assert (est >= 0.9) == by_rate, (w.name, est)
         assert (est >= 0.9 or mean_listed <= FUSED_MEAN_TILES) == fused, (w.name, est, mean_listed)
+
+
+def test_int8_tile_bound_separates_16k_from_32k():
+    """With int8 Q/K the automatic path takes the fused pass on the LLM
+    recipe's rows at N 16384 (where it measured faster) and two passes at
+    32768 (where it measured slower): the pilot's mean listed tiles fall on
+    either side of the int8 bound, and both under the 16-bit one."""
+    from oracle import sparge_oracle as O
+    from free_block_sparse_mask_amd import inputs as I
+    means = {}
+    for N in (16384, 32768):
+        w = I.workload(2, N=N, H=1, H_kv=1)
+        q, k, _ = I.make_qkv(w)
+        Q, K = (O.widen(x, w.dtype) for x in (q, k))
+        mg = O.predict_mask(Q, K, w.tau, w.theta, w.causal)["mg"]
+        est, means[N] = pilot_estimate(Q, K, mg, w.lam, w.causal)
+        assert est < 0.9, (N, est)
+    assert means[16384] <= FUSED_MEAN_TILES_I8 < means[32768] <= FUSED_MEAN_TILES, means
 
 
 # ---------------------------------------------------------------------------
