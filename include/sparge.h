@@ -104,7 +104,8 @@ int sparge_rows_per_wave(void);
  *     the list) against it; the call takes the fused path when at least nine
  *     tenths of the sampled (tile, wavefront) pairs vote, each sample
  *     weighted by the listed tiles it stands for, or when the sampled blocks
- *     list at most 224 tiles on average.  Nothing is read back to the host.
+ *     list at most 224 tiles on average (112 with int8 Q/K, whose first pass
+ *     is cheaper).  Nothing is read back to the host.
  * Both paths take 16-bit or int8 Q/K; the fp8 P~V variant always takes two
  * passes.
  * sparge_attn_path(p) sets the path of later calls process-wide and returns
