@@ -214,8 +214,10 @@ MAX_TN = 4096   # SPARGE_MAX_TN of include/sparge.h
 
 
 @pytest.mark.parametrize("H,H_kv,causal,int8,fused", [(2, 1, True, False, False), (1, 1, False, False, False),
-                                                    (2, 1, True, True, False), (2, 1, True, False, True)],
-                         ids=["causal_gqa", "noncausal", "causal_gqa_int8", "causal_gqa_fused"])
+                                                    (2, 1, True, True, False), (2, 1, True, False, True),
+                                                    (2, 1, True, True, True)],
+                         ids=["causal_gqa", "noncausal", "causal_gqa_int8", "causal_gqa_fused",
+                              "causal_gqa_int8_fused"])
 def test_largest_supported_sequence(H, H_kv, causal, int8, fused):
     """N = 64 * SPARGE_MAX_TN = 262144, the longest sequence the library takes:
     Tn = 4096 key blocks, so the widest M_g rows and row lists, the largest
@@ -240,10 +242,10 @@ def test_largest_supported_sequence(H, H_kv, causal, int8, fused):
 
 
 def test_full_size_llm_32k_fused_path():
-    """The fused stage-2 path forced on the llm_32k workload (causal, 32
-    heads, lists up to 512 tiles; the automatic choice takes two passes
-    there): sampled mask rows and blocks against the oracle, whole-output
-    properties, and the two-pass path's counters."""
+    """The fused stage-2 path on the llm_32k workload (causal, 32 heads,
+    lists up to 512 tiles; the automatic choice takes it there too):
+    sampled mask rows and blocks against the oracle, whole-output
+    properties, and the same counters and decisions as the two-pass path."""
     from gpu_common import attn_path
     w = I.workload(2)
     log(f"[full] {w.name} on the fused path")
