@@ -86,9 +86,11 @@ constexpr int kPathFused = 2;
 constexpr int kPilotBlocks = 256;
 constexpr int kPilotCounts = 4;
 // the automatic path takes the fused pass when the sampled blocks list at
-// most this many tiles on average (16-bit Q/K; int8 Q/K, whose first pass is
-// cheaper, at most half as many)
+// most this many tiles on average: 16-bit Q/K and P~V; fp8 P~V, whose V
+// stream is half as large, twice as many; int8 Q/K, whose first pass is
+// cheaper, half as many
 constexpr int kFusedMeanTiles = 224;
+constexpr int kFusedMeanTilesF8 = 448;
 constexpr int kFusedMeanTilesI8 = 112;
 constexpr int kPilotTiles = 4;
 

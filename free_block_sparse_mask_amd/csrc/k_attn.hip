@@ -1321,9 +1321,10 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
 // and 1.0 where all vote (image, video).  The fused pass wins near full
 // rates (about 30% faster on image and video) and on short rows: bf16 9 to
 // 21% faster at N 8192 to 32768 (some 150 listed tiles per block or fewer),
-// int8 Q/K, whose first pass costs less, 9 to 19% at N 8192 and 16384 (some
-// 80 or fewer) but 15% slower at 32768.  It loses on long rows of low rates
-// (bf16 9% slower at 131072; int8 22% at 65536).
+// fp8 P~V (half the V bytes) 4 to 23% faster up to 65536 (some 300), int8
+// Q/K, whose first pass costs less, 6 to 20% at N 8192 and 16384 (some 80
+// or fewer) but 15% slower at 32768.  It loses on long rows of low rates
+// (bf16 15% slower at 131072, fp8 8%; int8 17% at 65536).
 // `groups`: the pilot's workgroups (0 when the path is forced).
 __global__ void pilot_decide(AttnArgs p, int groups, int mean_tiles) {
   unsigned long long v = 0, n = 0, uc = 0, nb = 0;
@@ -1360,11 +1361,21 @@ __device__ __forceinline__ bool fused_packs(const AttnArgs& p) {
   return (CAUSAL ? p.Tn / 2 : p.Tn) >= 192;
 }
 
-template <int D, int KIND, int NP>
+// the fused pass's ring: bytes of a (K, V^T) slot (fp8 V^T with PV8), and
+// slots: four for a pack; for a single block as many as keep the ring at
+// 64 KB (two or four)
+template <int D, int KIND, bool PV8>
+constexpr int fused_slot_bytes() {
+  return PV8 ? Geo<D, KIND>::E8_BYTES : Geo<D, KIND>::E_BYTES;
+}
+template <int D, int KIND, int NP, bool PV8>
+constexpr int fused_slots() {
+  return NP > 1 ? 4 : ((65536 / fused_slot_bytes<D, KIND, PV8>()) >= 4 ? 4 : 2);
+}
+template <int D, int KIND, int NP, bool PV8>
 size_t fused_lds_bytes(int Tn) {
-  using G = Geo<D, KIND>;
-  return (size_t)(NP == 1 ? G::NS2 : 4) * G::E_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
-         (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16);
+  return (size_t)fused_slots<D, KIND, NP, PV8>() * fused_slot_bytes<D, KIND, PV8>() +
+         (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) + (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16);
 }
 
 // The fused pass: the query blocks of a call in the grid order of attn_pv
@@ -1376,11 +1387,13 @@ size_t fused_lds_bytes(int Tn) {
 // of attn_pv) serves both.  Per tile, as Algorithm 1 orders it: S = Q K^T,
 // the running max m and row sum l (eq. 1), the wavefront's lambda vote, and,
 // when the vote runs P~V, O = exp(m_old - m_new) O + P~ V with P~ = exp(S -
-// m_new) rounded to V's type.  A tile whose rows all lie more than kFarLog2
-// below their running max leaves m, l and O as they are (their P~ are below
-// 2^-32; see attn_stats); its vote is still counted.  The votes, the decision
-// map and the counters are those of attn_stats.
-template <int D, int KIND, bool CAUSAL, int NP>
+// m_new) rounded to V's type (PV8: 2^8 P~ rounded to E4M3 at the running
+// max, as Algorithm 1 orders the steps, against attn_pv's fp8 V^T, and the
+// sum scaled by delta_c / 2^8 at the end).  A tile whose rows all lie more
+// than kFarLog2 below their running max leaves m, l and O as they are (their
+// P~ are below 2^-32; see attn_stats); its vote is still counted.  The votes,
+// the decision map and the counters are those of attn_stats.
+template <int D, int KIND, bool CAUSAL, int NP, bool PV8>
 __global__ __launch_bounds__(NP * kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fused(AttnArgs p) {
   using G = Geo<D, KIND>;
@@ -1390,12 +1403,17 @@ void attn_fused(AttnArgs p) {
   using LN = Lane<D, KIND, NW>;
   // ring slots, tiles loaded ahead, tiles per barrier: a pack's workgroup
   // (alone on its CU) passes one barrier per two tiles, as pass 1's pairs do
-  constexpr int NS = PACK ? 4 : G::NS2;
-  constexpr int PD = PACK ? 2 : G::NS2 - 1;
+  constexpr int NS = fused_slots<D, KIND, NP, PV8>();
+  constexpr int PD = PACK ? 2 : NS - 1;
   constexpr int TPB = PACK ? 2 : 1;
-  constexpr int EB = G::E_BYTES;
-  constexpr int VCWN = G::V_BYTES / 1024 / NW;    // V^T chunks per wavefront and tile
-  static_assert(VCWN >= 1 && G::V_BYTES == VCWN * 1024 * NW, "V^T tiles must split over the wavefronts");
+  constexpr int EB = fused_slot_bytes<D, KIND, PV8>();
+  // 1 KB chunks of a V^T tile, and per loading wavefront.  Where a tile has
+  // fewer chunks (of K or V^T) than the workgroup has wavefronts, some load
+  // fewer than others, and each barrier must then wait for every load.
+  constexpr int VCH = (PV8 ? G::V8_BYTES : G::V_BYTES) / 1024;
+  constexpr int VCWN = VCH >= NW ? VCH / NW : 1;
+  static_assert(VCH % NW == 0 || (VCH < NW && PD == TPB), "V^T tiles must split over the wavefronts");
+  static_assert(G::KCH % NW == 0 || (G::KCH < NW && PD == TPB), "K tiles must split over the wavefronts");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ unsigned long long red[NW][4];
   __shared__ int pick[2];
@@ -1444,10 +1462,16 @@ void attn_fused(AttnArgs p) {
   __syncthreads();
   auto entry_tile = [&](int e) -> int { return dense ? e : (int)lst[e]; };
 
-  // V^T tiles: rows of 128 bytes, granules XOR-swizzled by row / 2 (attn_pv);
-  // wavefront w loads rows 8w .. 8w + 7 of every 8 NW rows
+  // 16-bit V^T tiles: rows of 128 bytes, granules XOR-swizzled by row / 2
+  // (attn_pv); wavefront w loads rows 8w .. 8w + 7 of every 8 NW rows.  fp8
+  // V^T (PV8): attn_pv's layout, 1 KB chunk q (rows 16q .. 16q + 15) loaded
+  // by wavefront q % NW.
   const unsigned char* vtbase =
-      reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + L.hk) * D) * p.Np * 2;
+      reinterpret_cast<const unsigned char*>(p.vt) + ((long long)(b * p.Hkv + L.hk) * D) * p.Np * (PV8 ? 1 : 2);
+  const uint32_t v8_off = (uint32_t)((lane / 4) * p.Np) + (uint32_t)(((lane % 4) ^ ((lane / 16) & 3)) * 16);
+  const int f8 = (l32 >> 2) & 3;
+  const uint32_t v8_rd0 = (uint32_t)(l32 * 64 + (((2 * hl) ^ f8) * 16));
+  const uint32_t v8_rd1 = (uint32_t)(l32 * 64 + (((2 * hl + 1) ^ f8) * 16));
   const int v_row0 = 16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP) + lane / 8;
   const uint32_t v_off = (uint32_t)(v_row0 * p.Np * 2) + (uint32_t)(((lane % 8) ^ ((v_row0 / 2) % 8)) * 16);
   const uint32_t v_wl = (uint32_t)((16 * (wave / G::VGRP) + G::VR * (wave % G::VGRP)) * G::VROW);
@@ -1458,11 +1482,23 @@ void attn_fused(AttnArgs p) {
     const int j = __builtin_amdgcn_readfirstlane(entry_tile(e));
     const uint32_t sl = ring_lds + (uint32_t)(slot * EB);
     L.issue_k(p, j, sl);
+    if constexpr (PV8) {
 #pragma unroll
-    for (int c = 0; c < VCWN; ++c) {
-      const int row_c = 16 * c * (NW / G::VGRP);
-      const unsigned char* base = uniform_ptr(vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2);
-      dma16(base, v_off, (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + row_c * G::VROW + v_wl)));
+      for (int c = 0; c < VCWN; ++c) {
+        const int q = c * NW + wave;
+        if (q < VCH) {
+          const unsigned char* base = uniform_ptr(vtbase + (long long)(16 * q) * p.Np + (long long)j * kBk);
+          dma16(base, v8_off, (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + q * 1024)));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < VCWN; ++c) {
+        const int row_c = 16 * c * (NW / G::VGRP);
+        const unsigned char* base = uniform_ptr(vtbase + ((long long)row_c * p.Np + (long long)j * kBk) * 2);
+        dma16(base, v_off,
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl + G::K_BYTES + row_c * G::VROW + v_wl)));
+      }
     }
   };
 
@@ -1529,7 +1565,30 @@ void attn_fused(AttnArgs p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
       }
-      if (exec) {
+      if (exec && PV8) {
+        // 2^8 P~ as E4M3 (P~ <= 1 at the running max, so 2^8 P~ <= 256 is in
+        // range): byte 16t + r of the lane's 32 holds sv[t][r], the key order
+        // of the fp8 V^T rows; then one 64-key MFMA per 32 rows of O^T
+        i32x8 pb8;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int t = x >> 2, r0 = 4 * (x & 3);
+          float y[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] = fminf(sv[t][r0 + q] * 256.0f, 448.0f);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+          pb8[x] = w;
+        }
+#pragma unroll
+        for (int t = 0; t < G::OT; ++t) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(vt + t * 32 * 64 + v8_rd0);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(vt + t * 32 * 64 + v8_rd1);
+          const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                            (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb8, oacc[t], 0, 0, 0, 127, 0, 127);
+        }
+      } else if (exec) {
         // P~ in V's type as the B operand of 4 k-steps, then O^T += V_j^T P~^T
         u32x4 pb[4];
 #pragma unroll
@@ -1585,9 +1644,18 @@ void attn_fused(AttnArgs p) {
   }
   wait_barrier<0>();                       // every vote word is written
 
-  // ---- epilogue: O / l, as attn_pv stores it ----
+  // ---- epilogue: O / l, as attn_pv stores it (fp8: times delta_c / 2^8) ----
   const float l_tot = sum_halves(l_half);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if constexpr (PV8) {
+    const float* vs = p.vscale + (long long)(b * p.Hkv + L.hk) * D;
+#pragma unroll
+    for (int t = 0; t < G::OT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) oacc[t][4 * g + q] *= vs[32 * t + 8 * g + 4 * hl + q] * (1.0f / 256.0f);
+  }
   if (active && L.qvalid && p.out_f32) {
     float* ob = static_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (long long)L.qrow * p.o_sn;
 #pragma unroll
@@ -1790,19 +1858,17 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 
 template <int D, int KIND, bool CAUSAL, bool PV8>
 hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
-  // a 16-bit P~V may take the fused pass (16-bit or int8 Q/K); fp8 P~V
-  // always takes two passes (no path flag)
-  constexpr bool FUSABLE = !PV8;
   AttnArgs a = a0;
-  if (!FUSABLE) a.path_flag = nullptr;
   const long long blocks = (long long)a.B * a.H * a.Tm;
   const long long packs = (long long)a.B * a.Hkv * (pack_slots(a.H, a.Hkv, a.Tm) / kPackBlocks);
   const size_t lds1 = stats_lds_bytes<D, KIND, 1>(a.Tn);
   const size_t lds1p = stats_lds_bytes<D, KIND, kPackBlocks>(a.Tn);
   const size_t lds2 = pv_lds_bytes<D, KIND, PV8>(a.Tn);
   hipError_t e = hipSuccess;
-  if constexpr (FUSABLE) {
-    // the path of this call, on the device: the pilot's estimate or the request
+  {
+    // the path of this call, on the device: the pilot's estimate or the
+    // request (every call may take the fused pass: 16-bit or int8 Q/K,
+    // 16-bit or fp8 P~V)
     int groups = 0;
     if (a.path != kPathTwoPass && a.path != kPathFused) {
       const long long stride = (blocks + kPilotBlocks - 1) / kPilotBlocks;
@@ -1818,15 +1884,16 @@ hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(pilot_decide, dim3(1), dim3(64), 0, st, a, groups,
-                       Geo<D, KIND>::I8 ? kFusedMeanTilesI8 : kFusedMeanTiles);
+                       Geo<D, KIND>::I8 ? kFusedMeanTilesI8 : (PV8 ? kFusedMeanTilesF8 : kFusedMeanTiles));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL, 1>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fused_lds_bytes<D, KIND, 1>(a.Tn));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL, kPackBlocks>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL, 1, PV8>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)fused_lds_bytes<D, KIND, kPackBlocks>(a.Tn));
+                            (int)fused_lds_bytes<D, KIND, 1, PV8>(a.Tn));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL, kPackBlocks, PV8>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)fused_lds_bytes<D, KIND, kPackBlocks, PV8>(a.Tn));
     if (e != hipSuccess) return e;
   }
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stats<D, KIND, CAUSAL, 1>),
@@ -1849,15 +1916,15 @@ hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
   hipLaunchKernelGGL((attn_stats<D, KIND, CAUSAL, 1>), dim3((unsigned)blocks), dim3(kThreads), lds1, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (FUSABLE) {
+  {
     // the fused pass: dense blocks in packs, then the others
-    const size_t ldsfp = fused_lds_bytes<D, KIND, kPackBlocks>(a.Tn);
-    hipLaunchKernelGGL((attn_fused<D, KIND, CAUSAL, kPackBlocks>), dim3((unsigned)packs),
+    const size_t ldsfp = fused_lds_bytes<D, KIND, kPackBlocks, PV8>(a.Tn);
+    hipLaunchKernelGGL((attn_fused<D, KIND, CAUSAL, kPackBlocks, PV8>), dim3((unsigned)packs),
                        dim3(kPackBlocks * kThreads), ldsfp, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t ldsf = fused_lds_bytes<D, KIND, 1>(a.Tn);
-    hipLaunchKernelGGL((attn_fused<D, KIND, CAUSAL, 1>), dim3((unsigned)blocks), dim3(kThreads), ldsf, st, a);
+    const size_t ldsf = fused_lds_bytes<D, KIND, 1, PV8>(a.Tn);
+    hipLaunchKernelGGL((attn_fused<D, KIND, CAUSAL, 1, PV8>), dim3((unsigned)blocks), dim3(kThreads), ldsf, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -3,13 +3,14 @@
 order (oracle.sparse_attention(..., pv8=True)): E4M3 operands, P~ rounded at
 the running max of each step and rescaled exactly.
 
-The kernel rounds exp(S - m_final) in its second pass instead, so the two
-differ by rounding: every output element must lie within the room that
-E4M3's rounding error allows both schedules (tests/gpu_common.py,
-fp8_room), and the whole output within relative L1 2^-4 and cosine 0.998 of
-the oracle's.  Decisions and counters are those of the unquantised rule.
+The fused pass rounds at the running max too, in float32; the two-pass path
+rounds exp(S - m_final) in its second pass instead.  Either way every output
+element must lie within the room that E4M3's rounding error allows both
+schedules (tests/gpu_common.py, fp8_room), and the whole output within
+relative L1 2^-4 and cosine 0.998 of the oracle's.  Decisions and counters
+are those of the unquantised rule, on both paths.
 
-A second, tighter check compares the kernel with a model of its own
+A second, tighter check compares the two-pass path with a model of its own
 schedule (tests/fp8_kernel_model.py).  It is a diagnostic for arithmetic
 slips, not parity: its constants come from probes of the kernel.
 """
@@ -25,7 +26,7 @@ from free_block_sparse_mask_amd import inputs as I
 from oracle import sparge_oracle as O
 
 import fp8_kernel_model as KM
-from gpu_common import DEV, FP8_REL_L1, check_fp8, fp8_room, log, rel_l1, to_bits, to_dev
+from gpu_common import DEV, FP8_REL_L1, attn_path, check_fp8, fp8_room, log, rel_l1, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -68,12 +69,17 @@ def _all_blocks(w):
     return [(b, h, i) for b in range(w.B) for h in range(w.H) for i in range(O.num_blocks(w.N, O.BQ))]
 
 
+PATHS = [(fb.PATH_TWO_PASS, "two_pass"), (fb.PATH_FUSED, "fused")]
+
+
+@pytest.mark.parametrize("path,pname", PATHS, ids=[p[1] for p in PATHS])
 @pytest.mark.parametrize("label,wid,over", CASES, ids=[c[0] for c in CASES])
-def test_fp8pv_matches_oracle(label, wid, over):
+def test_fp8pv_matches_oracle(label, wid, over, path, pname):
     w = I.workload(wid, **over)
-    log(f"[fp8pv] {label}: H={w.H} Hkv={w.H_kv} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    log(f"[fp8pv {pname}] {label}: H={w.H} Hkv={w.H_kv} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
     q, k, v = I.make_qkv(w)
-    mask, o16, o32, counts, dbg = _run(w, q, k, v)
+    with attn_path(path):
+        mask, o16, o32, counts, dbg = _run(w, q, k, v)
     Q, K, V = (O.widen(x, w.dtype) for x in (q, k, v))
     mg = mask.mg.cpu().numpy().astype(bool)
     gdec = dbg.cpu().numpy().astype(np.int8)
@@ -93,12 +99,14 @@ def test_fp8pv_matches_oracle(label, wid, over):
     assert e_exact <= FP8_REL_L1
 
 
-def test_fp8pv_int8_qk_matches_oracle():
+@pytest.mark.parametrize("path,pname", PATHS, ids=[p[1] for p in PATHS])
+def test_fp8pv_int8_qk_matches_oracle(path, pname):
     w = I.workload(2, N=1000, H=2, H_kv=1)
     q, k, _ = I.make_qkv(w)
     v = I.make_tensor(w, I.TENSOR_V, dtype="f16")
-    log(f"[fp8pv int8] N={w.N}")
-    mask, o16, o32, counts, dbg = _run(w, q, k, v, v_dtype="f16", int8=True)
+    log(f"[fp8pv int8 {pname}] N={w.N}")
+    with attn_path(path):
+        mask, o16, o32, counts, dbg = _run(w, q, k, v, v_dtype="f16", int8=True)
     Q, K = O.widen(q, w.dtype), O.widen(k, w.dtype)
     V = O.widen(v, "f16")
     quant = O.quantize_qk(Q, K)
@@ -127,28 +135,34 @@ def test_fp8pv_channel_scales_and_extreme_channels():
     Q, K, V = (O.widen(x, "bf16") for x in (q, k, v))
     mg_np = np.ones((1, H, O.num_blocks(N, 128), O.num_blocks(N, 64)), dtype=bool)
     mg = torch.from_numpy(mg_np.astype(np.uint8)).to(DEV)
-    o32, counts, dbg = fb.attn(qd, kd, vd, mg, -np.inf, False, dbg=True, out_f32=True, fp8_pv=True)
+    with attn_path(fb.PATH_TWO_PASS):
+        o32, counts, dbg = fb.attn(qd, kd, vd, mg, -np.inf, False, dbg=True, out_f32=True, fp8_pv=True)
+    with attn_path(fb.PATH_FUSED):
+        o32f, counts_f, dbg_f = fb.attn(qd, kd, vd, mg, -np.inf, False, dbg=True, out_f32=True, fp8_pv=True)
     torch.cuda.synchronize()
+    assert torch.equal(counts, counts_f) and torch.equal(dbg, dbg_f)
     gdec = dbg.cpu().numpy().astype(np.int8)
     ref, _, _ = O.sparse_attention(Q, K, V, mg_np, -np.inf, False, skip_override=gdec, pv8=True)
     blocks = [(0, 0, i) for i in range(mg_np.shape[2])]
     room = fp8_room(Q, K, V, mg_np, False, gdec, blocks, ref=ref)
-    og = o32.cpu().double().numpy()
-    assert np.all(og[..., 1] == 0.0)
-    assert np.all(np.abs(og - ref) <= room)
-    for c in (0, 2, 3, 10):
-        e = rel_l1(ref[..., c], og[..., c])
-        log(f"   channel {c}: rel_l1 vs oracle {e:.2e}")
-        assert e <= FP8_REL_L1
+    for o in (o32, o32f):
+        og = o.cpu().double().numpy()
+        assert np.all(og[..., 1] == 0.0)
+        assert np.all(np.abs(og - ref) <= room)
+        for c in (0, 2, 3, 10):
+            e = rel_l1(ref[..., c], og[..., c])
+            log(f"   channel {c}: rel_l1 vs oracle {e:.2e}")
+            assert e <= FP8_REL_L1
 
 
 @pytest.mark.parametrize("label,wid,over", CASES[:4], ids=[c[0] for c in CASES[:4]])
 def test_fp8pv_kernel_schedule_model(label, wid, over):
-    """Diagnostic, not parity: the kernel against a float64 model of its own
-    two-pass schedule (P~ at the final max, V scales floored at 2^-100)."""
+    """Diagnostic, not parity: the two-pass path against a float64 model of
+    its own schedule (P~ at the final max, V scales floored at 2^-100)."""
     w = I.workload(wid, **over)
     q, k, v = I.make_qkv(w)
-    mask, o16, o32, counts, dbg = _run(w, q, k, v)
+    with attn_path(fb.PATH_TWO_PASS):
+        mask, o16, o32, counts, dbg = _run(w, q, k, v)
     Q, K, V = (O.widen(x, w.dtype) for x in (q, k, v))
     mg = mask.mg.cpu().numpy().astype(bool)
     gdec = dbg.cpu().numpy().astype(np.int8)

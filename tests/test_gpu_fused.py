@@ -225,20 +225,31 @@ def test_auto_path_follows_the_vote_rate(label, wid, over, expect):
         assert torch.equal(outs[path][1], outs[fb.PATH_AUTO][1])
 
 
-def test_fp8pv_takes_two_passes_whatever_the_request():
-    """fp8 P~V has no fused form: a forced fused path changes none of its
-    bits."""
-    w = I.workload(2, N=1000, H=2, H_kv=1)
+@pytest.mark.parametrize("label,wid,over,expect", [
+    ("video_small", 3, {"N": 4 * 16 * 12, "H": 2, "H_kv": 1, "grid": (4, 16, 12)}, "fused"),
+    ("llm_64k_causal", 2, {"N": 65536, "H": 2, "H_kv": 1}, "fused"),
+    ("llm_128k_causal", 2, {"N": 131072, "H": 2, "H_kv": 1}, "two_pass"),
+], ids=["video_small", "llm_64k_causal", "llm_128k_causal"])
+def test_fp8pv_paths_and_automatic_choice(label, wid, over, expect):
+    """fp8 P~V on each path: the same decisions, decision map and counters
+    (the oracle comparison of both is in test_gpu_fp8pv.py), different bits
+    (the fused pass rounds P~ at the running max, the second pass at the
+    final one), and the automatic choice: fused on the LLM recipe up to N
+    65536 (fp8's bound of 448 listed tiles), two passes at 131072."""
+    w = I.workload(wid, **over)
     q, k, v = I.make_qkv(w)
     qd, kd, vd = (to_dev(x, w.dtype) for x in (q, k, v))
     mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
     res = {}
-    for path in (fb.PATH_TWO_PASS, fb.PATH_FUSED):
+    for path in (fb.PATH_TWO_PASS, fb.PATH_FUSED, fb.PATH_AUTO):
         with attn_path(path):
-            res[path] = fb.attn(qd, kd, vd, mask, w.lam, w.causal, fp8_pv=True, dbg=True)
+            res[path] = fb.attn(qd, kd, vd, mask, w.lam, w.causal, fp8_pv=True, dbg=True, out_f32=True)
     torch.cuda.synchronize()
-    for x, y in zip(res[fb.PATH_TWO_PASS], res[fb.PATH_FUSED]):
-        assert torch.equal(x, y)
+    two, fused, auto = res[fb.PATH_TWO_PASS], res[fb.PATH_FUSED], res[fb.PATH_AUTO]
+    assert torch.equal(two[1], fused[1]) and torch.equal(two[2], fused[2])
+    assert not torch.equal(two[0], fused[0])
+    assert torch.equal(auto[0], fused[0] if expect == "fused" else two[0])
+    log(f"[fp8pv paths] {label}: counts {fb.counts_dict(two[1])}")
 
 
 INT8_CASES = [

@@ -356,6 +356,7 @@ def pilot_estimate(Q, K, mg, lam, causal, blocks_cap=256, tiles=4):
 
 FUSED_MEAN_TILES = 224    # kFusedMeanTiles of csrc/common.hpp
 FUSED_MEAN_TILES_I8 = 112  # kFusedMeanTilesI8 (int8 Q/K)
+FUSED_MEAN_TILES_F8 = 448  # kFusedMeanTilesF8 (16-bit Q/K, fp8 P~V)
 
 
 def test_pilot_estimate_separates_the_recipes():
@@ -401,6 +402,21 @@ def test_int8_tile_bound_separates_16k_from_32k():
         est, means[N] = pilot_estimate(Q, K, mg, w.lam, w.causal)
         assert est < 0.9, (N, est)
     assert means[16384] <= FUSED_MEAN_TILES_I8 < means[32768] <= FUSED_MEAN_TILES, means
+
+
+def test_fp8_tile_bound_takes_the_fused_pass_at_64k():
+    """With fp8 P~V the fused pass measured faster on the LLM recipe up to N
+    65536 and slower at 131072 (the 128K GQA workload lists 622 tiles per
+    block on average): the pilot's mean at 65536 falls under the fp8 bound
+    and over the 16-bit one."""
+    from oracle import sparge_oracle as O
+    from free_block_sparse_mask_amd import inputs as I
+    w = I.workload(2, N=65536, H=1, H_kv=1)
+    q, k, _ = I.make_qkv(w)
+    Q, K = (O.widen(x, w.dtype) for x in (q, k))
+    mg = O.predict_mask(Q, K, w.tau, w.theta, w.causal)["mg"]
+    est, mean = pilot_estimate(Q, K, mg, w.lam, w.causal)
+    assert est < 0.9 and FUSED_MEAN_TILES < mean <= FUSED_MEAN_TILES_F8 < 622, (est, mean)
 
 
 # ---------------------------------------------------------------------------
