@@ -104,10 +104,10 @@ int sparge_rows_per_wave(void);
  *     the list) against it; the call takes the fused path when at least nine
  *     tenths of the sampled (tile, wavefront) pairs vote, each sample
  *     weighted by the listed tiles it stands for, or when the sampled blocks
- *     list at most 224 tiles on average (112 with int8 Q/K, whose first pass
- *     is cheaper).  Nothing is read back to the host.
- * Both paths take 16-bit or int8 Q/K; the fp8 P~V variant always takes two
- * passes.
+ *     list at most 224 tiles on average (448 with fp8 P~V, whose V stream is
+ *     half as large; 112 with int8 Q/K, whose first pass is cheaper).
+ *     Nothing is read back to the host.
+ * Both paths take 16-bit or int8 Q/K and 16-bit or fp8 P~V.
  * sparge_attn_path(p) sets the path of later calls process-wide and returns
  * the previous setting; sparge_attn_path(-1) only returns it.  An unknown p
  * returns SPARGE_EINVAL.
@@ -275,8 +275,9 @@ int sparge_attn_noalloc(const void* q, const sparge_tensor* qs, const void* k, c
  *   V is scaled per channel by delta_c = 2^e, e the least integer with
  *     max_n |V[n, c]| <= 448 * 2^e (clamped at 2^-100; 1 for a zero
  *     channel), so V / delta_c is exact before its one rounding to E4M3;
- *   P~ = exp(S - m_final) (m_final: the row's final running max) is scaled
- *     by 2^8 and rounded to E4M3;
+ *   P~ = exp(S - m) is scaled by 2^8 and rounded to E4M3, m the running max
+ *     at that tile on the fused path (Algorithm 1's order), the row's final
+ *     running max on the two-pass path;
  *   O = delta_c * sum(P8 V8) / 2^8 / l, with l the float32 row sum of the
  *     unrounded P~ and the products summed in float32 on the matrix cores.
  * Arguments as sparge_attn, except v_dtype (SPARGE_F16 or SPARGE_BF16): the
