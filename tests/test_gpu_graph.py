@@ -51,15 +51,29 @@ def _same(got, ref):
 
 
 @pytest.mark.parametrize("path,pname", PATHS, ids=[p[1] for p in PATHS])
-@pytest.mark.parametrize("label,wid,over", CASES, ids=[c[0] for c in CASES])
-def test_graph_replay_matches_eager(label, wid, over, path, pname):
+@pytest.mark.parametrize("label,wid,over,variant", [c + (None,) for c in CASES] + [
+    ("llm_gqa_ragged_causal_int8", 2, {"N": 3000, "H": 4, "H_kv": 2}, "int8"),
+    ("video_small_fp8", 3, {"N": 4 * 16 * 12, "H": 2, "H_kv": 1, "grid": (4, 16, 12)}, "fp8"),
+], ids=[c[0] for c in CASES] + ["llm_gqa_ragged_causal_int8", "video_small_fp8"])
+def test_graph_replay_matches_eager(label, wid, over, variant, path, pname):
+    """Also with int8 Q/K (quantisation inside the graph) and with fp8 P~V."""
     w = I.workload(wid, **over)
     qd, kd, vd = _inputs(w, w.wid)
+    if variant == "int8":
+        vd = vd.float().to(torch.float16)
     ws = torch.empty_like(fb.workspace(qd, kd))
 
     def run(q, k, v):
+        if variant == "int8":
+            v = v.float().to(torch.float16) if v.dtype != torch.float16 else v
         mask = fb.predict_mask(q, k, w.tau, w.theta, w.causal, ws=ws)
-        o, counts, _ = fb.attn(q, k, v, mask, w.lam, w.causal, ws=ws)
+        kw = {}
+        if variant == "int8":
+            q, k, qs, ks = fb.quant_qk_int8(q, k, ws=ws)
+            kw = dict(q_scale=qs, k_scale=ks)
+        elif variant == "fp8":
+            kw = dict(fp8_pv=True)
+        o, counts, _ = fb.attn(q, k, v, mask, w.lam, w.causal, ws=ws, **kw)
         return mask, o, counts
 
     with attn_path(path):
