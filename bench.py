@@ -21,7 +21,11 @@ step counts:
 * ``mask_share_vs_n``: the llm_32k recipe at N = 8K ... 128K, the share of
   the step that mask prediction takes (the analogue of the pages' Table 3);
 * ``cpu_baseline``: the float64 oracle on a bounded sample of the headline
-  workload, on the host's cores.
+  workload, on the host's cores;
+* ``paths`` (only with ``--paths``): one attention call (after its mask) on
+  each stage-2 path, two passes, fused and the automatic choice, per
+  workload, for 16-bit Q/K and P~V, int8 Q/K (prefix ``int8/``) or fp8 P~V
+  (prefix ``fp8/``), with the share of (tile, wavefront) pairs that vote.
 
 Prints one JSON line.  The metric is dense-equivalent attention TFLOPS =
 (4 N^2 d H, halved for causal) / step time, with the achieved sparsity and
@@ -51,6 +55,9 @@ BQ, BK, ROWS = 128, 64, 32
 
 CONFIG_NAMES = ("tiny", "image_dit", "llm_32k", "video_dit_raster", "video_dit_hilbert")
 SWEEP_N = (8192, 16384, 32768, 65536, 131072)
+# --paths all: the workloads of the stage-2 path comparison, in each variant
+PATH_WORKLOADS = ("tiny", "image_dit", "video_dit_hilbert", "llm:8192", "llm:16384", "llm:32768", "llm:65536",
+                  "gqa:32768", "gqa:131072")
 # the pages' Table 3 (prediction ms vs full-attention ms; hardware, heads and
 # head dim not stated), quoted as context beside the sweep
 PAGES_TABLE3 = {8192: (0.251, 6.649), 16384: (0.487, 26.83), 32768: (0.972, 106.68),
@@ -79,6 +86,9 @@ def parse():
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    ap.add_argument("--paths", default="none",
+                    help="comma list of [int8/|fp8/]{tiny,image_dit,video_dit_hilbert,llm:N,gqa:N} to time on "
+                         "each stage-2 path, or 'all' (every workload in each variant)")
     return ap.parse_args()
 
 
@@ -290,6 +300,57 @@ def run_config(torch, fb, I, name, steps, warmup, dev, **over):
     return rec
 
 
+def run_paths(torch, fb, I, spec, steps, warmup, dev):
+    """One attention call (after its mask) on each stage-2 path: two passes,
+    fused, and the automatic choice; median and min over `steps` calls."""
+    variant, _, name = spec.rpartition("/")
+    if name.startswith("llm:"):
+        w = I.workload(2, N=int(name[4:]))
+    elif name.startswith("gqa:"):
+        w = I.workload(4, N=int(name[4:]))
+    else:
+        w = I.workload({"tiny": 0, "image_dit": 1, "video_dit_hilbert": 3}[name])
+    q, k, v = I.make_qkv(w, workers=16)
+    qd, kd, vd = (upload(torch, dev, x, w.dtype) for x in (q, k, v))
+    del q, k, v
+    if name == "video_dit_hilbert":
+        perm = torch.from_numpy(fb.hilbert_index(*w.grid)[0]).to(dev)
+        qd, kd, vd = (fb.hilbert_permute(x, perm) for x in (qd, kd, vd))
+    ws = fb.workspace(qd, kd)
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
+    kw = {}
+    if variant == "int8":
+        qd, kd, qs, ks = fb.quant_qk_int8(qd, kd, ws=ws)
+        vd = vd.float().to(torch.float16)
+        kw = dict(q_scale=qs, k_scale=ks)
+    elif variant == "fp8":
+        kw = dict(fp8_pv=True)
+    elif variant:
+        raise SystemExit(f"unknown variant {variant}")
+    rec = {"workload": spec, "H": w.H, "H_kv": w.H_kv, "N": w.N, "d": w.d, "causal": w.causal}
+    for path, pname in ((fb.PATH_TWO_PASS, "two_pass"), (fb.PATH_FUSED, "fused"), (fb.PATH_AUTO, "auto")):
+        old = fb.attn_path(path)
+        try:
+            def step(ev):
+                if ev is not None:
+                    ev[0].record()
+                out = fb.attn(qd, kd, vd, mask, w.lam, w.causal, ws=ws, **kw)
+                if ev is not None:
+                    ev[1].record()
+                return out[1]
+            counts, iv, _ = run_steps(torch, step, steps, warmup, 2)
+        finally:
+            fb.attn_path(old)
+        rec[pname + "_ms"] = stats(iv[0])
+    c = fb.counts_dict(counts)
+    rec["vote_share"] = c["pv_exec"] / max(1, c["pv_exec"] + c["pv_skip"])
+    log(f"[bench] paths {spec}: two passes {rec['two_pass_ms']['median']:.3f} ms, fused "
+        f"{rec['fused_ms']['median']:.3f} ms, automatic {rec['auto_ms']['median']:.3f} ms, "
+        f"vote share {rec['vote_share']:.3f}")
+    del qd, kd, vd, ws, mask
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -452,6 +513,12 @@ def main():
                          "pages_table3_share": None if pages is None else pages[0] / pages[1]})
         result["mask_share_vs_n"] = {"recipe": "llm_32k (B=1, H=32, d=128, causal, AR(1)+sink), N varied",
                                      "rows": rows}
+
+    specs = [] if args.paths == "none" else (
+        [v + x for v in ("", "int8/", "fp8/") for x in PATH_WORKLOADS if not (v and x == "tiny")]
+        if args.paths == "all" else [x for x in args.paths.split(",") if x])
+    if specs:
+        result["paths"] = [run_paths(torch, fb, I, x, args.steps, args.warmup, dev) for x in specs]
 
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4
