@@ -24,8 +24,9 @@ step counts:
   workload, on the host's cores;
 * ``paths`` (only with ``--paths``): one attention call (after its mask) on
   each stage-2 path, two passes, fused and the automatic choice, per
-  workload, for 16-bit Q/K and P~V, int8 Q/K (prefix ``int8/``) or fp8 P~V
-  (prefix ``fp8/``), with the share of (tile, wavefront) pairs that vote.
+  workload, for 16-bit Q/K and P~V, int8 Q/K (prefix ``int8/``), fp8 P~V
+  (prefix ``fp8/``) or both (``int8fp8/``), with the share of (tile,
+  wavefront) pairs that vote.
 
 Prints one JSON line.  The metric is dense-equivalent attention TFLOPS =
 (4 N^2 d H, halved for causal) / step time, with the achieved sparsity and
@@ -87,8 +88,8 @@ def parse():
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"))
     ap.add_argument("--paths", default="none",
-                    help="comma list of [int8/|fp8/]{tiny,image_dit,video_dit_hilbert,llm:N,gqa:N} to time on "
-                         "each stage-2 path, or 'all' (every workload in each variant)")
+                    help="comma list of [int8/|fp8/|int8fp8/]{tiny,image_dit,video_dit_hilbert,llm:N,gqa:N} to "
+                         "time on each stage-2 path, or 'all' (every workload, 16-bit, int8/ and fp8/)")
     return ap.parse_args()
 
 
@@ -318,15 +319,15 @@ def run_paths(torch, fb, I, spec, steps, warmup, dev):
         qd, kd, vd = (fb.hilbert_permute(x, perm) for x in (qd, kd, vd))
     ws = fb.workspace(qd, kd)
     mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
+    if variant not in ("", "int8", "fp8", "int8fp8"):
+        raise SystemExit(f"unknown variant {variant}")
     kw = {}
-    if variant == "int8":
+    if variant.startswith("int8"):
         qd, kd, qs, ks = fb.quant_qk_int8(qd, kd, ws=ws)
         vd = vd.float().to(torch.float16)
         kw = dict(q_scale=qs, k_scale=ks)
-    elif variant == "fp8":
-        kw = dict(fp8_pv=True)
-    elif variant:
-        raise SystemExit(f"unknown variant {variant}")
+    if variant.endswith("fp8"):
+        kw["fp8_pv"] = True
     rec = {"workload": spec, "H": w.H, "H_kv": w.H_kv, "N": w.N, "d": w.d, "causal": w.causal}
     for path, pname in ((fb.PATH_TWO_PASS, "two_pass"), (fb.PATH_FUSED, "fused"), (fb.PATH_AUTO, "auto")):
         old = fb.attn_path(path)
