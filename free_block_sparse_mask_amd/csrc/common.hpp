@@ -88,10 +88,12 @@ constexpr int kPilotCounts = 4;
 // the automatic path takes the fused pass when the sampled blocks list at
 // most this many tiles on average: 16-bit Q/K and P~V; fp8 P~V, whose V
 // stream is half as large, twice as many; int8 Q/K, whose first pass is
-// cheaper, half as many
+// cheaper, half as many; int8 Q/K with fp8 P~V, whose first pass is cheap
+// and whose second reads the fewest bytes, a quarter
 constexpr int kFusedMeanTiles = 224;
 constexpr int kFusedMeanTilesF8 = 448;
 constexpr int kFusedMeanTilesI8 = 112;
+constexpr int kFusedMeanTilesI8F8 = 64;
 constexpr int kPilotTiles = 4;
 
 constexpr int kQuantChunkRows = 1024;       // tokens per partial K column sum

@@ -31,9 +31,10 @@
 //
 // attn_fused is the one-pass form (Algorithm 1's shape) for calls in which
 //   nearly every wavefront votes or rows are short: K and V^T tiles share
-//   its ring (two slots for a single block; four, one barrier per two tiles,
-//   for a pair of dense blocks), and the P~V of a voted tile follows its
-//   vote.  attn_pilot samples the call's
+//   its ring (for a single block two slots, or four where they fit in 64 KB;
+//   for a pair of dense blocks four, one barrier per two tiles), and the P~V
+//   of a voted tile follows its vote, for every Q/K and P~V type the passes
+//   take.  attn_pilot samples the call's
 //   blocks on the device and pilot_decide writes which path the call takes;
 //   the kernels of the other path read that flag and return at once.
 //
@@ -1323,8 +1324,9 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
 // 21% faster at N 8192 to 32768 (some 150 listed tiles per block or fewer),
 // fp8 P~V (half the V bytes) 4 to 23% faster up to 65536 (some 300), int8
 // Q/K, whose first pass costs less, 6 to 20% at N 8192 and 16384 (some 80
-// or fewer) but 15% slower at 32768.  It loses on long rows of low rates
-// (bf16 15% slower at 131072, fp8 8%; int8 17% at 65536).
+// or fewer) but 15% slower at 32768, and int8 Q/K with fp8 P~V 14% faster
+// at 8192 (some 40) but 4% slower at 16384.  It loses on long rows of low
+// rates (bf16 15% slower at 131072, fp8 8%; int8 17% at 65536).
 // `groups`: the pilot's workgroups (0 when the path is forced).
 __global__ void pilot_decide(AttnArgs p, int groups, int mean_tiles) {
   unsigned long long v = 0, n = 0, uc = 0, nb = 0;
@@ -1884,7 +1886,8 @@ hipError_t launch_passes(const AttnArgs& a0, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(pilot_decide, dim3(1), dim3(64), 0, st, a, groups,
-                       Geo<D, KIND>::I8 ? kFusedMeanTilesI8 : (PV8 ? kFusedMeanTilesF8 : kFusedMeanTiles));
+                       Geo<D, KIND>::I8 ? (PV8 ? kFusedMeanTilesI8F8 : kFusedMeanTilesI8)
+                                        : (PV8 ? kFusedMeanTilesF8 : kFusedMeanTiles));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused<D, KIND, CAUSAL, 1, PV8>),

@@ -105,7 +105,8 @@ int sparge_rows_per_wave(void);
  *     tenths of the sampled (tile, wavefront) pairs vote, each sample
  *     weighted by the listed tiles it stands for, or when the sampled blocks
  *     list at most 224 tiles on average (448 with fp8 P~V, whose V stream is
- *     half as large; 112 with int8 Q/K, whose first pass is cheaper).
+ *     half as large; 112 with int8 Q/K, whose first pass is cheaper; 64 with
+ *     both).
  *     Nothing is read back to the host.
  * Both paths take 16-bit or int8 Q/K and 16-bit or fp8 P~V.
  * sparge_attn_path(p) sets the path of later calls process-wide and returns

@@ -252,6 +252,31 @@ def test_fp8pv_paths_and_automatic_choice(label, wid, over, expect):
     log(f"[fp8pv paths] {label}: counts {fb.counts_dict(two[1])}")
 
 
+@pytest.mark.parametrize("N,expect", [(8192, "fused"), (16384, "two_pass")])
+def test_int8_fp8pv_automatic_choice(N, expect):
+    """int8 Q/K with fp8 P~V: both paths give the same decisions and
+    counters, and the automatic choice takes the fused pass on the LLM
+    recipe at N 8192 (some 40 listed tiles per block, under that pair's bound
+    of 64) and two passes at 16384 (some 80)."""
+    w = I.workload(2, N=N, H=2, H_kv=1)
+    q, k, _ = I.make_qkv(w)
+    v = I.make_tensor(w, I.TENSOR_V, dtype="f16")
+    qd, kd, vd = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, "f16")
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
+    q8, k8, qs, ks = fb.quant_qk_int8(qd, kd)
+    res = {}
+    for path in (fb.PATH_TWO_PASS, fb.PATH_FUSED, fb.PATH_AUTO):
+        with attn_path(path):
+            res[path] = fb.attn(q8, k8, vd, mask, w.lam, w.causal, q_scale=qs, k_scale=ks, fp8_pv=True, dbg=True,
+                                out_f32=True)
+    torch.cuda.synchronize()
+    two, fused, auto = res[fb.PATH_TWO_PASS], res[fb.PATH_FUSED], res[fb.PATH_AUTO]
+    assert torch.equal(two[1], fused[1]) and torch.equal(two[2], fused[2])
+    assert not torch.equal(two[0], fused[0])
+    assert torch.equal(auto[0], fused[0] if expect == "fused" else two[0])
+    log(f"[int8 fp8pv paths] N={N}: counts {fb.counts_dict(two[1])}")
+
+
 INT8_CASES = [
     # label, workload, overrides, V type, sampled blocks (None: every block), automatic path
     ("llm_gqa_ragged_causal_f16", 2, {"N": 1100, "H": 4, "H_kv": 2}, "f16", None, "fused"),

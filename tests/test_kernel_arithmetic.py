@@ -357,6 +357,7 @@ def pilot_estimate(Q, K, mg, lam, causal, blocks_cap=256, tiles=4):
 FUSED_MEAN_TILES = 224    # kFusedMeanTiles of csrc/common.hpp
 FUSED_MEAN_TILES_I8 = 112  # kFusedMeanTilesI8 (int8 Q/K)
 FUSED_MEAN_TILES_F8 = 448  # kFusedMeanTilesF8 (16-bit Q/K, fp8 P~V)
+FUSED_MEAN_TILES_I8F8 = 64  # kFusedMeanTilesI8F8 (int8 Q/K, fp8 P~V)
 
 
 def test_pilot_estimate_separates_the_recipes():
@@ -477,3 +478,20 @@ def test_vote_codes_counted_from_the_packed_words():
                 continue
             want = 1 if ex else (2 if fin else 3)
             assert 3 - fin - ex == want
+
+
+def test_int8_fp8_tile_bound_separates_8k_from_16k():
+    """With int8 Q/K and fp8 P~V the fused pass measured faster on the LLM
+    recipe at N 8192 and slower at 16384: the pilot's mean listed tiles fall
+    on either side of that pair's bound, and both under the int8 one."""
+    from oracle import sparge_oracle as O
+    from free_block_sparse_mask_amd import inputs as I
+    means = {}
+    for N in (8192, 16384):
+        w = I.workload(2, N=N, H=1, H_kv=1)
+        q, k, _ = I.make_qkv(w)
+        Q, K = (O.widen(x, w.dtype) for x in (q, k))
+        mg = O.predict_mask(Q, K, w.tau, w.theta, w.causal)["mg"]
+        est, means[N] = pilot_estimate(Q, K, mg, w.lam, w.causal)
+        assert est < 0.9, (N, est)
+    assert means[8192] <= FUSED_MEAN_TILES_I8F8 < means[16384] <= FUSED_MEAN_TILES_I8, means
