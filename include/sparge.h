@@ -86,8 +86,8 @@ const char* sparge_last_error(void);
 int sparge_rows_per_wave(void);
 
 /*
- * How sparge_attn (and sparge_attn_noalloc) run stage 2 for 16-bit Q/K/V.
- * Both paths compute the same method ([Review] eq. 1, the sparse warp online
+ * How sparge_attn, sparge_attn_fp8pv and sparge_attn_noalloc run stage 2,
+ * for every Q/K and P~V type they take.  Both paths compute the same method ([Review] eq. 1, the sparse warp online
  * softmax rule, Algorithm 1) with the same lambda decisions and counters;
  * they round P~ at different points:
  *   SPARGE_PATH_TWO_PASS: a statistics pass (running max, row sums, votes;
@@ -106,9 +106,7 @@ int sparge_rows_per_wave(void);
  *     weighted by the listed tiles it stands for, or when the sampled blocks
  *     list at most 224 tiles on average (448 with fp8 P~V, whose V stream is
  *     half as large; 112 with int8 Q/K, whose first pass is cheaper; 64 with
- *     both).
- *     Nothing is read back to the host.
- * Both paths take 16-bit or int8 Q/K and 16-bit or fp8 P~V.
+ *     both).  Nothing is read back to the host.
  * sparge_attn_path(p) sets the path of later calls process-wide and returns
  * the previous setting; sparge_attn_path(-1) only returns it.  An unknown p
  * returns SPARGE_EINVAL.
