@@ -153,6 +153,7 @@ int sparge_attn_path(int path) {
 size_t sparge_workspace_size(const sparge_tensor* q, const sparge_tensor* k) {
   if (q == nullptr || k == nullptr || q->B < 0 || q->H < 0 || q->N < 0 || q->d <= 0 || k->H <= 0)
     return 0;
+  if (k->B != q->B || k->N != q->N || k->d != q->d || q->H % k->H != 0) return 0;
   return carve_workspace(nullptr, q->B, q->H, k->H, q->N, q->d).total + 256;
 }
 

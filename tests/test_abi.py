@@ -5,6 +5,8 @@ import ctypes
 import math
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -234,3 +236,23 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     assert L.sparge_attn_noalloc(FAKE, ctypes.byref(q), FAKE, ctypes.byref(k), FAKE, ctypes.byref(k), FAKE,
                                  ctypes.byref(q), fb.BF16, fb.BF16, fb.BF16, None, None, FAKE, None, None,
                                  0.5, 1, FAKE, None, None) == fb.SPARGE_EINVAL
+
+
+def test_header_and_library_from_c(tmp_path):
+    """include/sparge.h compiles as C99 with every warning an error, a C
+    program links against libsparge.so, and its host-only calls (version,
+    rows per wavefront, the path setting, Hilbert and grid orders, workspace
+    sizes, the error codes and messages) behave as the header states
+    (tests/c/abi_from_c.c)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    libdir = os.path.dirname(fb.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    cmd = [cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c", "abi_from_c.c"), "-o", exe, f"-L{libdir}", "-lsparge",
+           f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
