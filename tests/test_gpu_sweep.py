@@ -5,7 +5,8 @@ cover a few at a time: the input recipe (segments, 2-D or 3-D Gaussian
 fields, AR(1) with sinks), B, H, H_kv and the GQA group, a ragged N (down to
 a single token), d, the storage type, causal or not, tau, theta, lambda
 (down to -inf, where every visited tile runs P~V), the stage-2 path (forced
-or automatic) and the Q/K and P~V types (16-bit, int8 Q/K, fp8 P~V, both).
+or automatic), the Q/K and P~V types (16-bit, int8 Q/K, fp8 P~V, both) and
+the layout of Q, K and V ([B, H, N, d], or the strides of [B, N, H, d]).
 Every case runs stage 1 and stage 2 through the C ABI and meets the same
 acceptance as the fixed cases: M_g and the lists bit-exact outside the
 oracle's ambiguous entries, the output and the counters against the oracle
@@ -35,7 +36,7 @@ PATHS = {"auto": fb.PATH_AUTO, "two_pass": fb.PATH_TWO_PASS, "fused": fb.PATH_FU
 
 
 def draw_case(n: int):
-    """Case n: (workload, path name, variant, V's type)."""
+    """Case n: (workload, path name, variant, V's type, input layout)."""
     rng = np.random.default_rng([SWEEP_SEED, n])
     recipe = str(rng.choice(["segments", "grf2d", "grf3d", "ar1"]))
     d = int(rng.choice([64, 128]))
@@ -65,20 +66,22 @@ def draw_case(n: int):
     path = str(rng.choice(list(PATHS)))
     variant = str(rng.choice(["", "", "int8", "fp8", "int8fp8"]))
     v_dtype = str(rng.choice(["f16", "bf16"])) if variant.startswith("int8") else dtype
+    # a third of the cases pass Q, K and V with the strides of [B, N, H, d]
+    layout = str(rng.choice(["bhnd", "bhnd", "bnhd"]))
     w = I.Workload(900 + n, f"sweep{n}", B, H, H_kv, N, d, dtype, causal, tau, theta, lam, recipe,
                    grid=grid, text_tokens=text)
-    return w, path, variant, v_dtype
+    return w, path, variant, v_dtype, layout
 
 
 def _label(n: int) -> str:
-    w, path, variant, v_dtype = draw_case(n)
+    w, path, variant, v_dtype, layout = draw_case(n)
     return (f"{n:02d}-{w.recipe}-B{w.B}H{w.H}kv{w.H_kv}-N{w.N}-d{w.d}-{w.dtype}{'-causal' if w.causal else ''}"
-            f"-{path}{'-' + variant if variant else ''}")
+            f"-{path}{'-' + variant if variant else ''}{'-' + layout if layout != 'bhnd' else ''}")
 
 
 @pytest.mark.parametrize("n", range(N_CASES), ids=[_label(n) for n in range(N_CASES)])
 def test_random_configuration_matches_oracle(n):
-    w, path, variant, v_dtype = draw_case(n)
+    w, path, variant, v_dtype, layout = draw_case(n)
     int8 = variant.startswith("int8")
     fp8 = variant.endswith("fp8")
     log(f"[sweep {n}] {_label(n)} tau={w.tau} theta={w.theta} lam={w.lam} V {v_dtype}")
@@ -86,6 +89,8 @@ def test_random_configuration_matches_oracle(n):
     Q, K = O.widen(q, w.dtype), O.widen(k, w.dtype)
     V = O.widen(v, v_dtype)
     qd, kd, vd = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, v_dtype)
+    if layout == "bnhd":     # the same values, token stride H * d, head stride d
+        qd, kd, vd = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (qd, kd, vd))
 
     with attn_path(PATHS[path]):
         mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal)
