@@ -723,3 +723,59 @@ def test_predict_mask_head_flags_the_same_entries(label, p, tau, flagged, kept):
     for i in range(r["mg"].shape[0]):
         assert set(np.nonzero(r["mg"][i])[0]) == kept, i
         assert set(np.nonzero(r["ambiguous"][i])[0]) == flagged, i
+
+
+# ---------------------------------------------------------------------------
+# Monotone structure the definitions fix
+# ---------------------------------------------------------------------------
+
+def test_topcdf_keep_set_grows_with_tau():
+    """[Review] eq. 8: TopCdf keeps the shortest prefix of the probabilities
+    in descending order whose mass reaches tau of the row, so a larger tau
+    keeps a prefix of the same order that is at least as long; the fix blocks
+    of eq. 9 and the -inf key blocks of eq. 7 do not depend on tau.  M_g can
+    only gain ones as tau grows (a reversed cut or comparison breaks this)."""
+    Q = _rand((1, 2, 1100, 64), 41)
+    K = _rand((1, 1, 1100, 64), 42)
+    # smooth the tokens so that some blocks are self-similar and TopCdf acts
+    Q += 2.0 * _rand((1, 2, 1, 64), 43)
+    K += 2.0 * _rand((1, 1, 1, 64), 44)
+    prev = None
+    sizes = []
+    for tau in (0.1, 0.3, 0.5, 0.7, 0.9, 0.99, 1.0):
+        mg = O.predict_mask(Q, K, tau, 0.5, causal=True)["mg"]
+        if prev is not None:
+            assert not (prev & ~mg).any(), tau
+        prev = mg
+        sizes.append(int(mg.sum()))
+    assert sizes[0] < sizes[-1], sizes
+
+
+def test_lambda_decisions_nest_and_leave_the_row_sums_alone():
+    """[Review] sparse warp online softmax: a group skips P~V on a tile when
+    every row's tile maximum lies more than |lambda| below its running max.
+    The running max and the row sum l never depend on lambda (P~ feeds l
+    before the test), so lowering lambda can only turn skips into executions:
+    the executed (tile, group) pairs nest, their total with the skipped ones
+    stays fixed, and with V = 1 (every row of O is then l_exec / l) O grows
+    toward 1 as lambda falls."""
+    from free_block_sparse_mask_amd import inputs as I
+    w = I.workload(2, N=700, H=1, H_kv=1)      # AR(1) tokens with sinks: skips at every lambda below
+    q, k, _ = I.make_qkv(w)
+    Q, K = (O.widen(x, w.dtype) for x in (q, k))
+    V = np.ones((1, 1, w.N, w.d))
+    mg = O.tile_live(w.N, O.BQ, O.BK, True)[None, None]
+    prev_dec, prev_o, totals, execs = None, None, set(), []
+    for lam in (-0.5, -1.0, -2.0, -4.0, -8.0, -16.0, -np.inf):
+        o, cnt, dec = O.sparse_attention(Q, K, V, mg, lam, True)
+        ran = dec == 1
+        totals.add(cnt["pv_exec"] + cnt["pv_skip"])
+        execs.append(cnt["pv_exec"])
+        if prev_dec is not None:
+            assert not (prev_dec & ~ran).any(), lam
+            assert np.all(o >= prev_o - 1e-12), lam
+        assert np.all(o <= 1.0 + 1e-12)
+        prev_dec, prev_o = ran, o
+    assert len(totals) == 1
+    assert execs == sorted(execs) and execs[0] < execs[-1], execs
+    assert np.allclose(prev_o, 1.0, atol=1e-12)
