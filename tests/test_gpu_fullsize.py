@@ -22,7 +22,7 @@ import free_block_sparse_mask_amd as fb
 from free_block_sparse_mask_amd import inputs as I
 from oracle import sparge_oracle as O
 
-from gpu_common import DEV, check_attention, check_mask, log
+from gpu_common import DEV, attn_path, check_attention, check_mask, log
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -258,3 +258,44 @@ def test_full_size_llm_32k_fused_path():
     c = _check_whole(w, mask, counts, o16, o32)
     log(f"   counts {c}")
     _check_heads(w, q, k, v, mask, dbg, o32, [0, 31], o16=o16, extra_blocks=_random_blocks(w, 24, seed=170))
+
+
+def test_full_size_mask_and_decisions_are_monotone():
+    """At 128K GQA, over every head, tile and wavefront (where the oracle
+    cannot follow): eq. 8 keeps a longer prefix of one order as tau grows and
+    eqs. 7 and 9 do not depend on tau, so M_g at tau 0.8 lies inside M_g at
+    0.9; the running max and the row sums do not depend on lambda, so on one
+    mask the (tile, wavefront) pairs that run P~V at lambda -4 lie inside
+    those at -6, which lie inside those at -8, executed plus skipped stays
+    fixed, and the fused pass takes the same decisions as the two passes."""
+    w = I.workload(4)
+    q, k, v = I.make_qkv(w)
+    qd, kd, vd = _up(q, w.dtype), _up(k, w.dtype), _up(v, w.dtype)
+    ws = fb.workspace(qd, kd)
+    log(f"[monotone] {w.name}: tau 0.8 / 0.9, lambda -4 / -6 / -8")
+    mg_lo = fb.predict_mask(qd, kd, 0.8, w.theta, w.causal, ws=ws).mg.clone()
+    mask = fb.predict_mask(qd, kd, 0.9, w.theta, w.causal, ws=ws)
+    torch.cuda.synchronize()
+    assert not bool((mg_lo.bool() & ~mask.mg.bool()).any())
+    n_lo, n_hi = int(mg_lo.sum().item()), int(mask.mg.sum().item())
+    assert n_lo < n_hi
+    prev, totals = None, set()
+    for lam in (-4.0, -6.0, -8.0):
+        with attn_path(fb.PATH_TWO_PASS):
+            _, counts, dbg = fb.attn(qd, kd, vd, mask, lam, w.causal, ws=ws, dbg=True)
+        torch.cuda.synchronize()
+        ran = dbg == 1
+        c = fb.counts_dict(counts)
+        totals.add(c["pv_exec"] + c["pv_skip"])
+        log(f"   lambda {lam}: pv_exec {c['pv_exec']} pv_skip {c['pv_skip']}")
+        if prev is not None:
+            assert not bool((prev & ~ran).any()), lam
+        prev = ran
+        if lam == -6.0:
+            dbg6, counts6 = dbg, counts
+    assert len(totals) == 1
+    with attn_path(fb.PATH_FUSED):
+        _, counts_f, dbg_f = fb.attn(qd, kd, vd, mask, -6.0, w.causal, ws=ws, dbg=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dbg_f, dbg6) and torch.equal(counts_f, counts6)
+    log(f"   M_g ones: {n_lo} at tau 0.8, {n_hi} at 0.9; fused decisions equal at lambda -6")
