@@ -299,3 +299,35 @@ def test_full_size_mask_and_decisions_are_monotone():
     torch.cuda.synchronize()
     assert torch.equal(dbg_f, dbg6) and torch.equal(counts_f, counts6)
     log(f"   M_g ones: {n_lo} at tau 0.8, {n_hi} at 0.9; fused decisions equal at lambda -6")
+
+
+def test_full_size_rows_normalise():
+    """With V = 1 every output element is the share of its row's softmax
+    weight that ran P~V (eq. 1 divides by the row sum of all visited
+    weights).  At lambda = -inf every listed tile runs, so each of the 4.2 M
+    rows at 128K GQA gives 1 up to the rounding of P~ to bf16 (each weight
+    within 2^-8 of itself, the row's largest, exp(0) = 1 at its tile,
+    exactly; 1e-5 more for float32 sums and rescales), and exactly the empty
+    rows give 0; at lambda -6 no element exceeds that bound above 1.  On
+    both stage-2 paths."""
+    w = I.workload(4)
+    q, k, _ = I.make_qkv(w)
+    qd, kd = _up(q, w.dtype), _up(k, w.dtype)
+    vd = torch.ones((w.B, w.H_kv, w.N, w.d), dtype=torch.bfloat16, device=DEV)
+    ws = fb.workspace(qd, kd)
+    mask = fb.predict_mask(qd, kd, w.tau, w.theta, w.causal, ws=ws)
+    for path, pname in ((fb.PATH_TWO_PASS, "two_pass"), (fb.PATH_FUSED, "fused")):
+        with attn_path(path):
+            o_all, c_all, _ = fb.attn(qd, kd, vd, mask, -np.inf, w.causal, ws=ws, out_f32=True)
+            o_lam, _, _ = fb.attn(qd, kd, vd, mask, w.lam, w.causal, ws=ws, out_f32=True)
+        torch.cuda.synchronize()
+        c = fb.counts_dict(c_all)
+        empty = (o_all == 0).all(dim=-1)
+        assert int(empty.sum().item()) == c["empty_rows"], (int(empty.sum().item()), c)
+        dev = float((o_all[~empty] - 1.0).abs().max().item())
+        top = float(o_lam.max().item())
+        lo = float(o_lam.min().item())
+        log(f"[normalise] {pname}: empty rows {c['empty_rows']}, max |O - 1| {dev:.2e} at lambda -inf; "
+            f"O in [{lo:.3g}, {top:.6f}] at lambda {w.lam}")
+        assert dev <= 2.0 ** -8 + 1e-5
+        assert lo >= 0.0 and top <= 1.0 + 2.0 ** -8 + 1e-5
