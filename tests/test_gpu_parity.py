@@ -84,6 +84,37 @@ def test_predict_mask_at_tau_near_one(label, wid, over, tau):
         log(f"   every column with p >= 2^-61 kept ({kept_small} of them below 1e-6)")
 
 
+@pytest.mark.parametrize("tau,theta", [(1e-9, 0.0), (1e-9, 2.0), (0.5, 0.0), (0.5, -1.0)],
+                         ids=["tau0_no_fix", "tau0_all_fix", "half_no_fix", "half_theta_negative"])
+@pytest.mark.parametrize("label,wid,over", [CASES[2], CASES[5]], ids=[CASES[2][0], CASES[5][0]])
+def test_predict_mask_at_extreme_tau_and_theta(label, wid, over, tau, theta):
+    """The ends of the hyper-parameters: tau -> 0+ keeps only each selective
+    row's largest probability (its exclusive prefix 0 is below any positive
+    tau * sum; ties go to the lower j); theta <= 0 leaves no fix block (a
+    self-similarity is never negative) so TopCdf alone decides; theta > 1
+    makes every block fix, so M_g is the live tiles."""
+    w, q, k, v = _case(wid, **over)
+    log(f"[predict ends] {label}: tau={tau} theta={theta} N={w.N} causal={w.causal}")
+    qd, kd = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    mask = fb.predict_mask(qd, kd, tau, theta, w.causal)
+    torch.cuda.synchronize()
+    Q, K = O.widen(q, w.dtype), O.widen(k, w.dtype)
+    rep = check_mask(mask, Q, K, tau, theta, w.causal)
+    mg = mask.mg.cpu().numpy().astype(bool)
+    live = O.tile_live(w.N, O.BQ, O.BK, w.causal)
+    if theta > 1.0:
+        assert np.array_equal(mg, np.broadcast_to(live, mg.shape))
+    elif tau < 1e-6:
+        # one block per row: the row's largest probability (no fix block forces
+        # more).  The ambiguity window marks exactly that entry (its exclusive
+        # prefix 0 lies within 1e-4 of tau * sum), so compare it directly: both
+        # sides rank the same float64 map, and no other entry lies near a tie.
+        assert np.all(mg.sum(axis=-1) == 1)
+        assert rep["ambiguous"] == mg.shape[0] * mg.shape[1] * mg.shape[2]
+        assert np.array_equal(mg, rep["ref_mg"])
+    log(f"   ones per row {mg.sum(axis=-1).mean():.2f}; ambiguous={rep['ambiguous']}")
+
+
 @pytest.mark.parametrize("label,wid,over", CASES, ids=[c[0] for c in CASES])
 def test_attention_given_oracle_mask(label, wid, over):
     w, q, k, v = _case(wid, **over)
