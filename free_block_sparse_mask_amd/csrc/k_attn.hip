@@ -113,6 +113,11 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Whether x holds on any active lane: the lane mask of the compare itself
+// (an SGPR pair), so a vote and everything built from it stay scalar; HIP's
+// __any() takes the predicate through a VGPR and back.
+__device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -589,7 +594,7 @@ void attn_stats(AttnArgs p) {
   }
   LN L;
   L.init(p, b, h, i, wq);
-  const int jm = first_masked_tile<CAUSAL>(p, L.q0);
+  const int jm = __builtin_amdgcn_readfirstlane(first_masked_tile<CAUSAL>(p, L.q0));   // q0 is wavefront-uniform
   const long long row_id = L.row_id;
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
   const int n_live = live_tiles<CAUSAL>(p, i);
@@ -713,15 +718,16 @@ void attn_stats(AttnArgs p) {
     const float m_new = fmaxf(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
     // lambda vote over the wavefront's 32 rows
-    const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
-    const bool any_finite = __any(finite_row);
-    const bool exec = __any(wants_pv);
+    // (ballots of single compares, so each is the compare's lane mask)
+    const unsigned long long fin_mask = __builtin_amdgcn_ballot_w64(finite_row);
+    const bool any_finite = fin_mask != 0;
+    const bool exec = (fin_mask & __builtin_amdgcn_ballot_w64(!(mloc - m_new < p.lam_log2))) != 0;
     // P~ always feeds l (Algorithm 1 computes it before the M_pv test).  When
     // every row's tile maximum lies more than kFarLog2 below its running max,
     // m does not move and each P~ is below 2^-kFarLog2: the tile adds less
     // than 64 * 2^-32 to l >= 1, under half an ulp of l, so its exponentials
     // are not evaluated.
-    const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
+    const bool far = (fin_mask & __builtin_amdgcn_ballot_w64(!(mloc - m_new < -kFarLog2))) == 0;
     if (!far) {
       if (!have_sv) to_float();
       const float neg_m = (m_new == kNegInf) ? 0.0f : -m_new;
@@ -935,7 +941,7 @@ void attn_pv(AttnArgs p) {
   if (!map_block(p, p.Tm, b, h, i)) return;
   Lane<D, KIND, kWavesPerBlock> L;
   L.init(p, b, h, i, (int)(threadIdx.x >> 6));
-  const int jm = first_masked_tile<CAUSAL>(p, L.q0);
+  const int jm = __builtin_amdgcn_readfirstlane(first_masked_tile<CAUSAL>(p, L.q0));   // q0 is wavefront-uniform
   const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
   const long long row_id = L.row_id;
   const int U = p.ucnt[row_id];
@@ -1234,7 +1240,7 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
   LN L;
   L.init(p, b, h, i, wave);
-  const int jm = first_masked_tile<CAUSAL>(p, L.q0);
+  const int jm = __builtin_amdgcn_readfirstlane(first_masked_tile<CAUSAL>(p, L.q0));   // q0 is wavefront-uniform
   const int n_live = live_tiles<CAUSAL>(p, i);
   const int UC = p.row_cnt[L.row_id];
   const bool dense = UC == n_live;
@@ -1276,7 +1282,7 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
     }
   }
   // the first tile votes wherever a row sees a key (m_new = its own max)
-  unsigned long long v_first = __any(mk[0] > kNegInf) ? 1 : 0;
+  unsigned long long v_first = wave_any(mk[0] > kNegInf) ? 1 : 0;
   unsigned long long votes = 0, pairs = 0;
   float m_run = mk[0];
 #pragma unroll
@@ -1285,9 +1291,9 @@ __global__ __launch_bounds__(kThreads) void attn_pilot(AttnArgs p, int stride) {
       const float m_new = fmaxf(m_run, mk[k]);
       const bool fin = mk[k] > kNegInf;
       const bool v = fin && !(mk[k] - m_new < p.lam_log2);
-      if (__any(fin)) {
+      if (wave_any(fin)) {
         pairs += 1;
-        votes += __any(v) ? 1 : 0;
+        votes += wave_any(v) ? 1 : 0;
       }
       m_run = m_new;
     }
@@ -1447,7 +1453,7 @@ void attn_fused(AttnArgs p) {
   }
   LN L;
   L.init(p, b, h, i, wq);
-  const int jm = first_masked_tile<CAUSAL>(p, L.q0);
+  const int jm = __builtin_amdgcn_readfirstlane(first_masked_tile<CAUSAL>(p, L.q0));   // q0 is wavefront-uniform
   const int l32 = L.l32, hl = L.hl;
   const long long row_id = L.row_id;
   const int last_q = min(p.N, (i + 1) * kBq) - 1;
@@ -1538,10 +1544,11 @@ void attn_fused(AttnArgs p) {
     const float mloc = tile_scores<D, KIND, CAUSAL, NW>(p, L, kt, j, jm, c_scale, sv);
     const float m_new = fmaxf(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
-    const bool wants_pv = finite_row && !(mloc - m_new < p.lam_log2);
-    const bool any_finite = __any(finite_row);
-    const bool exec = __any(wants_pv);
-    const bool far = !__any(finite_row && !(mloc - m_new < -kFarLog2));
+    // (ballots of single compares, so each is the compare's lane mask)
+    const unsigned long long fin_mask = __builtin_amdgcn_ballot_w64(finite_row);
+    const bool any_finite = fin_mask != 0;
+    const bool exec = (fin_mask & __builtin_amdgcn_ballot_w64(!(mloc - m_new < p.lam_log2))) != 0;
+    const bool far = (fin_mask & __builtin_amdgcn_ballot_w64(!(mloc - m_new < -kFarLog2))) == 0;
     if (!far) {
       // P~ against the running max itself, so a row's largest score gives
       // exactly 1 (a trailing reference saved O rescales but rounded that
@@ -1561,7 +1568,7 @@ void attn_fused(AttnArgs p) {
         ps[q] = (vv[o] + vv[o + 1]) + (vv[o + 2] + vv[o + 3]);
       }
       l_half = alpha * l_half + (((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
-      if (__any(alpha != 1.0f)) {
+      if (wave_any(alpha != 1.0f)) {
 #pragma unroll
         for (int t = 0; t < G::OT; ++t)
 #pragma unroll
