@@ -177,20 +177,26 @@ __device__ __forceinline__ void dma16(const unsigned char* sbase, uint32_t voff,
 
 // Waits until at most N vector-memory operations of this wavefront are in
 // flight and its LDS operations are done, then joins the workgroup barrier.
-template <int N>
+// LGKM = false leaves the LDS and scalar-load counter alone: for a loop
+// whose LDS reads have all been consumed before it gets here, so scalar
+// loads may stay in flight across the barrier.
+template <int N, bool LGKM = true>
 __device__ __forceinline__ void wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  if constexpr (LGKM)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 // the same with N = pending * PER, pending (wavefront-uniform) clamped to [0, P]
-template <int PER, int P>
+template <int PER, int P, bool LGKM = true>
 __device__ __forceinline__ void wait_pending(int pending) {
   if constexpr (P <= 0) {
-    wait_barrier<0>();
+    wait_barrier<0, LGKM>();
   } else {
     if (pending >= P)
-      wait_barrier<P * PER>();
+      wait_barrier<P * PER, LGKM>();
     else
-      wait_pending<PER, P - 1>(pending);
+      wait_pending<PER, P - 1, LGKM>(pending);
   }
 }
 
@@ -275,11 +281,28 @@ size_t stats_lds_bytes(int Tn) {
   return (size_t)(NP == 1 ? kStatsSlots : PackRing<G::I8>::slots) * G::K_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
          (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
 }
+// Pass 2 with int8 Q/K, 16-bit P~V and a two-slot ring (d = 128) reads its
+// entry list and the K block scales with scalar loads, one step ahead,
+// instead of staging them in LDS: the ring alone (48 KB) is then the
+// workgroup's LDS, and three workgroups share a CU instead of two.
+template <int D, int KIND, bool PV8>
+constexpr bool pv_scalar_list() {
+  return Geo<D, KIND>::I8 && !PV8 && Geo<D, KIND>::NS2 == 2;
+}
 template <int D, int KIND, bool PV8>
 size_t pv_lds_bytes(int Tn) {
   using G = Geo<D, KIND>;
   const size_t ring = PV8 ? (size_t)G::NS8 * G::E8_BYTES : (size_t)G::NS2 * G::E_BYTES;
+  if (pv_scalar_list<D, KIND, PV8>()) return ring;
   return ring + (size_t)4 * Tn + (G::I8 ? (size_t)4 * Tn : 0);
+}
+
+// A 32-bit load that the compiler issues as a scalar (SMEM) load: the
+// address must be wavefront-uniform, and the memory is not written while
+// the kernel runs (the constant address space promises that).
+typedef const __attribute__((address_space(4))) uint32_t const_u32;
+__device__ __forceinline__ uint32_t load_scalar(const void* base, long long idx) {
+  return ((const_u32*)base)[idx];
 }
 
 // Per-lane pieces common to both passes: Q fragment, K DMA offsets, read bases.
@@ -944,15 +967,28 @@ void attn_pv(AttnArgs p) {
   const int jm = __builtin_amdgcn_readfirstlane(first_masked_tile<CAUSAL>(p, L.q0));   // q0 is wavefront-uniform
   const int tid = L.tid, wave = L.wave, lane = L.lane, l32 = L.l32, hl = L.hl;
   const long long row_id = L.row_id;
-  const int U = p.ucnt[row_id];
+  constexpr bool SLIST = pv_scalar_list<D, KIND, PV8>();
+  const int U = __builtin_amdgcn_readfirstlane(p.ucnt[row_id]);
   const uint32_t* gul = p.ulist + row_id * p.Tn;
   const float* kscale_row = G::I8 ? p.k_scale + (long long)(b * p.Hkv + L.hk) * p.Tn : nullptr;
   uint32_t* ent = reinterpret_cast<uint32_t*>(smem + NS * EB);
   float* ksc = reinterpret_cast<float*>(ent + p.Tn);
-  for (int e = tid; e < U; e += kThreads) {
-    const uint32_t en = gul[e];
-    ent[e] = en;
-    if constexpr (G::I8) ksc[e] = kscale_row[en & 0xffffu];
+  if constexpr (!SLIST) {
+    for (int e = tid; e < U; e += kThreads) {
+      const uint32_t en = gul[e];
+      ent[e] = en;
+      if constexpr (G::I8) ksc[e] = kscale_row[en & 0xffffu];
+    }
+  }
+  // SLIST: entry e and its K scale (en_c, ks_c), entry e + 1 (en_n)
+  uint32_t en_c = 0, en_n = 0;
+  float ks_c = 0.0f;
+  if constexpr (SLIST) {
+    if (U > 0) {
+      en_c = load_scalar(gul, 0);
+      ks_c = __uint_as_float(load_scalar(kscale_row, en_c & 0xffffu));
+    }
+    if (U > 1) en_n = load_scalar(gul, 1);
   }
   const long long srow = (long long)(b * p.H + h) * p.N + L.qrow;
   float m_row = L.qvalid ? p.row_m[srow] : kNegInf;
@@ -981,7 +1017,8 @@ void attn_pv(AttnArgs p) {
 
   // entry e -> slot: its K tile, then its V^T tile (KCW + VCWX loads per wavefront)
   auto issue = [&](int e, int slot) {
-    const int j = __builtin_amdgcn_readfirstlane((int)(ent[e] & 0xffffu));
+    const int j = __builtin_amdgcn_readfirstlane(SLIST ? (int)((e == 0 ? en_c : en_n) & 0xffffu)
+                                                       : (int)(ent[e] & 0xffffu));
     const uint32_t sl = ring_lds + (uint32_t)(slot * EB);
     L.issue_k(p, j, sl);
     if constexpr (PV8) {
@@ -1013,10 +1050,19 @@ void attn_pv(AttnArgs p) {
   for (int t = 0; t < pre; ++t) issue(t, t);
   for (int e = 0; e < U; ++e) {
     const int pend = min(U - 1, e + NS - 2) - e;    // entries issued after entry e
-    wait_pending<Lane<D, KIND, kWavesPerBlock>::KCW + VCWX, NS - 2>(pend);
+    // (SLIST: every LDS read of the previous step fed its MFMAs, and the
+    // loop writes no LDS but through the tile loads)
+    wait_pending<Lane<D, KIND, kWavesPerBlock>::KCW + VCWX, NS - 2, !SLIST>(pend);
     if (e + NS - 1 < U) issue(e + NS - 1, (e + NS - 1) % NS);
-    const uint32_t en = (uint32_t)__builtin_amdgcn_readfirstlane((int)ent[e]);
+    const uint32_t en = SLIST ? en_c : (uint32_t)__builtin_amdgcn_readfirstlane((int)ent[e]);
     const int j = (int)(en & 0xffffu);
+    // SLIST: the next step's entries, loaded while this step runs
+    float ks_n = 0.0f;
+    uint32_t en_nn = 0;
+    if constexpr (SLIST) {
+      if (e + 1 < U) ks_n = __uint_as_float(load_scalar(kscale_row, en_n & 0xffffu));
+      if (e + 2 < U) en_nn = load_scalar(gul, e + 2);
+    }
     if ((en >> (16 + wave)) & 1u) {       // this wavefront's group ran P~V on tile j
       const unsigned char* kt = smem + (e % NS) * EB;
       const unsigned char* vt = kt + G::K_BYTES;
@@ -1030,7 +1076,7 @@ void attn_pv(AttnArgs p) {
         for (int s = 0; s < G::QS; ++s) acc[t] = mfma_qk<KIND>(kf[t][s], L.qf[s], acc[t]);
       }
       float c_scale = p.scale_log2;
-      if constexpr (G::I8) c_scale = L.qscale * ksc[e] * p.scale_log2;
+      if constexpr (G::I8) c_scale = L.qscale * (SLIST ? ks_c : ksc[e]) * p.scale_log2;
       f32x16 sv[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -1084,6 +1130,11 @@ void attn_pv(AttnArgs p) {
           }
         }
       }
+    }
+    if constexpr (SLIST) {
+      en_c = en_n;
+      ks_c = ks_n;
+      en_n = en_nn;
     }
   }
 
