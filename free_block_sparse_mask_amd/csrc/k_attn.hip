@@ -281,18 +281,29 @@ size_t stats_lds_bytes(int Tn) {
   return (size_t)(NP == 1 ? kStatsSlots : PackRing<G::I8>::slots) * G::K_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
          (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
 }
-// Pass 2 with int8 Q/K, 16-bit P~V and a two-slot ring (d = 128) reads its
-// entry list and the K block scales with scalar loads, one step ahead,
-// instead of staging them in LDS: the ring alone (48 KB) is then the
-// workgroup's LDS, and three workgroups share a CU instead of two.
+// Pass 2 with 24 KB (K, V^T) entries at d = 128 (int8 K with 16-bit V^T,
+// or 16-bit K with fp8 V^T) runs a two-slot ring and reads its entry list
+// (and the int8 K block scales) with scalar loads, one step ahead, instead
+// of staging them in LDS: the ring alone (48 KB) is then the workgroup's
+// LDS, and three workgroups share a CU instead of two.
 template <int D, int KIND, bool PV8>
 constexpr bool pv_scalar_list() {
-  return Geo<D, KIND>::I8 && !PV8 && Geo<D, KIND>::NS2 == 2;
+  using G = Geo<D, KIND>;
+  return D == 128 && (PV8 ? G::E8_BYTES : G::E_BYTES) == 24576;
+}
+template <int D, int KIND, bool PV8>
+constexpr int pv_slots() {
+  using G = Geo<D, KIND>;
+  return pv_scalar_list<D, KIND, PV8>() ? 2 : (PV8 ? G::NS8 : G::NS2);
+}
+template <int D, int KIND, bool PV8>
+constexpr int pv_waves_per_eu() {
+  return pv_scalar_list<D, KIND, PV8>() ? 3 : 2;
 }
 template <int D, int KIND, bool PV8>
 size_t pv_lds_bytes(int Tn) {
   using G = Geo<D, KIND>;
-  const size_t ring = PV8 ? (size_t)G::NS8 * G::E8_BYTES : (size_t)G::NS2 * G::E_BYTES;
+  const size_t ring = (size_t)pv_slots<D, KIND, PV8>() * (PV8 ? G::E8_BYTES : G::E_BYTES);
   if (pv_scalar_list<D, KIND, PV8>()) return ring;
   return ring + (size_t)4 * Tn + (G::I8 ? (size_t)4 * Tn : 0);
 }
@@ -950,11 +961,11 @@ void attn_stats(AttnArgs p) {
 // per-channel power of two), and one v_mfma_scale_f32_32x32x64_f8f6f4 takes a
 // whole 64-key tile per 32 output rows; O = delta_c * O^T / 2^8 / l.
 template <int D, int KIND, bool CAUSAL, bool PV8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(pv_waves_per_eu<D, KIND, PV8>())))
 void attn_pv(AttnArgs p) {
   using G = Geo<D, KIND>;
   using Acc = typename std::conditional<G::I8, i32x16, f32x16>::type;
-  constexpr int NS = PV8 ? G::NS8 : G::NS2;
+  constexpr int NS = pv_slots<D, KIND, PV8>();
   constexpr int EB = PV8 ? G::E8_BYTES : G::E_BYTES;
   constexpr int VCWX = PV8 ? G::V8CW : G::VCW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -986,7 +997,7 @@ void attn_pv(AttnArgs p) {
   if constexpr (SLIST) {
     if (U > 0) {
       en_c = load_scalar(gul, 0);
-      ks_c = __uint_as_float(load_scalar(kscale_row, en_c & 0xffffu));
+      if constexpr (G::I8) ks_c = __uint_as_float(load_scalar(kscale_row, en_c & 0xffffu));
     }
     if (U > 1) en_n = load_scalar(gul, 1);
   }
@@ -1060,7 +1071,8 @@ void attn_pv(AttnArgs p) {
     float ks_n = 0.0f;
     uint32_t en_nn = 0;
     if constexpr (SLIST) {
-      if (e + 1 < U) ks_n = __uint_as_float(load_scalar(kscale_row, en_n & 0xffffu));
+      if constexpr (G::I8)
+        if (e + 1 < U) ks_n = __uint_as_float(load_scalar(kscale_row, en_n & 0xffffu));
       if (e + 2 < U) en_nn = load_scalar(gul, e + 2);
     }
     if ((en >> (16 + wave)) & 1u) {       // this wavefront's group ran P~V on tile j
