@@ -281,15 +281,16 @@ size_t stats_lds_bytes(int Tn) {
   return (size_t)(NP == 1 ? kStatsSlots : PackRing<G::I8>::slots) * G::K_BYTES + (NP == 1 ? (size_t)2 * ((Tn + 1) & ~1) : 0) +
          (size_t)4 * NP * kWavesPerBlock * ((Tn + 15) / 16) + (G::I8 ? (size_t)4 * Tn : 0);
 }
-// Pass 2 with 24 KB (K, V^T) entries at d = 128 (int8 K with 16-bit V^T,
-// or 16-bit K with fp8 V^T) runs a two-slot ring and reads its entry list
-// (and the int8 K block scales) with scalar loads, one step ahead, instead
-// of staging them in LDS: the ring alone (48 KB) is then the workgroup's
-// LDS, and three workgroups share a CU instead of two.
+// Pass 2 at d = 128 with (K, V^T) entries of at most 24 KB (int8 K with
+// 16-bit V^T, 16-bit K with fp8 V^T, int8 K with fp8 V^T) runs a two-slot
+// ring and reads its entry list (and the int8 K block scales) with scalar
+// loads, one step ahead, instead of staging them in LDS: the ring alone
+// (48 or 32 KB) is then the workgroup's LDS, and three workgroups share a
+// CU instead of two.
 template <int D, int KIND, bool PV8>
 constexpr bool pv_scalar_list() {
   using G = Geo<D, KIND>;
-  return D == 128 && (PV8 ? G::E8_BYTES : G::E_BYTES) == 24576;
+  return D == 128 && (PV8 ? G::E8_BYTES : G::E_BYTES) <= 24576;
 }
 template <int D, int KIND, bool PV8>
 constexpr int pv_slots() {
