@@ -96,11 +96,21 @@ struct PackRing {
   static constexpr int per = I8 ? 3 : 2;
 };
 
+// The larger of two floats that are not NaN (scores, their maxima, -inf) in
+// one v_max_f32: fmaxf first quiets each operand the compiler cannot prove
+// canonical (a lane exchange's result, a loop-carried max), one more
+// instruction apiece.
+__device__ __forceinline__ float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // v_permlane32_swap(x, x) leaves x[l % 32] in one result and x[32 + l % 32]
 // in the other, so combining the two gives every lane the pair (l, l ^ 32).
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ int max_halves_i(int x) {
   const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
@@ -750,7 +760,7 @@ void attn_stats(AttnArgs p) {
       mx = max_halves(fmaxf(fmaxf(fmaxf(mq[0], mq[1]), mq[2]), mq[3]));
     }
     const float mloc = mx * c_scale;               // c_scale > 0: max commutes with the scale
-    const float m_new = fmaxf(m_run, mloc);
+    const float m_new = max_nn(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
     // lambda vote over the wavefront's 32 rows
     // (ballots of single compares, so each is the compare's lane mask)
@@ -1606,7 +1616,7 @@ void attn_fused(AttnArgs p) {
     f32x16 sv[2];
     const float c_scale = tile_scale(p, L, ks_row, j);
     const float mloc = tile_scores<D, KIND, CAUSAL, NW>(p, L, kt, j, jm, c_scale, sv);
-    const float m_new = fmaxf(m_run, mloc);
+    const float m_new = max_nn(m_run, mloc);
     const bool finite_row = mloc > kNegInf;
     // (ballots of single compares, so each is the compare's lane mask)
     const unsigned long long fin_mask = __builtin_amdgcn_ballot_w64(finite_row);
